@@ -1,0 +1,400 @@
+"""CPU oracle for the tile-aligned W4/W8 x A8 mixed-precision linear layer.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow, obviously-correct
+definition that the HIP path is checked against.  Only the test suite, the
+package smoke check and the benchmark's CPU-baseline leg may import it; the
+product path never does, and it shares no code, table or constant generator
+with the HIP sources.
+
+Source: "AlignQuant: Tile-Aligned Mixed-Precision Quantization for Efficient
+LLM Generation" (arXiv 2610.07457), as carried by the paperz deep-dive page.
+Each function names the section / equation it follows.
+
+Notation (paper Sec. 3.1): Y = X W^T with X in R^{M x K}, W in R^{N x K}; W is
+cut into equal b_N x b_K tiles, R = N / b_N tile rows, C = K / b_K tile
+columns, T = R*C.  z[r, j] in {4, 8} is the precision map.
+
+Readings taken where the pages are silent or are overridden by the task
+statement (each one is listed with its justification in the design doc):
+  * weight scale: one FP32 scale per (output row n, tile column j), absmax rule
+    s = max(absmax / q_max, 1e-12) computed in FP64 (App. B.2 eq. 5 and the
+    1e-12 floor of eq. 6);
+  * activation scale: one per token, s = max(absmax / 127, 1e-12), FP64;
+  * intra-tile byte order: our own (the pages' CUTLASS order is specific to
+    NVIDIA tensor cores):
+      W8 tile = b_K/16 panels; panel p holds, for every tile row i in order,
+        the 16 codes k = 16p .. 16p+15 (one byte each);
+      W4 tile = b_K/32 panels; panel p holds, for every tile row i in order,
+        16 bytes; byte b packs q0 = code at k = 32p + b and q1 = code at
+        k = 32p + 16 + b as (q0 mod 16) + 16 (q1 mod 16)   (App. E.1 eq. 17).
+
+Parity status: every function here is pinned by tests/test_oracle_*.py
+(hand-worked fixtures under tests/golden/, closed forms, brute force and
+invariants).  Parity with numbers printed on the pages is unpinned for the
+linear outputs themselves: the pages print no per-layer input/output example.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# App. B.2: q_min,b = -2^(b-1), q_max,b = 2^(b-1) - 1.
+def qrange(b: int) -> tuple[int, int]:
+    """Integer code range of a b-bit symmetric quantizer (App. B.2)."""
+    if b not in (4, 8):
+        raise ValueError("precision must be 4 or 8")
+    return -(2 ** (b - 1)), 2 ** (b - 1) - 1
+
+
+SCALE_FLOOR = 1e-12  # App. B.2 eq. 6: the scale is never below 1e-12.
+
+
+# --------------------------------------------------------------------------
+# Geometry and labels (Sec. 3.1; App. E.1)
+# --------------------------------------------------------------------------
+
+def tile_grid(N: int, K: int, bN: int, bK: int) -> tuple[int, int]:
+    """Number of tile rows R and tile columns C (Sec. 3.1 tile partition)."""
+    if N % bN or K % bK:
+        raise ValueError("N and K must be multiples of the tile size")
+    if bK % 32:
+        raise ValueError("b_K must be a multiple of 32 for the packed layout")
+    return N // bN, K // bK
+
+
+def labels_from_map(zmap: np.ndarray) -> np.ndarray:
+    """1-bit precision labels, 1 for W4 and 0 for W8, in row-major tile order,
+    eight labels per byte with the first label in the least significant bit
+    (App. E.1)."""
+    R, C = zmap.shape
+    T = R * C
+    out = np.zeros((T + 7) // 8, dtype=np.uint8)
+    for r in range(R):
+        for j in range(C):
+            t = r * C + j
+            if zmap[r, j] == 4:
+                out[t // 8] |= np.uint8(1 << (t % 8))
+            elif zmap[r, j] != 8:
+                raise ValueError("precision map entries must be 4 or 8")
+    return out
+
+
+def map_from_labels(labels: np.ndarray, R: int, C: int) -> np.ndarray:
+    """Inverse of labels_from_map (App. E.1)."""
+    z = np.empty((R, C), dtype=np.int64)
+    for r in range(R):
+        for j in range(C):
+            t = r * C + j
+            z[r, j] = 4 if (int(labels[t // 8]) >> (t % 8)) & 1 else 8
+    return z
+
+
+def row_offsets(zmap: np.ndarray, b: int) -> np.ndarray:
+    """INT32[R+1]: number of b-bit tiles in tile rows before r (App. E.1
+    eq. 16 'stored row offset'; App. E.2 length R+1)."""
+    R, _ = zmap.shape
+    off = np.zeros(R + 1, dtype=np.int32)
+    for r in range(R):
+        off[r + 1] = off[r] + int(np.sum(zmap[r] == b))
+    return off
+
+
+def tile_index(zmap: np.ndarray, r: int, j: int) -> int:
+    """Physical index of tile (r, j) inside the buffer of its own precision
+    (App. E.1 eq. 16): same-precision tiles in earlier rows plus those before
+    column j in row r."""
+    b = int(zmap[r, j])
+    before_rows = sum(int(zmap[rr, jj] == b) for rr in range(r)
+                      for jj in range(zmap.shape[1]))
+    in_row = sum(int(zmap[r, jj] == b) for jj in range(j))
+    return before_rows + in_row
+
+
+def int8_tile_count(frac8: float, T: int) -> int:
+    """Tile count from a fraction, nearest integer with ties to even
+    (App. D.4 rounding of k = round(rho |T|))."""
+    return int(round(frac8 * T))  # Python's round() is half-to-even
+
+
+# --------------------------------------------------------------------------
+# Quantizers (App. B.2 eq. 5-6; App. B.3)
+# --------------------------------------------------------------------------
+
+def quantize(A: np.ndarray, s: float, b: int) -> np.ndarray:
+    """Q_b(A; s) = clip(round_even(A / s), q_min, q_max), zero point 0
+    (App. B.2 eq. 5).  Division and rounding in FP64."""
+    lo, hi = qrange(b)
+    A64 = np.asarray(A, dtype=np.float64)
+    s64 = np.asarray(s, dtype=np.float64)
+    return np.clip(np.rint(A64 / s64), lo, hi).astype(np.int64)
+
+
+def absmax_scale(A: np.ndarray, b: int) -> float:
+    """max(max|A| / q_max,b, 1e-12) in FP64 (absmax form of the scale with the
+    floor of App. B.2 eq. 6)."""
+    _, hi = qrange(b)
+    a = float(np.max(np.abs(np.asarray(A, dtype=np.float64)))) if np.size(A) else 0.0
+    return max(a / hi, SCALE_FLOOR)
+
+
+def quant_weights(W: np.ndarray, zmap: np.ndarray, bN: int, bK: int):
+    """Per-tile-row weight quantization.
+
+    For tile (r, j) with precision b = z[r, j] and each row n of that tile the
+    FP64 scale s = max(absmax(W[n, tile cols]) / q_max,b, 1e-12) gives codes
+    Q_b(W[n, tile cols]; s); the stored scale is FP32(s) (App. B.2: integer
+    construction in FP64, s_b,t = FP32(s*)).
+
+    Returns codes int64 [N, K] and sW float32 [N, C].
+    """
+    N, K = W.shape
+    R, C = tile_grid(N, K, bN, bK)
+    codes = np.zeros((N, K), dtype=np.int64)
+    sW = np.zeros((N, C), dtype=np.float32)
+    for r in range(R):
+        for j in range(C):
+            b = int(zmap[r, j])
+            _, hi = qrange(b)
+            rows = slice(r * bN, (r + 1) * bN)
+            cols = slice(j * bK, (j + 1) * bK)
+            seg = np.asarray(W[rows, cols], dtype=np.float64)      # [bN, bK]
+            s = np.maximum(np.max(np.abs(seg), axis=1) / hi, SCALE_FLOOR)  # [bN]
+            codes[rows, cols] = quantize(seg, s[:, None], b)
+            sW[rows, j] = s.astype(np.float32)
+    return codes, sW
+
+
+def quant_act(X: np.ndarray):
+    """Per-token INT8 activation quantization: for row m,
+    s = max(max_k |X[m,k]| / 127, 1e-12) in FP64, qx = Q_8(X[m]; s), and the
+    stored scale is FP32(s) (App. B.3 computes in FP64 and stores INT8 codes
+    with FP32 scales; eq. 5 rounding)."""
+    X = np.asarray(X)
+    M, K = X.shape
+    qx = np.zeros((M, K), dtype=np.int64)
+    sx = np.zeros(M, dtype=np.float32)
+    for m in range(M):
+        row = X[m].astype(np.float64)
+        s = absmax_scale(row, 8)
+        qx[m] = quantize(row, s, 8)
+        sx[m] = np.float32(s)
+    return qx, sx
+
+
+# --------------------------------------------------------------------------
+# Packing (Sec. 3.2; App. E.1 eq. 16-17; App. E.2)
+# --------------------------------------------------------------------------
+
+def pack_tile_w8(tile_codes: np.ndarray) -> np.ndarray:
+    """Bytes of one W8 tile: b_K/16 panels, each holding 16 codes per tile row
+    (rows in order), one two's-complement byte per code."""
+    bN, bK = tile_codes.shape
+    out = np.zeros((bK // 16, bN, 16), dtype=np.uint8)
+    for p in range(bK // 16):
+        out[p] = (tile_codes[:, 16 * p:16 * p + 16] % 256).astype(np.uint8)
+    return out.reshape(-1)
+
+
+def nibble_byte(q0, q1):
+    """byte(q0, q1) = (q0 mod 16) + 16 (q1 mod 16)  (App. E.1 eq. 17)."""
+    return (np.asarray(q0) % 16) + 16 * (np.asarray(q1) % 16)
+
+
+def nibble_value(v):
+    """A nibble v expands to v if v < 8 and to v - 16 otherwise (App. E.1)."""
+    v = np.asarray(v)
+    return np.where(v < 8, v, v - 16)
+
+
+def pack_tile_w4(tile_codes: np.ndarray) -> np.ndarray:
+    """Bytes of one W4 tile: b_K/32 panels, each holding 16 bytes per tile row
+    (rows in order); byte b of a row's 16 packs the codes at k = 32p + b and
+    k = 32p + 16 + b by eq. 17."""
+    bN, bK = tile_codes.shape
+    lo, hi = qrange(4)
+    if tile_codes.min(initial=0) < lo or tile_codes.max(initial=0) > hi:
+        raise ValueError("INT4 code out of range")
+    out = np.zeros((bK // 32, bN, 16), dtype=np.uint8)
+    for p in range(bK // 32):
+        q0 = tile_codes[:, 32 * p:32 * p + 16]
+        q1 = tile_codes[:, 32 * p + 16:32 * p + 32]
+        out[p] = nibble_byte(q0, q1).astype(np.uint8)
+    return out.reshape(-1)
+
+
+def unpack_tile_w8(buf: np.ndarray, bN: int, bK: int) -> np.ndarray:
+    panels = buf.reshape(bK // 16, bN, 16).astype(np.int64)
+    codes = np.zeros((bN, bK), dtype=np.int64)
+    for p in range(bK // 16):
+        codes[:, 16 * p:16 * p + 16] = np.where(panels[p] < 128, panels[p], panels[p] - 256)
+    return codes
+
+
+def unpack_tile_w4(buf: np.ndarray, bN: int, bK: int) -> np.ndarray:
+    panels = buf.reshape(bK // 32, bN, 16).astype(np.int64)
+    codes = np.zeros((bN, bK), dtype=np.int64)
+    for p in range(bK // 32):
+        codes[:, 32 * p:32 * p + 16] = nibble_value(panels[p] % 16)
+        codes[:, 32 * p + 16:32 * p + 32] = nibble_value(panels[p] // 16)
+    return codes
+
+
+def pack(codes: np.ndarray, sW: np.ndarray, zmap: np.ndarray, bN: int, bK: int) -> dict:
+    """Split W4/W8 packed representation (Sec. 3.2; App. E.1-E.2).
+
+    Selected W4 and W8 tiles go to two contiguous buffers in row order; tile
+    (r, j) sits at index_b(r, j) of eq. 16 in the buffer of its precision; its
+    b_N per-row FP32 scales sit at the same index in s4 / s8.  Returns a dict
+    with labels, row_off4, row_off8, w4 (uint8 [T4*bN*bK/2]),
+    w8 (uint8 [T8*bN*bK]), s4 (float32 [T4*bN]), s8 (float32 [T8*bN]).
+    """
+    N, K = codes.shape
+    R, C = tile_grid(N, K, bN, bK)
+    T4 = int(np.sum(zmap == 4))
+    T8 = int(np.sum(zmap == 8))
+    w4 = np.zeros(T4 * bN * bK // 2, dtype=np.uint8)
+    w8 = np.zeros(T8 * bN * bK, dtype=np.uint8)
+    s4 = np.zeros(T4 * bN, dtype=np.float32)
+    s8 = np.zeros(T8 * bN, dtype=np.float32)
+    off4 = row_offsets(zmap, 4)
+    off8 = row_offsets(zmap, 8)
+    for r in range(R):
+        seen4 = 0
+        seen8 = 0
+        for j in range(C):
+            tile = codes[r * bN:(r + 1) * bN, j * bK:(j + 1) * bK]
+            scales = sW[r * bN:(r + 1) * bN, j]
+            if zmap[r, j] == 4:
+                idx = int(off4[r]) + seen4
+                seen4 += 1
+                nb = bN * bK // 2
+                w4[idx * nb:(idx + 1) * nb] = pack_tile_w4(tile)
+                s4[idx * bN:(idx + 1) * bN] = scales
+            else:
+                idx = int(off8[r]) + seen8
+                seen8 += 1
+                nb = bN * bK
+                w8[idx * nb:(idx + 1) * nb] = pack_tile_w8(tile)
+                s8[idx * bN:(idx + 1) * bN] = scales
+    return dict(labels=labels_from_map(zmap), row_off4=off4, row_off8=off8,
+                w4=w4, w8=w8, s4=s4, s8=s8, N=N, K=K, bN=bN, bK=bK, T4=T4, T8=T8)
+
+
+def unpack(packed: dict):
+    """Inverse of pack: returns codes int64 [N, K], sW float32 [N, C] and the
+    precision map, locating every tile from its logical coordinate through
+    its label, its row offset and eq. 16 (App. E.1)."""
+    N, K, bN, bK = packed["N"], packed["K"], packed["bN"], packed["bK"]
+    R, C = tile_grid(N, K, bN, bK)
+    zmap = map_from_labels(packed["labels"], R, C)
+    codes = np.zeros((N, K), dtype=np.int64)
+    sW = np.zeros((N, C), dtype=np.float32)
+    for r in range(R):
+        for j in range(C):
+            b = int(zmap[r, j])
+            off = packed["row_off4"] if b == 4 else packed["row_off8"]
+            pos = sum(int(zmap[r, jj] == b) for jj in range(j))
+            idx = int(off[r]) + pos
+            if b == 4:
+                nb = bN * bK // 2
+                tile = unpack_tile_w4(packed["w4"][idx * nb:(idx + 1) * nb], bN, bK)
+                sc = packed["s4"][idx * bN:(idx + 1) * bN]
+            else:
+                nb = bN * bK
+                tile = unpack_tile_w8(packed["w8"][idx * nb:(idx + 1) * nb], bN, bK)
+                sc = packed["s8"][idx * bN:(idx + 1) * bN]
+            codes[r * bN:(r + 1) * bN, j * bK:(j + 1) * bK] = tile
+            sW[r * bN:(r + 1) * bN, j] = sc
+    return codes, sW, zmap
+
+
+def pack_weights(W: np.ndarray, zmap: np.ndarray, bN: int, bK: int) -> dict:
+    """Quantize then pack (App. B.2 followed by App. E.1)."""
+    codes, sW = quant_weights(W, zmap, bN, bK)
+    return pack(codes, sW, zmap, bN, bK)
+
+
+# --------------------------------------------------------------------------
+# Tile products and output reconstruction (Sec. 3.3; App. E.3 eq. 19)
+# --------------------------------------------------------------------------
+
+def tile_partials(qx: np.ndarray, codes: np.ndarray, bK: int) -> np.ndarray:
+    """P[m, n, j] = sum over k in tile column j of qx[m, k] * codes[n, k]: the
+    parenthesized integer tile product of eq. 19, int64 [M, N, C].
+
+    Each product is formed with a float64 matrix product: every term and
+    partial sum is an integer below 2^53, so the result is exact."""
+    M, K = qx.shape
+    N, K2 = codes.shape
+    if K != K2 or K % bK:
+        raise ValueError("shape mismatch")
+    C = K // bK
+    P = np.zeros((M, N, C), dtype=np.int64)
+    for j in range(C):
+        a = qx[:, j * bK:(j + 1) * bK].astype(np.float64)
+        w = codes[:, j * bK:(j + 1) * bK].astype(np.float64)
+        P[:, :, j] = np.rint(a @ w.T).astype(np.int64)
+    if P.size and (P.max() > 2**31 - 1 or P.min() < -2**31):
+        raise OverflowError("tile partial exceeds INT32")
+    return P
+
+
+def linear_from_partials(P: np.ndarray, sx: np.ndarray, sW: np.ndarray,
+                         bias: np.ndarray | None = None) -> np.ndarray:
+    """y[m, n] = sum_j s^X_m s^W_{n,j} P[m, n, j] (+ bias[n]) in FP64,
+    j in increasing order (App. E.3 eq. 19; interface adds bias when present)."""
+    M, N, C = P.shape
+    y = np.zeros((M, N), dtype=np.float64)
+    sx64 = np.asarray(sx, dtype=np.float64)
+    sW64 = np.asarray(sW, dtype=np.float64)
+    for j in range(C):
+        y += (sx64[:, None] * sW64[None, :, j]) * P[:, :, j].astype(np.float64)
+    if bias is not None:
+        y += np.asarray(bias, dtype=np.float64)[None, :]
+    return y
+
+
+def abs_contrib(P: np.ndarray, sx: np.ndarray, sW: np.ndarray) -> np.ndarray:
+    """sum_j |s^X_m s^W_{n,j} P[m, n, j]|: the scale of the rounding error an
+    FP32 evaluation of eq. 19 can make; used by the componentwise gate."""
+    M, N, C = P.shape
+    a = np.zeros((M, N), dtype=np.float64)
+    sx64 = np.asarray(sx, dtype=np.float64)
+    sW64 = np.asarray(sW, dtype=np.float64)
+    for j in range(C):
+        a += np.abs((sx64[:, None] * sW64[None, :, j]) * P[:, :, j].astype(np.float64))
+    return a
+
+
+def linear(X: np.ndarray, W: np.ndarray, zmap: np.ndarray, bN: int, bK: int,
+           bias: np.ndarray | None = None) -> np.ndarray:
+    """The whole path: quantize weights and activations, integer tile
+    products, FP64 rescale and sum (Sec. 3.3)."""
+    codes, sW = quant_weights(W, zmap, bN, bK)
+    qx, sx = quant_act(X)
+    return linear_from_partials(tile_partials(qx, codes, bK), sx, sW, bias)
+
+
+# --------------------------------------------------------------------------
+# Storage accounting (App. E.2 eq. 18)
+# --------------------------------------------------------------------------
+
+def packed_bytes_paper(T4: int, T8: int, R: int, C: int, bN: int, bK: int) -> int:
+    """S_packed = B/2 T4 + B T8 + 4 (T4 + T8) + ceil(RC/8) + 8 (R+1), with
+    one FP32 scale per tile (App. E.2 eq. 18)."""
+    B = bN * bK
+    return B * T4 // 2 + B * T8 + 4 * (T4 + T8) + math.ceil(R * C / 8) + 8 * (R + 1)
+
+
+def packed_bytes_rowscale(T4: int, T8: int, R: int, C: int, bN: int, bK: int) -> int:
+    """Eq. 18 with one FP32 scale per tile row instead of per tile: the scale
+    term becomes 4 b_N (T4 + T8)."""
+    B = bN * bK
+    return B * T4 // 2 + B * T8 + 4 * bN * (T4 + T8) + math.ceil(R * C / 8) + 8 * (R + 1)
+
+
+def bits_per_weight(S_packed: int, T4: int, T8: int, bN: int, bK: int) -> float:
+    """Complete packed bits per weight 8 S / (B (T4 + T8)) (App. E.2)."""
+    return 8.0 * S_packed / (bN * bK * (T4 + T8))
