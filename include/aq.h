@@ -1,0 +1,186 @@
+/*
+ * aq.h -- C ABI of the tile-aligned W4/W8 x A8 mixed-precision linear layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "AlignQuant: Tile-Aligned Mixed-Precision Quantization for
+ * Efficient LLM Generation" (arXiv 2610.07457).  A projection Y = X W^T,
+ * X in R^{M x K} (activation rows), W in R^{N x K} (rows = output features),
+ * is cut into equal b_N x b_K weight tiles (Sec. 3.1).  Each tile stores one
+ * representation, INT4 or INT8, selected by a 1-bit label (Sec. 3.2); the
+ * runtime quantizes activations to INT8, widens every weight tile to INT8 on
+ * chip, forms INT32 tile products and rescales them into an FP32 result
+ * (Sec. 3.3; App. E.3 eq. 19).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers documented "device" are GPU global-memory pointers owned by the
+ *    caller; "host" pointers are CPU memory owned by the caller.  The library
+ *    never allocates, frees or retains caller memory and keeps no mutable
+ *    global state; calls are re-entrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Device work is enqueued asynchronously on it; results are ready when
+ *    that stream is synchronized.  A fault inside a kernel surfaces at the
+ *    caller's next synchronization, not as a return code.
+ *  - All arguments are validated on the host before anything is enqueued; on
+ *    any error nothing is launched and a negative aq_status is returned.  No
+ *    C++ exception crosses this boundary.
+ *  - GPU tile geometry: b_N = 64 and b_K in {64, 128}.  N % b_N == 0,
+ *    K % b_K == 0.  Device buffers must be 16-byte aligned.
+ *  - Inputs must be finite; NaN / Inf behaviour is unspecified.
+ *
+ * Packed layout (App. E.1-E.2; intra-tile order is this library's own, the
+ * pages' CUTLASS order being specific to NVIDIA tensor cores)
+ *  - labels  : ceil(R*C/8) bytes; tile t = r*C + j is bit (t & 7) of byte
+ *              t >> 3 (first label in the least significant bit); 1 = INT4.
+ *  - row_off4, row_off8 : INT32[R+1]; number of INT4 (INT8) tiles in tile
+ *              rows before r.  Tile (r, j) of precision b sits at
+ *              index_b(r, j) = row_off_b[r] + (tiles of precision b before
+ *              column j in row r)   (App. E.1 eq. 16).
+ *  - w8      : T8 tiles of b_N*b_K bytes.  A tile is b_K/16 panels; panel p
+ *              holds, for tile rows i = 0..b_N-1 in order, the 16 INT8 codes
+ *              of columns 16p .. 16p+15.
+ *  - w4      : T4 tiles of b_N*b_K/2 bytes.  A tile is b_K/32 panels; panel p
+ *              holds, for tile rows i in order, 16 bytes; byte b packs the
+ *              codes q0 at column 32p+b and q1 at column 32p+16+b as
+ *              (q0 mod 16) + 16*(q1 mod 16)   (App. E.1 eq. 17).
+ *  - s8, s4  : FP32[T_b][b_N]; the scale of row i of the tile at index_b(r,j)
+ *              (one scale per tile row of each tile; the pages store one per
+ *              tile, App. E.2).
+ */
+#ifndef AQ_H
+#define AQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AQ_ABI_VERSION 1
+
+typedef enum aq_status {
+  AQ_OK = 0,
+  AQ_ERR_NULL = -1,       /* a required pointer is NULL                      */
+  AQ_ERR_SHAPE = -2,      /* N, K, M not compatible with the tile geometry   */
+  AQ_ERR_TILE = -3,       /* tile size not supported on the GPU              */
+  AQ_ERR_MAP = -4,        /* labels disagree with T4 / T8, or bad map entry  */
+  AQ_ERR_ALIGN = -5,      /* a device pointer is not 16-byte aligned         */
+  AQ_ERR_WORKSPACE = -6,  /* workspace missing or smaller than required      */
+  AQ_ERR_HIP = -7,        /* the HIP runtime reported an error at launch     */
+  AQ_ERR_ARG = -8         /* any other invalid argument                      */
+} aq_status;
+
+/* Sizes of a packed projection, computed on the host from its labels. */
+typedef struct aq_plan {
+  int32_t N, K, bN, bK;   /* projection and tile geometry                    */
+  int32_t R, C;           /* tile rows N/bN and tile columns K/bK            */
+  int32_t T4, T8;         /* INT4 and INT8 tile counts, T4 + T8 = R*C        */
+  size_t labels_bytes;    /* ceil(R*C/8)                                     */
+  size_t offs_bytes;      /* 4*(R+1), for each of row_off4 and row_off8      */
+  size_t w4_bytes, w8_bytes;  /* T4*bN*bK/2 and T8*bN*bK                     */
+  size_t s4_bytes, s8_bytes;  /* 4*T4*bN and 4*T8*bN                         */
+} aq_plan;
+
+/* A packed projection: geometry plus device buffers sized by aq_plan.
+ * aq_pack_weights writes the buffers; the linear entry points only read
+ * them.  w4/s4 may be NULL when T4 == 0, w8/s8 when T8 == 0. */
+typedef struct aq_packed {
+  int32_t N, K, bN, bK, T4, T8;
+  uint8_t *labels;        /* device, labels_bytes                           */
+  int32_t *row_off4;      /* device, R+1                                    */
+  int32_t *row_off8;      /* device, R+1                                    */
+  uint8_t *w4;            /* device, w4_bytes                               */
+  int8_t *w8;             /* device, w8_bytes                               */
+  float *s4;              /* device, T4*bN                                  */
+  float *s8;              /* device, T8*bN                                  */
+} aq_packed;
+
+/* Phase selector for aq_workspace_bytes / aq_linear_tile_partials. */
+#define AQ_PHASE_DECODE 0
+#define AQ_PHASE_PREFILL 1
+
+/* ABI version of the loaded library (AQ_ABI_VERSION). */
+int aq_abi_version(void);
+
+/* Human-readable text of a status code.  Never NULL. */
+const char *aq_status_string(aq_status status);
+
+/* Host only.  Labels from a precision map: zmap_host holds R*C entries in
+ * row-major tile order, each 4 or 8 (Sec. 3.1 map z_{r,j}); labels_host
+ * receives ceil(R*C/8) bytes, bit set = INT4, first tile in the LSB
+ * (App. E.1).  AQ_ERR_MAP if an entry is neither 4 nor 8. */
+aq_status aq_labels_from_map(const uint8_t *zmap_host, int R, int C, uint8_t *labels_host);
+
+/* Host only.  Buffer sizes of a packed projection (App. E.2): checks the
+ * geometry (any b_N >= 1 and b_K a multiple of 32 are planned; the GPU entry
+ * points further require b_N = 64, b_K in {64, 128}) and counts T4 / T8 from
+ * the host labels.  Does not touch the GPU. */
+aq_status aq_plan_pack(int N, int K, int bN, int bK, const uint8_t *labels_host, aq_plan *out);
+
+/* Quantize and pack one projection (App. B.2 eq. 5 with the 1e-12 floor of
+ * eq. 6; App. E.1-E.2).  For tile (r, j) of precision b = 8 - 4*label and each
+ * row n of it, s = max(max|W[n, tile cols]| / (2^(b-1) - 1), 1e-12) in FP64,
+ * codes = clip(round_half_even(W / s), -2^(b-1), 2^(b-1) - 1) in FP64, the
+ * stored scale is FP32(s) rounded to nearest even.
+ *   W           device, FP32 [N][K] row-major; may be freed once the stream
+ *               has passed this call.
+ *   labels_host host, ceil(R*C/8) bytes; T4 / T8 in *out must match them.
+ *   out         geometry (N, K, bN, bK, T4, T8) and device buffers, sized by
+ *               aq_plan_pack.  labels and row offsets are copied in from the
+ *               host (the host copy may be reused when this call returns).
+ */
+aq_status aq_pack_weights(const float *W, const uint8_t *labels_host, aq_packed *out, void *stream);
+
+/* Per-token INT8 activation quantization (App. B.3 FP64 preparation, eq. 5
+ * rounding): for each row m, s = max(max_k |X[m,k]| / 127, 1e-12) in FP64,
+ * qx[m,k] = clip(round_half_even(X[m,k] / s), -128, 127) in FP64,
+ * sx[m] = FP32(s).
+ *   X   device, FP32 [M][K] row-major;  qx device, INT8 [M][K];
+ *   sx  device, FP32 [M].  K must be a multiple of 64; M == 0 is a no-op. */
+aq_status aq_quant_act(const float *X, int M, int K, int8_t *qx, float *sx, void *stream);
+
+/* Device workspace, in bytes, that aq_linear_decode (phase 0) or
+ * aq_linear_prefill (phase 1) needs for M rows with the given decode split
+ * (0 = adaptive).  0 means no workspace is needed. */
+size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split);
+
+/* Split count that aq_linear_decode uses for `split` = 0 (adaptive split
+ * over input-tile columns, chosen from the projection geometry). */
+int aq_decode_split(const aq_packed *W, int M);
+
+/* Memory-bound phase (Sec. 3.3 "Decode parallelism"; App. E.3 Table 5):
+ *   Y[m,n] = sx[m] * sum_j sW[n,j] * P[m,n,j]  (+ bias[n]),
+ * P[m,n,j] the INT32 product of the INT8 activation codes and the tile's
+ * codes widened to INT8 (eq. 19).  Work is spread over output-tile rows and
+ * `split` groups of input-tile columns: split s covers tile columns
+ * floor(C*s/S) .. floor(C*(s+1)/S)-1 and the FP32 partials of the splits are
+ * summed in increasing s (App. E.3).
+ *   qx    device INT8 [M][K] (from aq_quant_act);  sx device FP32 [M]
+ *   bias  device FP32 [N] or NULL
+ *   Y     device FP32 [M][N] row-major (written, not accumulated)
+ *   split 0 = adaptive (aq_decode_split), else 1..C
+ *   ws    device workspace of at least aq_workspace_bytes(W, M, 0, split)
+ * Any M >= 1 is accepted; M == 0 is a no-op. */
+aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                           const float *bias, float *Y, int split, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* Compute-bound phase (Sec. 3.3 "Prefill weight reuse"; App. E.3): the same
+ * Y as aq_linear_decode, computed with INT8 matrix-core (MFMA) tiles that
+ * reuse each weight tile across many activation rows.  Same arguments; the
+ * workspace may be NULL when aq_workspace_bytes(W, M, 1, 0) is 0.  Any
+ * M >= 1 is accepted. */
+aq_status aq_linear_prefill(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                            const float *bias, float *Y, void *ws, size_t ws_bytes, void *stream);
+
+/* Debug: the INT32 tile products P[m, n, j] of eq. 19 (the parenthesized
+ * product, before any scaling), written to P as INT32 [M][N][C] row-major,
+ * computed by the decode (phase 0) or prefill (phase 1) kernels themselves. */
+aq_status aq_linear_tile_partials(const aq_packed *W, const int8_t *qx, int M, int phase,
+                                  int32_t *P, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AQ_H */

@@ -1,0 +1,248 @@
+"""Thin Python binding of libaq.so (include/aq.h).
+
+Argument marshalling only: every step of the linear layer runs in the HIP
+kernels of libaq.so.  PyTorch provides device memory and the current stream.
+The functions keep the C names; they take torch tensors and raise AqError on
+a non-zero status.  There is no fallback: without the built library every
+call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaq.so")
+
+AQ_PHASE_DECODE = 0
+AQ_PHASE_PREFILL = 1
+
+STATUS = {0: "AQ_OK", -1: "AQ_ERR_NULL", -2: "AQ_ERR_SHAPE", -3: "AQ_ERR_TILE", -4: "AQ_ERR_MAP",
+          -5: "AQ_ERR_ALIGN", -6: "AQ_ERR_WORKSPACE", -7: "AQ_ERR_HIP", -8: "AQ_ERR_ARG"}
+
+# Every symbol include/aq.h declares.
+EXPORTS = ["aq_abi_version", "aq_status_string", "aq_labels_from_map", "aq_plan_pack",
+           "aq_pack_weights", "aq_quant_act", "aq_workspace_bytes", "aq_decode_split",
+           "aq_linear_decode", "aq_linear_prefill", "aq_linear_tile_partials"]
+
+
+class AqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_status_text(status)})")
+
+
+class AqPlan(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("bN", ctypes.c_int32),
+                ("bK", ctypes.c_int32), ("R", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("T4", ctypes.c_int32), ("T8", ctypes.c_int32),
+                ("labels_bytes", ctypes.c_size_t), ("offs_bytes", ctypes.c_size_t),
+                ("w4_bytes", ctypes.c_size_t), ("w8_bytes", ctypes.c_size_t),
+                ("s4_bytes", ctypes.c_size_t), ("s8_bytes", ctypes.c_size_t)]
+
+
+class AqPacked(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("bN", ctypes.c_int32),
+                ("bK", ctypes.c_int32), ("T4", ctypes.c_int32), ("T8", ctypes.c_int32),
+                ("labels", ctypes.c_void_p), ("row_off4", ctypes.c_void_p),
+                ("row_off8", ctypes.c_void_p), ("w4", ctypes.c_void_p), ("w8", ctypes.c_void_p),
+                ("s4", ctypes.c_void_p), ("s8", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libaq.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m mixed_precision_int_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "aq_abi_version": (i32, []),
+        "aq_status_string": (ctypes.c_char_p, [i32]),
+        "aq_labels_from_map": (i32, [vp, i32, i32, vp]),
+        "aq_plan_pack": (i32, [i32, i32, i32, i32, vp, ctypes.POINTER(AqPlan)]),
+        "aq_pack_weights": (i32, [vp, vp, ctypes.POINTER(AqPacked), vp]),
+        "aq_quant_act": (i32, [vp, i32, i32, vp, vp, vp]),
+        "aq_workspace_bytes": (sz, [ctypes.POINTER(AqPacked), i32, i32, i32]),
+        "aq_decode_split": (i32, [ctypes.POINTER(AqPacked), i32]),
+        "aq_linear_decode": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp, sz, vp]),
+        "aq_linear_prefill": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
+        "aq_linear_tile_partials": (i32, [ctypes.POINTER(AqPacked), vp, i32, i32, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = L
+    return L
+
+
+def _status_text(status: int) -> str:
+    try:
+        return lib().aq_status_string(status).decode()
+    except Exception:  # pragma: no cover - only when the library is absent
+        return "?"
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise AqError(status, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------- host calls
+
+def aq_abi_version() -> int:
+    return lib().aq_abi_version()
+
+
+def aq_labels_from_map(zmap: np.ndarray) -> np.ndarray:
+    """Labels (1 = INT4, LSB first) of an [R, C] map of 4 / 8."""
+    z = np.ascontiguousarray(zmap, dtype=np.uint8)
+    R, C = z.shape
+    out = np.zeros((R * C + 7) // 8, dtype=np.uint8)
+    _check(lib().aq_labels_from_map(z.ctypes.data, R, C, out.ctypes.data), "aq_labels_from_map")
+    return out
+
+
+def aq_plan_pack(N: int, K: int, bN: int, bK: int, labels: np.ndarray) -> AqPlan:
+    lab = np.ascontiguousarray(labels, dtype=np.uint8)
+    plan = AqPlan()
+    _check(lib().aq_plan_pack(N, K, bN, bK, lab.ctypes.data, ctypes.byref(plan)), "aq_plan_pack")
+    return plan
+
+
+# ---------------------------------------------------------------- device calls
+
+@dataclass
+class PackedWeights:
+    """Device buffers of one packed projection and the C descriptor over them."""
+    plan: AqPlan
+    labels_host: np.ndarray
+    labels: object
+    row_off4: object
+    row_off8: object
+    w4: object
+    w8: object
+    s4: object
+    s8: object
+    desc: AqPacked
+
+    @property
+    def N(self):
+        return self.plan.N
+
+    @property
+    def K(self):
+        return self.plan.K
+
+    def nbytes(self) -> int:
+        p = self.plan
+        return int(p.labels_bytes + 2 * p.offs_bytes + p.w4_bytes + p.w8_bytes + p.s4_bytes + p.s8_bytes)
+
+
+def _dev_bytes(n: int, device):
+    import torch
+    # at least 16 bytes so that every pointer is valid and aligned
+    return torch.empty(max(int(n), 16), dtype=torch.uint8, device=device)
+
+
+def aq_alloc_packed(plan: AqPlan, labels: np.ndarray, device="cuda") -> PackedWeights:
+    t = dict(labels=_dev_bytes(plan.labels_bytes, device), row_off4=_dev_bytes(plan.offs_bytes, device),
+             row_off8=_dev_bytes(plan.offs_bytes, device), w4=_dev_bytes(plan.w4_bytes, device),
+             w8=_dev_bytes(plan.w8_bytes, device), s4=_dev_bytes(plan.s4_bytes, device),
+             s8=_dev_bytes(plan.s8_bytes, device))
+    d = AqPacked(plan.N, plan.K, plan.bN, plan.bK, plan.T4, plan.T8,
+                 *(t[k].data_ptr() for k in ("labels", "row_off4", "row_off8", "w4", "w8", "s4", "s8")))
+    return PackedWeights(plan=plan, labels_host=np.ascontiguousarray(labels, dtype=np.uint8), desc=d, **t)
+
+
+def aq_pack_weights(W, labels: np.ndarray, bN: int = 64, bK: int = 128, stream=None) -> PackedWeights:
+    """Quantize and pack W (device FP32 [N, K]) under the given labels."""
+    N, K = W.shape
+    lab = np.ascontiguousarray(labels, dtype=np.uint8)
+    plan = aq_plan_pack(N, K, bN, bK, lab)
+    pw = aq_alloc_packed(plan, lab, W.device)
+    _check(lib().aq_pack_weights(ctypes.c_void_p(W.data_ptr()), lab.ctypes.data,
+                                 ctypes.byref(pw.desc), _stream(stream)), "aq_pack_weights")
+    return pw
+
+
+def aq_quant_act(X, qx=None, sx=None, stream=None):
+    """INT8 codes [M, K] and FP32 scales [M] of device FP32 X [M, K]."""
+    import torch
+    M, K = X.shape
+    if qx is None:
+        qx = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float32, device=X.device)
+    _check(lib().aq_quant_act(ctypes.c_void_p(X.data_ptr()), M, K, ctypes.c_void_p(qx.data_ptr()),
+                              ctypes.c_void_p(sx.data_ptr()), _stream(stream)), "aq_quant_act")
+    return qx, sx
+
+
+def aq_workspace_bytes(pw: PackedWeights, M: int, phase: int, split: int = 0) -> int:
+    return int(lib().aq_workspace_bytes(ctypes.byref(pw.desc), M, phase, split))
+
+
+def aq_decode_split(pw: PackedWeights, M: int) -> int:
+    return int(lib().aq_decode_split(ctypes.byref(pw.desc), M))
+
+
+def aq_linear_decode(pw: PackedWeights, qx, sx, bias=None, split: int = 0, out=None, ws=None,
+                     stream=None):
+    """Decode-phase linear: FP32 Y [M, N]."""
+    import torch
+    M = qx.shape[0]
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=qx.device)
+    need = aq_workspace_bytes(pw, M, AQ_PHASE_DECODE, split)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=qx.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().aq_linear_decode(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias),
+                                  _ptr(out), split, _ptr(ws), ws_bytes, _stream(stream)),
+           "aq_linear_decode")
+    return out
+
+
+def aq_linear_prefill(pw: PackedWeights, qx, sx, bias=None, out=None, stream=None):
+    """Prefill-phase linear (INT8 MFMA): FP32 Y [M, N]."""
+    import torch
+    M = qx.shape[0]
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=qx.device)
+    _check(lib().aq_linear_prefill(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias),
+                                   _ptr(out), None, 0, _stream(stream)), "aq_linear_prefill")
+    return out
+
+
+def aq_linear_tile_partials(pw: PackedWeights, qx, phase: int, out=None, stream=None):
+    """INT32 tile products P [M, N, C] computed by the decode or prefill kernels."""
+    import torch
+    M = qx.shape[0]
+    C = pw.plan.C
+    if out is None:
+        out = torch.empty((M, pw.N, C), dtype=torch.int32, device=qx.device)
+    _check(lib().aq_linear_tile_partials(ctypes.byref(pw.desc), _ptr(qx), M, phase, _ptr(out),
+                                         _stream(stream)), "aq_linear_tile_partials")
+    return out

@@ -1,0 +1,233 @@
+// Host side of the C ABI declared in include/aq.h: argument validation,
+// planning, metadata upload and kernel dispatch.  Everything is checked
+// before any HIP call is made, so invalid calls never touch the GPU.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/aq.h"
+#include "aq_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int bit_of(const uint8_t *labels, int t) { return (labels[t >> 3] >> (t & 7)) & 1; }
+
+// Geometry accepted by the GPU kernels.
+aq_status check_gpu_geometry(int N, int K, int bN, int bK) {
+  if (bN != aq::kTileRows || (bK != 64 && bK != 128)) return AQ_ERR_TILE;
+  if (N <= 0 || K <= 0 || N % bN || K % bK) return AQ_ERR_SHAPE;
+  // int32 tile counts and K-offsets inside kernels
+  if ((long long)(N / bN) * (K / bK) > (1LL << 30)) return AQ_ERR_SHAPE;
+  return AQ_OK;
+}
+
+aq_status check_packed(const aq_packed *W) {
+  if (!W) return AQ_ERR_NULL;
+  aq_status st = check_gpu_geometry(W->N, W->K, W->bN, W->bK);
+  if (st != AQ_OK) return st;
+  const long long T = (long long)(W->N / W->bN) * (W->K / W->bK);
+  if (W->T4 < 0 || W->T8 < 0 || (long long)W->T4 + W->T8 != T) return AQ_ERR_MAP;
+  if (!W->labels || !W->row_off4 || !W->row_off8) return AQ_ERR_NULL;
+  if (W->T4 > 0 && (!W->w4 || !W->s4)) return AQ_ERR_NULL;
+  if (W->T8 > 0 && (!W->w8 || !W->s8)) return AQ_ERR_NULL;
+  if (!aligned4(W->row_off4) || !aligned4(W->row_off8)) return AQ_ERR_ALIGN;
+  if (W->T4 > 0 && (!aligned16(W->w4) || !aligned16(W->s4))) return AQ_ERR_ALIGN;
+  if (W->T8 > 0 && (!aligned16(W->w8) || !aligned16(W->s8))) return AQ_ERR_ALIGN;
+  return AQ_OK;
+}
+
+aq_status check_linear_io(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                          const float *bias, const void *out) {
+  if (M < 0) return AQ_ERR_SHAPE;
+  if (M == 0) return AQ_OK;
+  if (!qx || !sx || !out) return AQ_ERR_NULL;
+  if (!aligned16(qx) || !aligned16(out) || !aligned4(sx)) return AQ_ERR_ALIGN;
+  if (bias && !aligned16(bias)) return AQ_ERR_ALIGN;
+  // 64-bit products are used for every offset; keep each dimension sane.
+  if ((long long)M * W->K > (1LL << 40) || (long long)M * W->N > (1LL << 40)) return AQ_ERR_SHAPE;
+  return AQ_OK;
+}
+
+int effective_split(const aq::PackedView &v, int M, int split) {
+  return split > 0 ? split : aq::decode_split(v, M);
+}
+
+}  // namespace
+
+extern "C" {
+
+int aq_abi_version(void) { return AQ_ABI_VERSION; }
+
+const char *aq_status_string(aq_status s) {
+  switch (s) {
+    case AQ_OK: return "ok";
+    case AQ_ERR_NULL: return "a required pointer is NULL";
+    case AQ_ERR_SHAPE: return "shape not compatible with the tile geometry";
+    case AQ_ERR_TILE: return "tile size not supported (GPU: b_N = 64, b_K in {64, 128})";
+    case AQ_ERR_MAP: return "labels disagree with T4/T8 or a map entry is not 4 or 8";
+    case AQ_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case AQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case AQ_ERR_HIP: return "HIP runtime error at launch";
+    case AQ_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+aq_status aq_labels_from_map(const uint8_t *zmap, int R, int C, uint8_t *labels) {
+  if (!zmap || !labels) return AQ_ERR_NULL;
+  if (R <= 0 || C <= 0) return AQ_ERR_SHAPE;
+  const long long T = (long long)R * C;
+  for (long long b = 0; b < (T + 7) / 8; ++b) labels[b] = 0;
+  for (long long t = 0; t < T; ++t) {
+    if (zmap[t] == 4) labels[t >> 3] |= (uint8_t)(1u << (t & 7));
+    else if (zmap[t] != 8) return AQ_ERR_MAP;
+  }
+  return AQ_OK;
+}
+
+aq_status aq_plan_pack(int N, int K, int bN, int bK, const uint8_t *labels, aq_plan *out) {
+  if (!labels || !out) return AQ_ERR_NULL;
+  if (bN < 1 || bK < 32 || bK % 32) return AQ_ERR_TILE;
+  if (N <= 0 || K <= 0 || N % bN || K % bK) return AQ_ERR_SHAPE;
+  const long long R = N / bN, C = K / bK, T = R * C;
+  if (T > (1LL << 30)) return AQ_ERR_SHAPE;
+  long long T4 = 0;
+  for (long long t = 0; t < T; ++t) T4 += bit_of(labels, (int)t);
+  aq_plan p;
+  p.N = N; p.K = K; p.bN = bN; p.bK = bK;
+  p.R = (int32_t)R; p.C = (int32_t)C;
+  p.T4 = (int32_t)T4; p.T8 = (int32_t)(T - T4);
+  const size_t B = (size_t)bN * bK;
+  p.labels_bytes = (size_t)((T + 7) / 8);
+  p.offs_bytes = 4 * (size_t)(R + 1);
+  p.w4_bytes = B / 2 * (size_t)p.T4;
+  p.w8_bytes = B * (size_t)p.T8;
+  p.s4_bytes = 4 * (size_t)bN * p.T4;
+  p.s8_bytes = 4 * (size_t)bN * p.T8;
+  *out = p;
+  return AQ_OK;
+}
+
+aq_status aq_pack_weights(const float *W, const uint8_t *labels_host, aq_packed *out,
+                          void *stream) {
+  if (!W || !labels_host || !out) return AQ_ERR_NULL;
+  aq_status st = check_packed(out);
+  if (st != AQ_OK) return st;
+  if (!aligned16(W)) return AQ_ERR_ALIGN;
+  aq_plan plan;
+  st = aq_plan_pack(out->N, out->K, out->bN, out->bK, labels_host, &plan);
+  if (st != AQ_OK) return st;
+  if (plan.T4 != out->T4 || plan.T8 != out->T8) return AQ_ERR_MAP;
+
+  // Row offsets (App. E.2): two INT32 arrays of length R+1.
+  std::vector<int32_t> offs;
+  try {
+    offs.resize(2 * (size_t)(plan.R + 1));
+  } catch (const std::bad_alloc &) {
+    return AQ_ERR_ARG;
+  }
+  int32_t *o4 = offs.data(), *o8 = offs.data() + plan.R + 1;
+  o4[0] = o8[0] = 0;
+  for (int r = 0; r < plan.R; ++r) {
+    int c4 = 0;
+    for (int j = 0; j < plan.C; ++j) c4 += bit_of(labels_host, r * plan.C + j);
+    o4[r + 1] = o4[r] + c4;
+    o8[r + 1] = o8[r] + (plan.C - c4);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(out->labels, labels_host, plan.labels_bytes, hipMemcpyHostToDevice, s) !=
+          hipSuccess ||
+      hipMemcpyAsync(out->row_off4, o4, plan.offs_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(out->row_off8, o8, plan.offs_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)  // host buffers are released on return
+    return AQ_ERR_HIP;
+  return aq::launch_pack(W, *out, s) == hipSuccess ? AQ_OK : AQ_ERR_HIP;
+}
+
+aq_status aq_quant_act(const float *X, int M, int K, int8_t *qx, float *sx, void *stream) {
+  if (M < 0 || K <= 0 || K % 64) return AQ_ERR_SHAPE;
+  if (M == 0) return AQ_OK;
+  if (!X || !qx || !sx) return AQ_ERR_NULL;
+  if (!aligned16(X) || !aligned16(qx) || !aligned4(sx)) return AQ_ERR_ALIGN;
+  if ((long long)M * K > (1LL << 40) || M > (1 << 30)) return AQ_ERR_SHAPE;
+  return aq::launch_quant_act(X, M, K, qx, sx, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
+int aq_decode_split(const aq_packed *W, int M) {
+  if (check_packed(W) != AQ_OK || M < 0) return 0;
+  return aq::decode_split(aq::view_of(*W), M);
+}
+
+size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split) {
+  if (check_packed(W) != AQ_OK || M <= 0) return 0;
+  if (phase != AQ_PHASE_DECODE) return 0;
+  const aq::PackedView v = aq::view_of(*W);
+  if (split < 0 || split > v.C) return 0;
+  const int S = effective_split(v, M, split);
+  if (S <= 1) return 0;
+  return (size_t)S * (size_t)M * (size_t)v.N * sizeof(float);
+}
+
+aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                           const float *bias, float *Y, int split, void *ws, size_t ws_bytes,
+                           void *stream) {
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  st = check_linear_io(W, qx, sx, M, bias, Y);
+  if (st != AQ_OK || M == 0) return st;
+  const aq::PackedView v = aq::view_of(*W);
+  if (split < 0 || split > v.C) return AQ_ERR_ARG;
+  const int S = effective_split(v, M, split);
+  if (S > 1) {
+    const size_t need = (size_t)S * (size_t)M * (size_t)v.N * sizeof(float);
+    if (!ws || ws_bytes < need) return AQ_ERR_WORKSPACE;
+    if (!aligned16(ws)) return AQ_ERR_ALIGN;
+  }
+  return aq::launch_decode(v, qx, sx, M, bias, Y, S, static_cast<float *>(ws), nullptr,
+                           static_cast<hipStream_t>(stream)) == hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
+aq_status aq_linear_prefill(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                            const float *bias, float *Y, void *ws, size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  st = check_linear_io(W, qx, sx, M, bias, Y);
+  if (st != AQ_OK || M == 0) return st;
+  return aq::launch_prefill(aq::view_of(*W), qx, sx, M, bias, Y, nullptr,
+                            static_cast<hipStream_t>(stream)) == hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
+aq_status aq_linear_tile_partials(const aq_packed *W, const int8_t *qx, int M, int phase,
+                                  int32_t *P, void *stream) {
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  if (phase != AQ_PHASE_DECODE && phase != AQ_PHASE_PREFILL) return AQ_ERR_ARG;
+  if (M < 0) return AQ_ERR_SHAPE;
+  if (M == 0) return AQ_OK;
+  if (!qx || !P) return AQ_ERR_NULL;
+  if (!aligned16(qx) || !aligned4(P)) return AQ_ERR_ALIGN;
+  const aq::PackedView v = aq::view_of(*W);
+  if ((long long)M * v.N * v.C > (1LL << 40)) return AQ_ERR_SHAPE;
+  hipError_t e = phase == AQ_PHASE_DECODE
+                     ? aq::launch_decode(v, qx, nullptr, M, nullptr, nullptr, 1, nullptr, P,
+                                         static_cast<hipStream_t>(stream))
+                     : aq::launch_prefill(v, qx, nullptr, M, nullptr, nullptr, P,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AQ_OK : AQ_ERR_HIP;
+}
+
+}  // extern "C"

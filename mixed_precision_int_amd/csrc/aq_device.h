@@ -1,0 +1,54 @@
+// Device helpers shared by the gfx950 kernels: precision labels, physical
+// tile indices and INT4 widening.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace aq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// Label of logical tile t: 1 = INT4, 0 = INT8; bit (t & 7) of byte t >> 3
+// (AlignQuant App. E.1 label order, first label in the least significant bit).
+__device__ __forceinline__ int tile_label(const uint8_t *__restrict__ labels, int t) {
+  return (labels[t >> 3] >> (t & 7)) & 1;
+}
+
+// 32 consecutive labels starting at tile t, bit k = label of tile t + k.
+// Reads only bytes below nbytes (bits past the end read as 0).
+__device__ __forceinline__ uint32_t label_bits32(const uint8_t *__restrict__ labels, int t,
+                                                 int nbytes) {
+  const int b0 = t >> 3;
+  uint64_t v = 0;
+#pragma unroll
+  for (int k = 0; k < 5; ++k)
+    if (b0 + k < nbytes) v |= (uint64_t)labels[b0 + k] << (8 * k);
+  return (uint32_t)(v >> (t & 7));
+}
+
+// Number of INT4 labels among tiles [t0, t0 + n).
+__device__ __forceinline__ int count_int4(const uint8_t *__restrict__ labels, int t0, int n,
+                                          int nbytes) {
+  int c = 0;
+  for (int k = 0; k < n; k += 32) {
+    uint32_t bits = label_bits32(labels, t0 + k, nbytes);
+    const int left = n - k;
+    if (left < 32) bits &= (1u << left) - 1u;
+    c += __popc(bits);
+  }
+  return c;
+}
+
+// INT4 widening, scaled by 16.  A 32-bit word of the packed tile holds four
+// bytes, each byte two signed nibbles (App. E.1 eq. 17: low nibble q0, high
+// nibble q1).  Masking the high nibble in place gives the int8 value 16*q1;
+// shifting the low nibble up gives 16*q0.  Both are exact two's-complement
+// int8 values, so a dot product over them is exactly 16x the dot product over
+// the codes, and the caller divides by 16 (an exact shift or a power-of-two
+// scale).  Two bit operations replace a full sign extension.
+__device__ __forceinline__ int w4_lo16(uint32_t w) { return (int)((w << 4) & 0xF0F0F0F0u); }
+__device__ __forceinline__ int w4_hi16(uint32_t w) { return (int)(w & 0xF0F0F0F0u); }
+
+}  // namespace aq

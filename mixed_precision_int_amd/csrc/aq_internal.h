@@ -1,0 +1,53 @@
+// Internal interface between the host ABI layer (aq_api.cpp) and the HIP
+// kernel launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/aq.h"
+
+namespace aq {
+
+// Geometry the GPU kernels are built for.
+constexpr int kTileRows = 64;  // b_N
+
+// Read-only view of a packed projection plus derived geometry.
+struct PackedView {
+  int N, K, bK, R, C, T4, T8;
+  const uint8_t *labels;
+  const int32_t *off4, *off8;
+  const uint8_t *w4;
+  const int8_t *w8;
+  const float *s4, *s8;
+};
+
+inline PackedView view_of(const aq_packed &p) {
+  PackedView v;
+  v.N = p.N; v.K = p.K; v.bK = p.bK;
+  v.R = p.N / kTileRows; v.C = p.K / p.bK;
+  v.T4 = p.T4; v.T8 = p.T8;
+  v.labels = p.labels; v.off4 = p.row_off4; v.off8 = p.row_off8;
+  v.w4 = p.w4; v.w8 = p.w8; v.s4 = p.s4; v.s8 = p.s8;
+  return v;
+}
+
+// Launchers.  Arguments are already validated; each returns the launch
+// status reported by hipGetLastError().
+hipError_t launch_pack(const float *W, const aq_packed &out, hipStream_t stream);
+hipError_t launch_quant_act(const float *X, int M, int K, int8_t *qx, float *sx,
+                            hipStream_t stream);
+// Decode: if S == 1 writes Y directly; else writes FP32 split partials to ws
+// ([S][M][N]) and reduces them into Y.  P != nullptr selects the debug mode
+// that writes INT32 tile products instead (S, ws, Y unused).
+hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx, int M,
+                         const float *bias, float *Y, int S, float *ws, int32_t *P,
+                         hipStream_t stream);
+hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx, int M,
+                          const float *bias, float *Y, int32_t *P, hipStream_t stream);
+
+// Adaptive decode split (host heuristic, also used for workspace sizing).
+int decode_split(const PackedView &w, int M);
+
+}  // namespace aq

@@ -1,0 +1,112 @@
+// Weight quantization and packing (AlignQuant App. B.2 eq. 5-6; App. E.1-E.2).
+//
+// One workgroup per logical tile (r, j).  BK/32 threads share a tile row;
+// thread q of row i owns the 32 consecutive columns 32q .. 32q+31, which are
+// exactly one INT4 panel or two INT8 panels of the packed layout, so every
+// thread writes whole 16-byte chunks.  Scale and code arithmetic is FP64 with
+// correctly rounded division and round-half-even, as the pages prescribe for
+// integer construction.
+
+#include "aq_device.h"
+#include "aq_internal.h"
+
+namespace aq {
+namespace {
+
+template <int BK>
+__global__ __launch_bounds__(64 * (BK / 32)) void pack_kernel(
+    const float *__restrict__ W, int K, int C, int labels_bytes,
+    const uint8_t *__restrict__ labels, const int32_t *__restrict__ off4,
+    const int32_t *__restrict__ off8, uint8_t *__restrict__ w4, int8_t *__restrict__ w8,
+    float *__restrict__ s4, float *__restrict__ s8, int T4, int T8) {
+  constexpr int TPR = BK / 32;  // threads per tile row
+  const int t = blockIdx.x;     // logical tile r*C + j
+  const int r = t / C;
+  const int j = t - r * C;
+  const int i = threadIdx.x / TPR;  // row inside the tile
+  const int q = threadIdx.x % TPR;  // 32-column chunk
+
+  // Physical index, eq. 16: stored row offset + same-precision tiles before j.
+  const int is4 = tile_label(labels, t);
+  const int n4_before = count_int4(labels, r * C, j, labels_bytes);
+  const int idx = is4 ? off4[r] + n4_before : off8[r] + (j - n4_before);
+  if (is4 ? (idx < 0 || idx >= T4) : (idx < 0 || idx >= T8)) return;  // inconsistent metadata
+
+  const size_t n = (size_t)r * kTileRows + i;
+  const float4 *src = reinterpret_cast<const float4 *>(W + n * K + (size_t)j * BK + q * 32);
+  float v[32];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float4 f = src[e];
+    v[4 * e + 0] = f.x; v[4 * e + 1] = f.y; v[4 * e + 2] = f.z; v[4 * e + 3] = f.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+  for (int o = 1; o < TPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+
+  const double qmax = is4 ? 7.0 : 127.0;
+  const double qmin = is4 ? -8.0 : -128.0;
+  const double s = fmax((double)amax / qmax, 1e-12);
+  int code[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    double c = rint((double)v[e] / s);
+    c = fmin(fmax(c, qmin), qmax);
+    code[e] = (int)c;
+  }
+
+  if (!is4) {
+    int8_t *tile = w8 + (size_t)idx * kTileRows * BK;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // panels 2q and 2q+1
+      uint32_t word[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        word[b] = (uint32_t)(code[16 * h + 4 * b + 0] & 0xFF) |
+                  ((uint32_t)(code[16 * h + 4 * b + 1] & 0xFF) << 8) |
+                  ((uint32_t)(code[16 * h + 4 * b + 2] & 0xFF) << 16) |
+                  ((uint32_t)(code[16 * h + 4 * b + 3] & 0xFF) << 24);
+      *reinterpret_cast<uint4 *>(tile + (size_t)(2 * q + h) * kTileRows * 16 + i * 16) =
+          make_uint4(word[0], word[1], word[2], word[3]);
+    }
+    if (q == 0) s8[(size_t)idx * kTileRows + i] = (float)s;
+  } else {
+    uint8_t *tile = w4 + (size_t)idx * kTileRows * BK / 2;
+    uint32_t word[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      uint32_t wv = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * b + e;  // byte k packs columns k (low) and k + 16 (high)
+        const uint32_t byte = (uint32_t)(code[k] & 0xF) | ((uint32_t)(code[k + 16] & 0xF) << 4);
+        wv |= byte << (8 * e);
+      }
+      word[b] = wv;
+    }
+    *reinterpret_cast<uint4 *>(tile + (size_t)q * kTileRows * 16 + i * 16) =
+        make_uint4(word[0], word[1], word[2], word[3]);
+    if (q == 0) s4[(size_t)idx * kTileRows + i] = (float)s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack(const float *W, const aq_packed &out, hipStream_t stream) {
+  const int R = out.N / kTileRows, C = out.K / out.bK;
+  const int T = R * C;
+  const int labels_bytes = (T + 7) / 8;
+  if (out.bK == 128)
+    hipLaunchKernelGGL(pack_kernel<128>, dim3(T), dim3(256), 0, stream, W, out.K, C, labels_bytes,
+                       out.labels, out.row_off4, out.row_off8, out.w4, out.w8, out.s4, out.s8,
+                       out.T4, out.T8);
+  else
+    hipLaunchKernelGGL(pack_kernel<64>, dim3(T), dim3(128), 0, stream, W, out.K, C, labels_bytes,
+                       out.labels, out.row_off4, out.row_off8, out.w4, out.w8, out.s4, out.s8,
+                       out.T4, out.T8);
+  return hipGetLastError();
+}
+
+}  // namespace aq

@@ -27,3 +27,13 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(scope="session")
+def aqlib():
+    """The built libaq.so (built in-tree first only if it is missing)."""
+    from mixed_precision_int_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from mixed_precision_int_amd import build
+        build.build()
+    return binding.lib()

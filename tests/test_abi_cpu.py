@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid calls on the host before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from mixed_precision_int_amd import binding as B
+from oracle import aq_oracle as O
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "aq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(aq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(aqlib):
+    names = declared_functions()
+    assert len(names) >= 11
+    missing = [n for n in names if not hasattr(aqlib, n)]
+    assert not missing, missing
+    assert sorted(B.EXPORTS) == names
+
+
+def test_abi_version_and_status_strings(aqlib):
+    assert B.aq_abi_version() == 1
+    for code in list(B.STATUS) + [-99]:
+        assert aqlib.aq_status_string(code)
+
+
+def test_labels_match_oracle(aqlib):
+    rng = np.random.default_rng(0)
+    for R, C in [(1, 1), (3, 5), (4, 4), (7, 13), (96, 20)]:
+        z = rng.choice([4, 8], size=(R, C))
+        assert np.array_equal(B.aq_labels_from_map(z), O.labels_from_map(z))
+    with pytest.raises(B.AqError) as e:
+        B.aq_labels_from_map(np.array([[4, 5]]))
+    assert e.value.status == -4
+
+
+def test_plan_sizes_match_oracle_pack(aqlib):
+    rng = np.random.default_rng(1)
+    for N, K, bN, bK in [(256, 512, 64, 128), (192, 640, 64, 64), (6, 96, 3, 32)]:
+        z = rng.choice([4, 8], size=(N // bN, K // bK))
+        lab = O.labels_from_map(z)
+        p = B.aq_plan_pack(N, K, bN, bK, lab)
+        pk = O.pack(np.zeros((N, K), np.int64), np.zeros((N, K // bK), np.float32), z, bN, bK)
+        assert (p.T4, p.T8) == (pk["T4"], pk["T8"])
+        assert p.w4_bytes == pk["w4"].size and p.w8_bytes == pk["w8"].size
+        assert p.s4_bytes == 4 * pk["s4"].size and p.s8_bytes == 4 * pk["s8"].size
+        assert p.labels_bytes == lab.size and p.offs_bytes == 4 * pk["row_off4"].size
+        # eq. 18 with per-row scales, term by term
+        total = p.labels_bytes + 2 * p.offs_bytes + p.w4_bytes + p.w8_bytes + p.s4_bytes + p.s8_bytes
+        assert total == O.packed_bytes_rowscale(p.T4, p.T8, p.R, p.C, bN, bK)
+    with pytest.raises(B.AqError):
+        B.aq_plan_pack(256, 512, 64, 48, np.zeros(2, np.uint8))       # bK not a multiple of 32
+    with pytest.raises(B.AqError):
+        B.aq_plan_pack(250, 512, 64, 128, np.zeros(2, np.uint8))      # N % bN
+
+
+FAKE = 1 << 20   # 16-byte-aligned fake device address; never dereferenced
+
+
+def fake_packed(N=256, K=512, bK=128, T4=8, T8=8, **over):
+    d = B.AqPacked(N, K, 64, bK, T4, T8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def decode(d, qx=FAKE, sx=FAKE, M=4, bias=None, Y=FAKE, split=1, ws=None, ws_bytes=0):
+    return B.lib().aq_linear_decode(ctypes.byref(d), qx, sx, M, bias, Y, split, ws, ws_bytes, None)
+
+
+def prefill(d, qx=FAKE, sx=FAKE, M=4, bias=None, Y=FAKE):
+    return B.lib().aq_linear_prefill(ctypes.byref(d), qx, sx, M, bias, Y, None, 0, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(bN=32), -3), (dict(bK=96), -3), (dict(N=250), -2),
+    (dict(T4=9), -4), (dict(T8=-1), -4), (dict(labels=None), -1), (dict(w8=None), -1),
+    (dict(s4=None), -1), (dict(w8=FAKE + 8), -5), (dict(s4=FAKE + 4), -5),
+])
+def test_packed_descriptor_rejected(aqlib, over, code):
+    d = fake_packed(**over)
+    assert decode(d) == code
+    assert prefill(d) == code
+
+
+def test_io_rejected(aqlib):
+    d = fake_packed()
+    assert decode(d, M=-1) == -2
+    assert decode(d, M=0) == 0 and prefill(d, M=0) == 0        # no-op, nothing launched
+    assert decode(d, qx=None) == -1 and prefill(d, Y=None) == -1
+    assert decode(d, qx=FAKE + 1) == -5 and prefill(d, Y=FAKE + 4) == -5
+    assert decode(d, bias=FAKE + 4) == -5
+    assert decode(d, split=5) == -8                              # C = 4 tile columns
+    # split 2 needs 2 * M * N * 4 bytes of workspace
+    need = B.lib().aq_workspace_bytes(ctypes.byref(d), 4, 0, 2)
+    assert need == 2 * 4 * 256 * 4
+    assert decode(d, split=2, ws=None, ws_bytes=0) == -6
+    assert decode(d, split=2, ws=FAKE, ws_bytes=need - 1) == -6
+    assert decode(d, split=2, ws=FAKE + 8, ws_bytes=need) == -5
+    assert B.lib().aq_workspace_bytes(ctypes.byref(d), 4, 1, 0) == 0   # prefill needs none
+
+
+def test_quant_act_and_partials_rejected(aqlib):
+    L = B.lib()
+    assert L.aq_quant_act(FAKE, 4, 100, FAKE, FAKE, None) == -2     # K % 64
+    assert L.aq_quant_act(FAKE, -1, 128, FAKE, FAKE, None) == -2
+    assert L.aq_quant_act(FAKE, 0, 128, FAKE, FAKE, None) == 0
+    assert L.aq_quant_act(None, 4, 128, FAKE, FAKE, None) == -1
+    assert L.aq_quant_act(FAKE + 4, 4, 128, FAKE, FAKE, None) == -5
+    d = fake_packed()
+    assert L.aq_linear_tile_partials(ctypes.byref(d), FAKE, 4, 2, FAKE, None) == -8
+    assert L.aq_linear_tile_partials(ctypes.byref(d), None, 4, 0, FAKE, None) == -1
+    assert L.aq_linear_tile_partials(ctypes.byref(d), FAKE, 0, 1, FAKE, None) == 0
+
+
+def test_pack_rejects_label_mismatch(aqlib):
+    lab = O.labels_from_map(np.full((4, 4), 4))                    # 16 INT4 tiles
+    d = fake_packed(T4=8, T8=8)
+    assert B.lib().aq_pack_weights(FAKE, lab.ctypes.data, ctypes.byref(d), None) == -4
+    assert B.lib().aq_pack_weights(FAKE + 4, lab.ctypes.data, ctypes.byref(d), None) == -5
+
+
+def test_adaptive_split_bounds(aqlib):
+    for N, K in [(256, 512), (5120, 3072), (16384, 3072), (3072, 8192), (2560, 9728)]:
+        R, C = N // 64, K // 128
+        d = fake_packed(N=N, K=K, T4=R * C, T8=0)
+        S = B.lib().aq_decode_split(ctypes.byref(d), 1)
+        assert 1 <= S <= C

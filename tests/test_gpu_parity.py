@@ -1,0 +1,134 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  The bar is stated in tests/parity.py."""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_int_amd as aq
+from tests.parity import Case, say
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _ragged(N, K, bK, M, seed, frac8=0.5, outliers=3):
+    rng = np.random.default_rng(seed)
+    W = gen.weights(rng, N, K)
+    z = gen.map_uniform(rng, N // 64, K // bK, frac8)
+    X = gen.acts_outliers(rng, M, K, outliers, 20.0)
+    return W, z, X
+
+
+def test_small_workload_all_stages():
+    d = gen.small()
+    c = Case(d["W"], d["zmap"], d["X"], d["bN"], d["bK"], name="small")
+    c.check_all(splits=(0, 1, 2, 3, 4))
+
+
+def test_small_workload_with_bias():
+    d = gen.small()
+    b = np.random.default_rng(7).standard_normal(256).astype(np.float32)
+    Case(d["W"], d["zmap"], d["X"], bias=b, name="small+bias").check_all(splits=(0, 1, 4))
+
+
+@pytest.mark.parametrize("N,K,bK,M", [
+    (64, 128, 128, 1),       # one tile, one token
+    (192, 4736, 128, 17),    # odd tile-row count, 37 tile columns (> 32), ragged M
+    (256, 512, 64, 4),       # the pages' 64 x 64 tiles
+    (128, 640, 64, 1),
+    (384, 2304, 64, 33),     # 36 tile columns at 64 x 64
+    (320, 1024, 128, 65),    # M spans two 64-token decode passes
+    (256, 512, 128, 130),    # M spans two 128-token prefill blocks, ragged
+    (512, 1536, 128, 200),
+])
+def test_ragged_shapes(N, K, bK, M):
+    W, z, X = _ragged(N, K, bK, M, seed=N * 7 + K + M)
+    Case(W, z, X, 64, bK, name=f"ragged{N}x{K}/bK{bK}/M{M}").check_all(splits=(0, 1, 2))
+
+
+@pytest.mark.parametrize("kind", ["all_int4", "all_int8", "checker", "zero_rows"])
+def test_uniform_and_degenerate_maps(kind):
+    rng = np.random.default_rng(11)
+    N, K, M = 256, 1024, 9
+    W = gen.weights(rng, N, K)
+    X = gen.acts_outliers(rng, M, K, 4, 30.0)
+    R, C = N // 64, K // 128
+    if kind == "all_int4":
+        z = np.full((R, C), 4)
+    elif kind == "all_int8":
+        z = np.full((R, C), 8)
+    else:
+        z = np.where((np.add.outer(np.arange(R), np.arange(C)) % 2) == 0, 4, 8)
+    if kind == "zero_rows":
+        W[3, :] = 0.0            # every tile row of output 3 is zero: scale 1e-12
+        W[70, 128:256] = 0.0     # one zero row segment inside a tile
+        X[2, :] = 0.0            # a zero token: scale 1e-12, codes 0
+    Case(W, z, X, name=kind).check_all(splits=(0, 1))
+
+
+def test_extreme_codes_and_ties():
+    """Weights and activations that hit +-q_max exactly and round at .5."""
+    N, K, M = 128, 256, 3
+    W = np.zeros((N, K), np.float32)
+    W[:, ::7] = 7.0
+    W[:, 1::7] = -2.5
+    W[:, 2::7] = 0.5
+    W[:, 3::7] = -7.0
+    X = np.zeros((M, K), np.float32)
+    X[:, ::5] = 127.0
+    X[:, 1::5] = -0.5
+    X[:, 2::5] = 2.5
+    X[:, 3::5] = -127.0
+    z = np.array([[4, 8], [8, 4]])
+    Case(W, z, X, name="ties").check_all(splits=(0, 1))
+
+
+@pytest.mark.parametrize("proj", [p[0] for p in gen.LLAMA3B])
+def test_llama3b_decode_linears(proj):
+    for M in (1, 4, 16):
+        d = gen.llama3b_decode(proj, M)
+        Case(d["W"], d["zmap"], d["X"], name=d["name"]).check_all(splits=(0,))
+
+
+@pytest.mark.parametrize("proj", [p[0] for p in gen.QWEN4B])
+def test_qwen4b_prefill_linears_sampled_rows(proj):
+    """Full M = 2048 through both kernels in the benchmarked launch shape;
+    outputs and tile products compared on 48 sampled token rows (every
+    128-row block boundary region, the last row included)."""
+    d = gen.qwen4b_prefill(proj, 2048)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 127, 128, 1023, 2047], rng.choice(2048, 43, replace=False)]))
+    c = Case(d["W"], d["zmap"], d["X"], name=d["name"])
+    ref = c.ref(rows)
+    c.check_all(rows=rows, phases=("prefill",))
+    # the whole 2048-row call, then the sampled rows of its output
+    qx_d, sx_d = c.qx_d, c.sx_d
+    Y = aq.aq_linear_prefill(c.pw, qx_d, sx_d)
+    torch.cuda.synchronize()
+    from tests.parity import assert_output_close
+    assert_output_close(Y.cpu().numpy()[rows], ref["y_rows"], ref["c_rows"], c.name + "/full-M")
+
+
+def test_determinism_bitwise():
+    d = gen.llama3b_decode("down", 16)
+    c = Case(d["W"], d["zmap"], d["X"], name="determinism")
+    pw = c.gpu_pack()
+    qx, sx = c.gpu_quant()
+    a1 = aq.aq_linear_decode(pw, qx, sx).cpu()
+    a2 = aq.aq_linear_decode(pw, qx, sx).cpu()
+    p1 = aq.aq_linear_prefill(pw, qx, sx).cpu()
+    p2 = aq.aq_linear_prefill(pw, qx, sx).cpu()
+    assert torch.equal(a1.view(torch.int32), a2.view(torch.int32))
+    assert torch.equal(p1.view(torch.int32), p2.view(torch.int32))
+    # the two phases agree to the output tolerance
+    say("  decode vs prefill max rel diff",
+        float((a1 - p1).abs().max() / p1.abs().max()))
+    assert float((a1 - p1).abs().max()) <= 1e-4 * float(p1.abs().max())
+
+
+def test_repeated_calls_split_independent():
+    """Every split count gives the same tile products and outputs within the
+    bar; the workspace is reused across calls."""
+    d = gen.llama3b_decode("qkv", 4)
+    c = Case(d["W"], d["zmap"], d["X"], name="splits")
+    c.check_all(splits=(1, 2, 5, 24, 0), phases=("decode",))
