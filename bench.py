@@ -1,0 +1,298 @@
+"""Benchmark of the tile-aligned W4/W8 x A8 linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  decode  : activation quantization + decode linear for the four
+            Llama-3.2-3B-shaped projections (fused qkv 5120x3072, o 3072x3072,
+            fused gate_up 16384x3072, down 3072x8192; 25% INT8 tiles) at
+            M = 1, 4 and 16 tokens (12 calls); every call reads a different
+            copy of the packed weights (24 copies, 1.6 GB) so the weights
+            come from HBM, not from the 256 MB last-level cache;
+  prefill : activation quantization + prefill linear for the four
+            Qwen3-4B-shaped projections (qkv 6144x2560, o 2560x4096,
+            gate_up 19456x2560, down 2560x9728; 30% INT8 tiles in bands) at
+            M = 2048 tokens.
+Inputs are resident in HBM before the timed region.  W warm-up steps, then K
+timed steps between device synchronizations; HIP events recorded on the
+launch stream time each segment and each linear call.
+
+The JSON line: value = decode HBM GB/s over the decode segment (algorithmic
+bytes: packed weights with per-row scales, labels, row offsets, INT8
+activations and their scales, FP32 outputs; activation quantization time is
+inside the segment); prefill.value = INT8 TOPS over the prefill segment
+(2 M N K per call); roofline objects for the decode kernel (HBM-bound) and
+the prefill kernel (MFMA-bound) from the per-call event durations;
+cpu_baseline = the CPU oracle on a bounded sample, single-threaded.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode linear HBM GB/s (% of peak) + prefill int8 TOPS (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA, published (no sparsity)
+DECODE_M = (1, 4, 16)
+PREFILL_M = 2048
+N_COPIES = 24
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def linear_bytes(plan, M: int) -> int:
+    """Algorithmic bytes of one linear call: the packed projection with
+    per-row scales, INT8 activations + FP32 scales, FP32 outputs."""
+    packed = (plan.labels_bytes + 2 * plan.offs_bytes + plan.w4_bytes + plan.w8_bytes
+              + plan.s4_bytes + plan.s8_bytes)
+    return int(packed + M * plan.K + 4 * M + 4 * M * plan.N)
+
+
+def clone_packed(aq, pw):
+    """A second device copy of a packed projection (same bytes)."""
+    t = {k: getattr(pw, k).clone() for k in ("labels", "row_off4", "row_off8", "w4", "w8", "s4", "s8")}
+    d = aq.AqPacked(pw.plan.N, pw.plan.K, pw.plan.bN, pw.plan.bK, pw.plan.T4, pw.plan.T8,
+                    *(t[k].data_ptr() for k in ("labels", "row_off4", "row_off8", "w4", "w8", "s4", "s8")))
+    return aq.PackedWeights(plan=pw.plan, labels_host=pw.labels_host, desc=d, **t)
+
+
+def setup(aq, gen, torch):
+    dev = torch.device("cuda", 0)
+    dec = []   # (name, [packed copies], {M: X}, {M: (qx, sx, Y)})
+    for proj, N, K in gen.LLAMA3B:
+        d = gen.llama3b_decode(proj, max(DECODE_M))
+        labels = aq.aq_labels_from_map(d["zmap"].astype(np.uint8))
+        pw = aq.aq_pack_weights(torch.from_numpy(d["W"]).to(dev), labels, 64, 128)
+        copies = [pw] + [clone_packed(aq, pw) for _ in range(N_COPIES - 1)]
+        xs, bufs = {}, {}
+        for M in DECODE_M:
+            x = gen.llama3b_decode(proj, M)["X"]
+            xs[M] = torch.from_numpy(x).to(dev)
+            bufs[M] = (torch.empty((M, K), dtype=torch.int8, device=dev),
+                       torch.empty((M,), dtype=torch.float32, device=dev),
+                       torch.empty((M, N), dtype=torch.float32, device=dev))
+        dec.append((proj, copies, xs, bufs))
+    ws_need = max(aq.aq_workspace_bytes(c[1][0], M, aq.AQ_PHASE_DECODE) for c in dec for M in DECODE_M)
+    ws = torch.zeros(max(ws_need, 16), dtype=torch.uint8, device=dev)  # counters start at zero
+    pre = []
+    for proj, N, K in gen.QWEN4B:
+        d = gen.qwen4b_prefill(proj, PREFILL_M)
+        labels = aq.aq_labels_from_map(d["zmap"].astype(np.uint8))
+        pw = aq.aq_pack_weights(torch.from_numpy(d["W"]).to(dev), labels, 64, 128)
+        x = torch.from_numpy(d["X"]).to(dev)
+        bufs = (torch.empty((PREFILL_M, K), dtype=torch.int8, device=dev),
+                torch.empty((PREFILL_M,), dtype=torch.float32, device=dev),
+                torch.empty((PREFILL_M, N), dtype=torch.float32, device=dev))
+        pre.append((proj, pw, x, bufs))
+    torch.cuda.synchronize()
+    return dec, ws, pre
+
+
+class Recorder:
+    """HIP events on the launch stream around segments and calls."""
+
+    def __init__(self, torch, enabled):
+        self.torch, self.enabled = torch, enabled
+        self.calls = {"decode": [], "prefill": []}   # (start, end, units)
+        self.segs = {"decode": [], "prefill": []}
+
+    def ev(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def totals(self, kind):
+        self.torch.cuda.synchronize()
+        seg_ms = sum(a.elapsed_time(b) for a, b in self.segs[kind])
+        call_ms = sum(a.elapsed_time(b) for a, b, _ in self.calls[kind])
+        units = sum(u for _, _, u in self.calls[kind])
+        return seg_ms, call_ms, units, len(self.calls[kind])
+
+
+def run_step(aq, i, dec, ws, pre, rec: Recorder | None):
+    ws_bytes = ws.numel()
+    # ---- decode segment
+    s0 = rec.ev() if rec else None
+    for mi, M in enumerate(DECODE_M):
+        c = (i * len(DECODE_M) + mi) % N_COPIES
+        for proj, copies, xs, bufs in dec:
+            qx, sx, Y = bufs[M]
+            aq.aq_quant_act(xs[M], qx, sx)
+            pw = copies[c]
+            if rec:
+                a = rec.ev()
+            aq.aq_linear_decode(pw, qx, sx, None, 0, Y, ws)
+            if rec:
+                rec.calls["decode"].append((a, rec.ev(), linear_bytes(pw.plan, M)))
+    if rec:
+        s1 = rec.ev()
+        rec.segs["decode"].append((s0, s1))
+    # ---- prefill segment
+    for proj, pw, x, (qx, sx, Y) in pre:
+        aq.aq_quant_act(x, qx, sx)
+        if rec:
+            a = rec.ev()
+        aq.aq_linear_prefill(pw, qx, sx, None, Y)
+        if rec:
+            rec.calls["prefill"].append((a, rec.ev(), 2 * PREFILL_M * pw.plan.N * pw.plan.K))
+    if rec:
+        rec.segs["prefill"].append((s1, rec.ev()))
+    del ws_bytes
+
+
+def cpu_baseline(budget_s: float):
+    """The CPU oracle as it stands, single-threaded, on a bounded sample:
+    decode linears of the Llama-3.2-3B shapes (activation quantization, INT32
+    tile products, FP64 rescale) at M = 1, 4, 16, repeated until the budget;
+    prefill on 64 token rows x all outputs of each Qwen3-4B-shaped
+    projection."""
+    from threadpoolctl import threadpool_limits
+    from oracle import aq_oracle as O
+    from workloads import gen
+
+    with threadpool_limits(limits=1):
+        prep = []
+        for proj, N, K in gen.LLAMA3B:
+            d = gen.llama3b_decode(proj, max(DECODE_M))
+            codes, sW = O.quant_weights(d["W"], d["zmap"], 64, 128)
+            pk_bytes = O.packed_bytes_rowscale(int((d["zmap"] == 4).sum()), int((d["zmap"] == 8).sum()),
+                                               N // 64, K // 128, 64, 128)
+            xs = {M: gen.llama3b_decode(proj, M)["X"] for M in DECODE_M}
+            prep.append((N, K, codes, sW, pk_bytes, xs))
+        nbytes, t_dec, reps = 0, 0.0, 0
+        while t_dec < budget_s * 0.6 or reps == 0:
+            for N, K, codes, sW, pk_bytes, xs in prep:
+                for M in DECODE_M:
+                    t0 = time.perf_counter()
+                    qx, sx = O.quant_act(xs[M])
+                    O.linear_from_partials(O.tile_partials(qx, codes, 128), sx, sW)
+                    t_dec += time.perf_counter() - t0
+                    nbytes += pk_bytes + M * K + 4 * M + 4 * M * N
+            reps += 1
+        ops, t_pre = 0, 0.0
+        for proj, N, K in gen.QWEN4B:
+            d = gen.qwen4b_prefill(proj, 64)
+            codes, sW = O.quant_weights(d["W"], d["zmap"], 64, 128)
+            t0 = time.perf_counter()
+            qx, sx = O.quant_act(d["X"])
+            O.linear_from_partials(O.tile_partials(qx, codes, 128), sx, sW)
+            t_pre += time.perf_counter() - t0
+            ops += 2 * 64 * N * K
+    return dict(
+        value=round(nbytes / t_dec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+        sample=(f"decode linears of the 4 Llama-3.2-3B-shaped projections at M=1,4,16, "
+                f"{reps} pass(es), {t_dec:.1f} s; numpy FP64 oracle, 1 thread"),
+        prefill=dict(value=round(ops / t_pre / 1e12, 6), unit="TOPS",
+                     sample=f"64 token rows x all outputs of the 4 Qwen3-4B-shaped projections, {t_pre:.1f} s"),
+        host_cores_available=len(os.sched_getaffinity(0)),
+    )
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a "
+                                   "design note, not implemented", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import mixed_precision_int_amd as aq
+    from workloads import gen
+
+    torch.cuda.set_device(0)
+    aq.lib()
+    dec, ws, pre = setup(aq, gen, torch)
+
+    for i in range(args.warmup):
+        run_step(aq, i, dec, ws, pre, None)
+    torch.cuda.synchronize()
+
+    rec = Recorder(torch, True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(aq, args.warmup + i, dec, ws, pre, rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    dseg, dcall, dbytes, ncalls_d = rec.totals("decode")
+    pseg, pcall, pops, ncalls_p = rec.totals("prefill")
+    decode_gbs = dbytes / (dseg * 1e-3) / 1e9
+    prefill_tops = pops / (pseg * 1e-3) / 1e12
+    dk_gbs = dbytes / (dcall * 1e-3) / 1e9
+    pk_tops = pops / (pcall * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(decode_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded random weights and activations of the stated shapes)",
+        "config": {
+            "workload": ("decode: Llama-3.2-3B-shaped linears qkv 5120x3072, o 3072x3072, "
+                         "gate_up 16384x3072, down 3072x8192, 25% INT8 tiles, M in {1,4,16}; "
+                         "prefill: Qwen3-4B-shaped linears qkv 6144x2560, o 2560x4096, "
+                         "gate_up 19456x2560, down 2560x9728, 30% INT8 tiles, M=2048"),
+            "tile": [64, 128],
+            "decode_weight_copies": N_COPIES,
+        },
+        "roofline": {
+            "kernel": "aq_linear_decode",
+            "bound": "hbm",
+            "achieved": round(dk_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dk_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_call_us": round(dcall * 1e3 / max(ncalls_d, 1), 3),
+            "bytes_per_step": dbytes // args.steps,
+        },
+        "prefill": {
+            "value": round(prefill_tops, 2),
+            "unit": "TOPS",
+            "roofline": {
+                "kernel": "aq_linear_prefill",
+                "bound": "mfma",
+                "achieved": round(pk_tops, 2),
+                "peak": INT8_PEAK_TOPS,
+                "unit": "TOPS",
+                "frac": round(pk_tops / INT8_PEAK_TOPS, 4),
+                "traffic": None,
+                "avg_call_us": round(pcall * 1e3 / max(ncalls_p, 1), 3),
+            },
+        },
+        "segments_ms_per_step": {"decode": round(dseg / args.steps, 4),
+                                 "prefill": round(pseg / args.steps, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,6 +31,8 @@
  * pages' CUTLASS order being specific to NVIDIA tensor cores)
  *  - labels  : ceil(R*C/8) bytes; tile t = r*C + j is bit (t & 7) of byte
  *              t >> 3 (first label in the least significant bit); 1 = INT4.
+ *              The device buffer is padded with zero bytes to a whole number
+ *              of 32-bit words (aq_plan.labels_alloc) so kernels read words.
  *  - row_off4, row_off8 : INT32[R+1]; number of INT4 (INT8) tiles in tile
  *              rows before r.  Tile (r, j) of precision b sits at
  *              index_b(r, j) = row_off_b[r] + (tiles of precision b before
@@ -75,7 +77,9 @@ typedef struct aq_plan {
   int32_t N, K, bN, bK;   /* projection and tile geometry                    */
   int32_t R, C;           /* tile rows N/bN and tile columns K/bK            */
   int32_t T4, T8;         /* INT4 and INT8 tile counts, T4 + T8 = R*C        */
-  size_t labels_bytes;    /* ceil(R*C/8)                                     */
+  size_t labels_bytes;    /* ceil(R*C/8): the label bytes of App. E.2        */
+  size_t labels_alloc;    /* 4*ceil(R*C/32): device allocation of the labels,
+                             padded to whole 32-bit words (padding is zero)  */
   size_t offs_bytes;      /* 4*(R+1), for each of row_off4 and row_off8      */
   size_t w4_bytes, w8_bytes;  /* T4*bN*bK/2 and T8*bN*bK                     */
   size_t s4_bytes, s8_bytes;  /* 4*T4*bN and 4*T8*bN                         */
@@ -86,7 +90,7 @@ typedef struct aq_plan {
  * them.  w4/s4 may be NULL when T4 == 0, w8/s8 when T8 == 0. */
 typedef struct aq_packed {
   int32_t N, K, bN, bK, T4, T8;
-  uint8_t *labels;        /* device, labels_bytes                           */
+  uint8_t *labels;        /* device, labels_alloc (4-byte aligned)          */
   int32_t *row_off4;      /* device, R+1                                    */
   int32_t *row_off8;      /* device, R+1                                    */
   uint8_t *w4;            /* device, w4_bytes                               */
@@ -126,8 +130,10 @@ aq_status aq_plan_pack(int N, int K, int bN, int bK, const uint8_t *labels_host,
  *               has passed this call.
  *   labels_host host, ceil(R*C/8) bytes; T4 / T8 in *out must match them.
  *   out         geometry (N, K, bN, bK, T4, T8) and device buffers, sized by
- *               aq_plan_pack.  labels and row offsets are copied in from the
- *               host (the host copy may be reused when this call returns).
+ *               aq_plan_pack.  labels (zero-padded to labels_alloc) and row
+ *               offsets are copied in from the host; this call synchronizes
+ *               `stream` once after those copies, so the host copy may be
+ *               reused when it returns.
  */
 aq_status aq_pack_weights(const float *W, const uint8_t *labels_host, aq_packed *out, void *stream);
 
@@ -141,26 +147,34 @@ aq_status aq_quant_act(const float *X, int M, int K, int8_t *qx, float *sx, void
 
 /* Device workspace, in bytes, that aq_linear_decode (phase 0) or
  * aq_linear_prefill (phase 1) needs for M rows with the given decode split
- * (0 = adaptive).  0 means no workspace is needed. */
+ * (0 = adaptive).  0 means no workspace is needed (the case for both phases
+ * in this version; the arguments are kept so that callers size and pass a
+ * workspace uniformly). */
 size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split);
 
-/* Split count that aq_linear_decode uses for `split` = 0 (adaptive split
- * over input-tile columns, chosen from the projection geometry). */
+/* Split count that aq_linear_decode uses for `split` = 0: the number of
+ * input-column groups each 16-row output group is divided into (adaptive,
+ * chosen from the projection geometry). */
 int aq_decode_split(const aq_packed *W, int M);
 
 /* Memory-bound phase (Sec. 3.3 "Decode parallelism"; App. E.3 Table 5):
  *   Y[m,n] = sx[m] * sum_j sW[n,j] * P[m,n,j]  (+ bias[n]),
  * P[m,n,j] the INT32 product of the INT8 activation codes and the tile's
- * codes widened to INT8 (eq. 19).  Work is spread over output-tile rows and
- * `split` groups of input-tile columns: split s covers tile columns
- * floor(C*s/S) .. floor(C*(s+1)/S)-1 and the FP32 partials of the splits are
- * summed in increasing s (App. E.3).
+ * codes widened to INT8 (eq. 19).  Work is spread over output features and
+ * input-column groups: each 16-row output group is divided into S splits,
+ * split s covering input-tile columns floor(C*s/S) .. floor(C*(s+1)/S)-1,
+ * and the FP32 partials of the splits are summed in increasing s (App. E.3)
+ * inside the same kernel launch.
  *   qx    device INT8 [M][K] (from aq_quant_act);  sx device FP32 [M]
  *   bias  device FP32 [N] or NULL
  *   Y     device FP32 [M][N] row-major (written, not accumulated)
- *   split 0 = adaptive (aq_decode_split), else 1..C
+ *   split 0 = adaptive (aq_decode_split); otherwise S, which must be one of
+ *         Wv, Wv/2, Wv/4 with Wv = 16 when M <= 32 and 8 above (other
+ *         values return AQ_ERR_ARG)
  *   ws    device workspace of at least aq_workspace_bytes(W, M, 0, split)
- * Any M >= 1 is accepted; M == 0 is a no-op. */
+ *         bytes (currently 0: NULL is accepted)
+ * Any M >= 1 is accepted (tokens are processed 64 at a time); M == 0 is a
+ * no-op. */
 aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx, int M,
                            const float *bias, float *Y, int split, void *ws, size_t ws_bytes,
                            void *stream);

@@ -39,7 +39,8 @@ class AqPlan(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32), ("bN", ctypes.c_int32),
                 ("bK", ctypes.c_int32), ("R", ctypes.c_int32), ("C", ctypes.c_int32),
                 ("T4", ctypes.c_int32), ("T8", ctypes.c_int32),
-                ("labels_bytes", ctypes.c_size_t), ("offs_bytes", ctypes.c_size_t),
+                ("labels_bytes", ctypes.c_size_t), ("labels_alloc", ctypes.c_size_t),
+                ("offs_bytes", ctypes.c_size_t),
                 ("w4_bytes", ctypes.c_size_t), ("w8_bytes", ctypes.c_size_t),
                 ("s4_bytes", ctypes.c_size_t), ("s8_bytes", ctypes.c_size_t)]
 
@@ -167,7 +168,7 @@ def _dev_bytes(n: int, device):
 
 
 def aq_alloc_packed(plan: AqPlan, labels: np.ndarray, device="cuda") -> PackedWeights:
-    t = dict(labels=_dev_bytes(plan.labels_bytes, device), row_off4=_dev_bytes(plan.offs_bytes, device),
+    t = dict(labels=_dev_bytes(plan.labels_alloc, device), row_off4=_dev_bytes(plan.offs_bytes, device),
              row_off8=_dev_bytes(plan.offs_bytes, device), w4=_dev_bytes(plan.w4_bytes, device),
              w8=_dev_bytes(plan.w8_bytes, device), s4=_dev_bytes(plan.s4_bytes, device),
              s8=_dev_bytes(plan.s8_bytes, device))
@@ -217,7 +218,7 @@ def aq_linear_decode(pw: PackedWeights, qx, sx, bias=None, split: int = 0, out=N
         out = torch.empty((M, pw.N), dtype=torch.float32, device=qx.device)
     need = aq_workspace_bytes(pw, M, AQ_PHASE_DECODE, split)
     if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=qx.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=qx.device)  # counters start at zero
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().aq_linear_decode(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias),
                                   _ptr(out), split, _ptr(ws), ws_bytes, _stream(stream)),

@@ -34,6 +34,7 @@ aq_status check_packed(const aq_packed *W) {
   const long long T = (long long)(W->N / W->bN) * (W->K / W->bK);
   if (W->T4 < 0 || W->T8 < 0 || (long long)W->T4 + W->T8 != T) return AQ_ERR_MAP;
   if (!W->labels || !W->row_off4 || !W->row_off8) return AQ_ERR_NULL;
+  if (!aligned4(W->labels)) return AQ_ERR_ALIGN;
   if (W->T4 > 0 && (!W->w4 || !W->s4)) return AQ_ERR_NULL;
   if (W->T8 > 0 && (!W->w8 || !W->s8)) return AQ_ERR_NULL;
   if (!aligned4(W->row_off4) || !aligned4(W->row_off8)) return AQ_ERR_ALIGN;
@@ -105,6 +106,7 @@ aq_status aq_plan_pack(int N, int K, int bN, int bK, const uint8_t *labels, aq_p
   p.T4 = (int32_t)T4; p.T8 = (int32_t)(T - T4);
   const size_t B = (size_t)bN * bK;
   p.labels_bytes = (size_t)((T + 7) / 8);
+  p.labels_alloc = 4 * (size_t)((T + 31) / 32);
   p.offs_bytes = 4 * (size_t)(R + 1);
   p.w4_bytes = B / 2 * (size_t)p.T4;
   p.w8_bytes = B * (size_t)p.T8;
@@ -125,13 +127,19 @@ aq_status aq_pack_weights(const float *W, const uint8_t *labels_host, aq_packed 
   if (st != AQ_OK) return st;
   if (plan.T4 != out->T4 || plan.T8 != out->T8) return AQ_ERR_MAP;
 
-  // Row offsets (App. E.2): two INT32 arrays of length R+1.
+  // Row offsets (App. E.2): two INT32 arrays of length R+1; labels padded
+  // with zero bytes to whole 32-bit words.
   std::vector<int32_t> offs;
+  std::vector<uint8_t> lab;
   try {
     offs.resize(2 * (size_t)(plan.R + 1));
+    lab.assign(plan.labels_alloc, 0);
   } catch (const std::bad_alloc &) {
     return AQ_ERR_ARG;
   }
+  for (size_t b = 0; b < plan.labels_bytes; ++b) lab[b] = labels_host[b];
+  const long long T = (long long)plan.R * plan.C;
+  if (T % 8) lab[plan.labels_bytes - 1] &= (uint8_t)((1u << (T % 8)) - 1u);  // unused bits zero
   int32_t *o4 = offs.data(), *o8 = offs.data() + plan.R + 1;
   o4[0] = o8[0] = 0;
   for (int r = 0; r < plan.R; ++r) {
@@ -141,7 +149,7 @@ aq_status aq_pack_weights(const float *W, const uint8_t *labels_host, aq_packed 
     o8[r + 1] = o8[r] + (plan.C - c4);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(out->labels, labels_host, plan.labels_bytes, hipMemcpyHostToDevice, s) !=
+  if (hipMemcpyAsync(out->labels, lab.data(), plan.labels_alloc, hipMemcpyHostToDevice, s) !=
           hipSuccess ||
       hipMemcpyAsync(out->row_off4, o4, plan.offs_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
       hipMemcpyAsync(out->row_off8, o8, plan.offs_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
@@ -170,10 +178,8 @@ size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split) {
   if (check_packed(W) != AQ_OK || M <= 0) return 0;
   if (phase != AQ_PHASE_DECODE) return 0;
   const aq::PackedView v = aq::view_of(*W);
-  if (split < 0 || split > v.C) return 0;
-  const int S = effective_split(v, M, split);
-  if (S <= 1) return 0;
-  return (size_t)S * (size_t)M * (size_t)v.N * sizeof(float);
+  if (split < 0 || (split > 0 && !aq::decode_split_supported(M, split))) return 0;
+  return aq::decode_workspace_bytes(v, M, effective_split(v, M, split));
 }
 
 aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx, int M,
@@ -184,14 +190,14 @@ aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx
   st = check_linear_io(W, qx, sx, M, bias, Y);
   if (st != AQ_OK || M == 0) return st;
   const aq::PackedView v = aq::view_of(*W);
-  if (split < 0 || split > v.C) return AQ_ERR_ARG;
+  if (split < 0 || (split > 0 && !aq::decode_split_supported(M, split))) return AQ_ERR_ARG;
   const int S = effective_split(v, M, split);
-  if (S > 1) {
-    const size_t need = (size_t)S * (size_t)M * (size_t)v.N * sizeof(float);
+  const size_t need = aq::decode_workspace_bytes(v, M, S);
+  if (need > 0) {
     if (!ws || ws_bytes < need) return AQ_ERR_WORKSPACE;
     if (!aligned16(ws)) return AQ_ERR_ALIGN;
   }
-  return aq::launch_decode(v, qx, sx, M, bias, Y, S, static_cast<float *>(ws), nullptr,
+  return aq::launch_decode(v, qx, sx, M, bias, Y, S, ws, nullptr,
                            static_cast<hipStream_t>(stream)) == hipSuccess
              ? AQ_OK
              : AQ_ERR_HIP;

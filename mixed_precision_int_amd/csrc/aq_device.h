@@ -16,24 +16,35 @@ __device__ __forceinline__ int tile_label(const uint8_t *__restrict__ labels, in
   return (labels[t >> 3] >> (t & 7)) & 1;
 }
 
-// 32 consecutive labels starting at tile t, bit k = label of tile t + k.
-// Reads only bytes below nbytes (bits past the end read as 0).
+// The device label buffer is padded with zero bytes to nwords = ceil(T/32)
+// 32-bit words, so labels are read as whole words (scalar loads when the
+// index is uniform).  Word w holds the labels of tiles 32w .. 32w+31.
+__device__ __forceinline__ uint32_t label_word(const uint8_t *__restrict__ labels, int nwords, int w) {
+  return (w >= 0 && w < nwords) ? reinterpret_cast<const uint32_t *>(labels)[w] : 0u;
+}
+
+// Labels of tiles t .. t+31 (bit k = tile t + k); zero past the end.
 __device__ __forceinline__ uint32_t label_bits32(const uint8_t *__restrict__ labels, int t,
-                                                 int nbytes) {
-  const int b0 = t >> 3;
-  uint64_t v = 0;
-#pragma unroll
-  for (int k = 0; k < 5; ++k)
-    if (b0 + k < nbytes) v |= (uint64_t)labels[b0 + k] << (8 * k);
-  return (uint32_t)(v >> (t & 7));
+                                                 int nwords) {
+  const int w = t >> 5, sh = t & 31;
+  const uint32_t lo = label_word(labels, nwords, w);
+  if (sh == 0) return lo;
+  return (lo >> sh) | (label_word(labels, nwords, w + 1) << (32 - sh));
+}
+
+// Labels of tiles t .. t+63.
+__device__ __forceinline__ uint64_t label_bits64(const uint8_t *__restrict__ labels, int t,
+                                                 int nwords) {
+  return (uint64_t)label_bits32(labels, t, nwords) |
+         ((uint64_t)label_bits32(labels, t + 32, nwords) << 32);
 }
 
 // Number of INT4 labels among tiles [t0, t0 + n).
 __device__ __forceinline__ int count_int4(const uint8_t *__restrict__ labels, int t0, int n,
-                                          int nbytes) {
+                                          int nwords) {
   int c = 0;
   for (int k = 0; k < n; k += 32) {
-    uint32_t bits = label_bits32(labels, t0 + k, nbytes);
+    uint32_t bits = label_bits32(labels, t0 + k, nwords);
     const int left = n - k;
     if (left < 32) bits &= (1u << left) - 1u;
     c += __popc(bits);

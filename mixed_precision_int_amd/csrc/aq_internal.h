@@ -38,16 +38,19 @@ inline PackedView view_of(const aq_packed &p) {
 hipError_t launch_pack(const float *W, const aq_packed &out, hipStream_t stream);
 hipError_t launch_quant_act(const float *X, int M, int K, int8_t *qx, float *sx,
                             hipStream_t stream);
-// Decode: if S == 1 writes Y directly; else writes FP32 split partials to ws
-// ([S][M][N]) and reduces them into Y.  P != nullptr selects the debug mode
-// that writes INT32 tile products instead (S, ws, Y unused).
+// Decode: one launch; S input-column groups per output row group are
+// reduced through LDS in increasing order.  P != nullptr selects the debug
+// mode that writes INT32 tile products instead (Y unused).
 hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx, int M,
-                         const float *bias, float *Y, int S, float *ws, int32_t *P,
+                         const float *bias, float *Y, int S, void *ws, int32_t *P,
                          hipStream_t stream);
 hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx, int M,
                           const float *bias, float *Y, int32_t *P, hipStream_t stream);
 
-// Adaptive decode split (host heuristic, also used for workspace sizing).
+// Adaptive decode split (host heuristic), the split values the kernel
+// supports for M tokens, and the workspace a split needs (none).
 int decode_split(const PackedView &w, int M);
+bool decode_split_supported(int M, int S);
+size_t decode_workspace_bytes(const PackedView &w, int M, int S);
 
 }  // namespace aq

@@ -15,7 +15,7 @@ namespace {
 
 template <int BK>
 __global__ __launch_bounds__(64 * (BK / 32)) void pack_kernel(
-    const float *__restrict__ W, int K, int C, int labels_bytes,
+    const float *__restrict__ W, int K, int C, int label_words,
     const uint8_t *__restrict__ labels, const int32_t *__restrict__ off4,
     const int32_t *__restrict__ off8, uint8_t *__restrict__ w4, int8_t *__restrict__ w8,
     float *__restrict__ s4, float *__restrict__ s8, int T4, int T8) {
@@ -28,7 +28,7 @@ __global__ __launch_bounds__(64 * (BK / 32)) void pack_kernel(
 
   // Physical index, eq. 16: stored row offset + same-precision tiles before j.
   const int is4 = tile_label(labels, t);
-  const int n4_before = count_int4(labels, r * C, j, labels_bytes);
+  const int n4_before = count_int4(labels, r * C, j, label_words);
   const int idx = is4 ? off4[r] + n4_before : off8[r] + (j - n4_before);
   if (is4 ? (idx < 0 || idx >= T4) : (idx < 0 || idx >= T8)) return;  // inconsistent metadata
 
@@ -97,13 +97,13 @@ __global__ __launch_bounds__(64 * (BK / 32)) void pack_kernel(
 hipError_t launch_pack(const float *W, const aq_packed &out, hipStream_t stream) {
   const int R = out.N / kTileRows, C = out.K / out.bK;
   const int T = R * C;
-  const int labels_bytes = (T + 7) / 8;
+  const int label_words = (T + 31) / 32;
   if (out.bK == 128)
-    hipLaunchKernelGGL(pack_kernel<128>, dim3(T), dim3(256), 0, stream, W, out.K, C, labels_bytes,
+    hipLaunchKernelGGL(pack_kernel<128>, dim3(T), dim3(256), 0, stream, W, out.K, C, label_words,
                        out.labels, out.row_off4, out.row_off8, out.w4, out.w8, out.s4, out.s8,
                        out.T4, out.T8);
   else
-    hipLaunchKernelGGL(pack_kernel<64>, dim3(T), dim3(128), 0, stream, W, out.K, C, labels_bytes,
+    hipLaunchKernelGGL(pack_kernel<64>, dim3(T), dim3(128), 0, stream, W, out.K, C, label_words,
                        out.labels, out.row_off4, out.row_off8, out.w4, out.w8, out.s4, out.s8,
                        out.T4, out.T8);
   return hipGetLastError();

@@ -37,7 +37,7 @@ struct PrefillArgs {
   const float *sx, *bias;
   float *Y;
   int32_t *P;
-  int N, K, R, C, T4, T8, M, MB, NB;
+  int N, K, R, C, T4, T8, M, MB, NB, label_words;
 };
 
 constexpr int BM = 128;
@@ -83,6 +83,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     nx8[tt] = a.off8[r];
   }
 
+  // labels of the two tile rows for the current 64-column chunk (scalar)
+  uint64_t lbits[2] = {0, 0};
+
   v4i ra[A_CH];
   v4i rb[2][W8_CH];
   int lab[2], idx[2];       // metadata of the column being loaded
@@ -102,7 +105,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (int tt = 0; tt < 2; ++tt) {
       const int r = r0 + tt;
       if (r >= a.R) { lab[tt] = 0; idx[tt] = -1; continue; }
-      const int l = tile_label(a.labels, r * a.C + j);
+      if ((j & 63) == 0) lbits[tt] = label_bits64(a.labels, r * a.C + j, a.label_words);
+      const int l = (int)((lbits[tt] >> (j & 63)) & 1u);
       int id = l ? nx4[tt]++ : nx8[tt]++;
       if (l ? (id >= a.T4) : (id >= a.T8)) id = -1;  // inconsistent metadata: skip
       lab[tt] = l;
@@ -279,6 +283,7 @@ hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx
   args.qx = qx; args.sx = sx; args.bias = bias; args.Y = Y; args.P = P;
   args.N = w.N; args.K = w.K; args.R = w.R; args.C = w.C; args.T4 = w.T4; args.T8 = w.T8;
   args.M = M;
+  args.label_words = (w.R * w.C + 31) / 32;
   args.MB = (M + BM - 1) / BM;
   args.NB = (w.R + 1) / 2;
   const dim3 grid(args.MB * args.NB);

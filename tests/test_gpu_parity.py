@@ -22,13 +22,13 @@ def _ragged(N, K, bK, M, seed, frac8=0.5, outliers=3):
 def test_small_workload_all_stages():
     d = gen.small()
     c = Case(d["W"], d["zmap"], d["X"], d["bN"], d["bK"], name="small")
-    c.check_all(splits=(0, 1, 2, 3, 4))
+    c.check_all(splits=(0, 2, 4, 8, 16))
 
 
 def test_small_workload_with_bias():
     d = gen.small()
     b = np.random.default_rng(7).standard_normal(256).astype(np.float32)
-    Case(d["W"], d["zmap"], d["X"], bias=b, name="small+bias").check_all(splits=(0, 1, 4))
+    Case(d["W"], d["zmap"], d["X"], bias=b, name="small+bias").check_all(splits=(0, 4, 16))
 
 
 @pytest.mark.parametrize("N,K,bK,M", [
@@ -43,7 +43,7 @@ def test_small_workload_with_bias():
 ])
 def test_ragged_shapes(N, K, bK, M):
     W, z, X = _ragged(N, K, bK, M, seed=N * 7 + K + M)
-    Case(W, z, X, 64, bK, name=f"ragged{N}x{K}/bK{bK}/M{M}").check_all(splits=(0, 1, 2))
+    Case(W, z, X, 64, bK, name=f"ragged{N}x{K}/bK{bK}/M{M}").check_all(splits=(0, 2, 4, 8, 16))
 
 
 @pytest.mark.parametrize("kind", ["all_int4", "all_int8", "checker", "zero_rows"])
@@ -63,7 +63,7 @@ def test_uniform_and_degenerate_maps(kind):
         W[3, :] = 0.0            # every tile row of output 3 is zero: scale 1e-12
         W[70, 128:256] = 0.0     # one zero row segment inside a tile
         X[2, :] = 0.0            # a zero token: scale 1e-12, codes 0
-    Case(W, z, X, name=kind).check_all(splits=(0, 1))
+    Case(W, z, X, name=kind).check_all(splits=(0, 4, 16))
 
 
 def test_extreme_codes_and_ties():
@@ -80,7 +80,7 @@ def test_extreme_codes_and_ties():
     X[:, 2::5] = 2.5
     X[:, 3::5] = -127.0
     z = np.array([[4, 8], [8, 4]])
-    Case(W, z, X, name="ties").check_all(splits=(0, 1))
+    Case(W, z, X, name="ties").check_all(splits=(0, 4, 8, 16))
 
 
 @pytest.mark.parametrize("proj", [p[0] for p in gen.LLAMA3B])
@@ -131,4 +131,4 @@ def test_repeated_calls_split_independent():
     bar; the workspace is reused across calls."""
     d = gen.llama3b_decode("qkv", 4)
     c = Case(d["W"], d["zmap"], d["X"], name="splits")
-    c.check_all(splits=(1, 2, 5, 24, 0), phases=("decode",))
+    c.check_all(splits=(4, 8, 16, 0), phases=("decode",))
