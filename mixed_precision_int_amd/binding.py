@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m mixed_precision_int_amd.build` (no fallback exists)")
+    # PyTorch ships its own HIP runtime under the same soname; it must be the
+    # one in the process before libaq.so resolves its dependency, so that
+    # torch streams and allocations are valid inside the library.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     sig = {

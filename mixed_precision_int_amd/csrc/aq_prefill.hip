@@ -1,20 +1,23 @@
 // Compute-bound phase of the tile-aligned W4/W8 x A8 linear layer
 // (AlignQuant Sec. 3.3 "Prefill weight reuse"; App. E.3, eq. 19).
 //
-// Workgroup = 256 threads = 4 wavefronts computing a 128 (tokens) x 128
-// (outputs) block, i.e. two 64-row weight-tile rows.  Wave (wm, wn) owns the
-// 64 x 64 sub-block of token half wm and weight-tile row r0 + wn, so within
-// one input-tile column every wave multiplies exactly one weight tile and
-// one precision.
+// Workgroup = WM x WN wavefronts computing a (64 WM tokens) x (64 WN
+// outputs) block: WN whole 64-row weight-tile rows, so within one
+// input-tile column every wave multiplies exactly one weight tile and one
+// precision.  Two workgroups share a CU; they are not synchronized with
+// each other, so one's MFMAs overlap the other's VALU rescale.
 //
 // For each input-tile column j the block stages, double-buffered in LDS:
-//   A: the 128 x b_K INT8 activation slab, row-major with the 16-byte chunk
-//      index XOR-swizzled by (row >> 1) so that MFMA fragment reads are free
-//      of bank conflicts;
-//   B: both weight tiles widened to INT8, as 16-column panels [panel][n][16]
-//      (the INT8 tile layout); INT4 tiles are widened x16 in registers on the
-//      way in (see w4_lo16), which the rescale undoes with an exact 1/16.
-// Global loads of column j+1 are issued before the MFMAs of column j.
+//   A: the BM x b_K INT8 activation slab, row-major with the 16-byte chunk
+//      index XOR-swizzled by (row >> 1) so that the MFMA fragment reads are
+//      free of bank conflicts;
+//   B: the WN weight tiles widened to INT8 as 16-column panels
+//      [panel][n][16] (the INT8 tile layout); INT4 tiles are widened x16 in
+//      registers on the way in (see w4_lo16), which the rescale undoes with
+//      an exact 1/16.
+// Global loads of column j+1 are issued before the MFMAs of column j and
+// written to the other LDS buffer after them.  Rows past M read row M-1
+// (their outputs are never stored), so activation loads need no branch.
 //
 // Each wave runs v_mfma_i32_32x32x32_i8 on 2 x 2 fragments per 32 columns,
 // then converts the INT32 tile product to FP32 and accumulates it with the
@@ -40,130 +43,165 @@ struct PrefillArgs {
   int N, K, R, C, T4, T8, M, MB, NB, label_words;
 };
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-
 __device__ __forceinline__ v4i ld16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
 
-template <int BK, bool PARTIALS>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
-  constexpr int NP = BK / 16;                // 16-byte chunks per activation row
-  constexpr int A_CH = BM * NP / 256;        // activation chunks per thread
-  constexpr int W8_CH = 64 * NP / 256;       // INT8 weight chunks per thread and tile
-  constexpr int W4_THREADS = 64 * NP / 2;    // threads loading one INT4 tile (1 chunk each)
-  constexpr int KSTEPS = BK / 32;
+template <int BK, int WM, int WN, bool PARTIALS>
+__global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN)) void prefill_kernel(const PrefillArgs a) {
+  constexpr int NT = 64 * WM * WN;            // threads
+  constexpr int BM = 64 * WM, BN = 64 * WN;   // block tile
+  constexpr int NP = BK / 16;                 // 16-byte chunks per row of a tile column
+  constexpr int KSTEPS = BK / 32;             // MFMA k-steps per tile column
+  constexpr int A_CH = BM * NP / NT;          // activation chunks per thread
+  constexpr int W8N = 64 * NP;                // 16-byte chunks of an INT8 tile
+  constexpr int W4N = 32 * NP;                // 16-byte chunks of an INT4 tile
+  constexpr int B8_CH = (W8N + NT - 1) / NT;  // INT8 chunks per thread per tile
+  constexpr int B4_CH = (W4N + NT - 1) / NT;  // INT4 chunks per thread per tile
+  static_assert(BM * NP % NT == 0, "activation slab must split evenly");
 
   __shared__ __attribute__((aligned(16))) int8_t As[2][BM * BK];
   __shared__ __attribute__((aligned(16))) int8_t Bs[2][NP * BN * 16];
 
-  // Blocks sharing weight columns run on one XCD: hardware places block k on
-  // XCD k % 8, so consecutive logical blocks are gathered per XCD.
+  // Rasterization.  Hardware places block k on XCD k % 8, so logical block
+  // L = (k % 8) * (G / 8) + k / 8 gives each XCD a contiguous range of L;
+  // consecutive L then walk GROUP_M M-blocks down one N-block column before
+  // moving right, so the blocks resident on an XCD at one time cover a
+  // compact GROUP_M x (resident / GROUP_M) rectangle whose A and B
+  // column slices are shared in that XCD's L2.
+  constexpr int GROUP_M = 8;
   const int G = gridDim.x;
-  const int k = blockIdx.x;
+  const int kb = blockIdx.x;
   const int per = G / 8;
-  const int L = (k < per * 8) ? (k % 8) * per + k / 8 : k;
-  const int bm = L % a.MB;
-  const int bn = L / a.MB;
+  const int L = (kb < per * 8) ? (kb % 8) * per + kb / 8 : kb;
+  const int in_group = GROUP_M * a.NB;
+  const int first_m = (L / in_group) * GROUP_M;
+  const int gsize = min(a.MB - first_m, GROUP_M);
+  const int bm = first_m + (L % in_group) % gsize;
+  const int bn = (L % in_group) / gsize;
   const int m0 = bm * BM;
-  const int r0 = 2 * bn;
+  const int r0 = WN * bn;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WM, wn = wave / WM;
   const int rw = r0 + wn;  // this wave's weight-tile row
   const bool wave_live = rw < a.R;
+  const int h = lane >> 5;
 
-  // running eq. 16 indices of the two tile rows (uniform)
-  int nx4[2], nx8[2];
+  // ---- per-thread activation chunk coordinates (fixed over j)
+  // (byte offsets are 32-bit against a uniform base, so the address of every
+  // load and LDS access is one scalar base plus a fixed per-lane offset)
+  uint32_t a_src[A_CH];
+  int a_dst[A_CH];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int it = 0; it < A_CH; ++it) {
+    const int c = it * NT + tid;
+    const int row = c / NP, p = c % NP;
+    const int m = min(m0 + row, a.M - 1);
+    a_src[it] = (uint32_t)m * (uint32_t)a.K + p * 16;
+    a_dst[it] = row * BK + ((p ^ ((row >> 1) & (NP - 1))) * 16);
+  }
+  uint32_t b_src[B8_CH];
+#pragma unroll
+  for (int e = 0; e < B8_CH; ++e) b_src[e] = (uint32_t)(e * NT + tid) * 16u;
+  // ---- per-lane fragment read offsets (fixed over j), for k-step u add 32u
+  int af_off[2][KSTEPS], bf_off[2][KSTEPS];
+#pragma unroll
+  for (int u = 0; u < KSTEPS; ++u) {
+    const int p = 2 * u + h;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int row = wm * 64 + f * 32 + (lane & 31);
+      af_off[f][u] = row * BK + ((p ^ ((row >> 1) & (NP - 1))) * 16);
+      const int n = wn * 64 + f * 32 + (lane & 31);
+      bf_off[f][u] = (p * BN + n) * 16;
+    }
+  }
+
+  // ---- eq. 16 walk of the WN tile rows (scalar)
+  int nx4[WN], nx8[WN];
+  uint64_t lbits[WN];
+#pragma unroll
+  for (int tt = 0; tt < WN; ++tt) {
     const int r = min(r0 + tt, a.R - 1);
     nx4[tt] = a.off4[r];
     nx8[tt] = a.off8[r];
+    lbits[tt] = 0;
   }
 
-  // labels of the two tile rows for the current 64-column chunk (scalar)
-  uint64_t lbits[2] = {0, 0};
-
+  // ---- staging registers for the column being loaded
   v4i ra[A_CH];
-  v4i rb[2][W8_CH];
-  int lab[2], idx[2];       // metadata of the column being loaded
-  float scl[2];             // this lane's weight scales for the wave's tile
-  int cur_lab = 0, cur_idx = 0;
-  float cur_sc[2] = {0.f, 0.f};
+  v4i rb[WN][B8_CH];
+  int ld_is4[WN], ld_idx[WN];
+  float ld_sc0 = 0.f, ld_sc1 = 0.f;
 
-  auto load_col = [&](int j) {
-#pragma unroll
-    for (int it = 0; it < A_CH; ++it) {
-      const int c = it * 256 + tid;
-      const int row = c / NP, p = c % NP;
-      const int m = m0 + row;
-      ra[it] = (m < a.M) ? ld16(a.qx + (size_t)m * a.K + (size_t)j * BK + p * 16) : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int r = r0 + tt;
-      if (r >= a.R) { lab[tt] = 0; idx[tt] = -1; continue; }
-      if ((j & 63) == 0) lbits[tt] = label_bits64(a.labels, r * a.C + j, a.label_words);
-      const int l = (int)((lbits[tt] >> (j & 63)) & 1u);
-      int id = l ? nx4[tt]++ : nx8[tt]++;
-      if (l ? (id >= a.T4) : (id >= a.T8)) id = -1;  // inconsistent metadata: skip
-      lab[tt] = l;
-      idx[tt] = id;
-      if (id < 0) continue;
-      if (l) {
-        if (tid < W4_THREADS) rb[tt][0] = ld16(a.w4 + (size_t)id * 64 * BK / 2 + tid * 16);
-      } else {
-#pragma unroll
-        for (int e = 0; e < W8_CH; ++e)
-          rb[tt][e] = ld16(a.w8 + (size_t)id * 64 * BK + (e * 256 + tid) * 16);
-      }
-    }
-    // scales of the wave's own tile: lane's output column n = 32 fn + (lane & 31)
-    const int id = idx[wn];
-    if (wave_live && id >= 0) {
-      const float *sp = (lab[wn] ? a.s4 : a.s8) + (size_t)id * 64 + (lane & 31);
-      const float f = lab[wn] ? 0.0625f : 1.0f;
-      scl[0] = sp[0] * f;
-      scl[1] = sp[32] * f;
-    } else {
-      scl[0] = scl[1] = 0.f;
-    }
-  };
+  // issue the global loads of tile column j.  Branch-free: every tile loads
+  // B8_CH chunks per thread (an INT4 tile re-reads its own chunks past its
+  // end), an absent or inconsistent tile re-reads tile 0 of a non-empty
+  // buffer and is marked dead, and nothing loaded is used before the MFMAs of
+  // the previous column have been issued.
+#define AQ_LOAD_COLUMN(j)                                                                      \
+  do {                                                                                         \
+    const int j_ = (j);                                                                        \
+    const int8_t *abase = a.qx + (size_t)j_ * BK;                                              \
+    _Pragma("unroll") for (int it = 0; it < A_CH; ++it) ra[it] = ld16(abase + a_src[it]);     \
+    _Pragma("unroll") for (int tt = 0; tt < WN; ++tt) {                                        \
+      const int r = r0 + tt;                                                                   \
+      if ((j_ & 63) == 0) lbits[tt] = label_bits64(a.labels, min(r, a.R - 1) * a.C + j_, a.label_words); \
+      int l = (int)((lbits[tt] >> (j_ & 63)) & 1u);                                          \
+      int id = l ? nx4[tt] : nx8[tt];                                                          \
+      nx4[tt] += l;                                                                            \
+      nx8[tt] += l ^ 1;                                                                        \
+      const int ok = r < a.R && id >= 0 && id < (l ? a.T4 : a.T8);                             \
+      if (!ok) { l = a.T4 > 0 ? 1 : 0; id = 0; }                                               \
+      ld_is4[tt] = l;                                                                          \
+      ld_idx[tt] = ok ? id : -1;                                                               \
+      const uint8_t *src = l ? a.w4 + (size_t)id * (64 * BK / 2)                               \
+                             : reinterpret_cast<const uint8_t *>(a.w8) + (size_t)id * (64 * BK); \
+      /* an INT4 tile has half the chunks: chunk c >= W4N re-reads c mod W4N */                \
+      const uint32_t wmask = l ? (uint32_t)W4N * 16u - 1u : (uint32_t)W8N * 16u - 1u;          \
+      _Pragma("unroll") for (int e = 0; e < B8_CH; ++e) rb[tt][e] = ld16(src + (b_src[e] & wmask)); \
+      if (tt == wn) {                                                                          \
+        const float *sp = (l ? a.s4 : a.s8) + (size_t)id * 64 + (lane & 31);                  \
+        ld_sc0 = sp[0];                                                                        \
+        ld_sc1 = sp[32];                                                                       \
+      }                                                                                        \
+    }                                                                                          \
+  } while (0)
 
-  auto store_col = [&](int st) {
-#pragma unroll
-    for (int it = 0; it < A_CH; ++it) {
-      const int c = it * 256 + tid;
-      const int row = c / NP, p = c % NP;
-      const int sw = p ^ ((row >> 1) & (NP - 1));
-      *reinterpret_cast<v4i *>(&As[st][row * BK + sw * 16]) = ra[it];
-    }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      if (idx[tt] < 0) continue;
-      if (lab[tt]) {
-        if (tid < W4_THREADS) {
-          const int q = tid / 64, i = tid % 64;
-          const v4i w = rb[tt][0];
-          const v4i lo = v4i{w4_lo16(w[0]), w4_lo16(w[1]), w4_lo16(w[2]), w4_lo16(w[3])};
-          const v4i hi = v4i{w4_hi16(w[0]), w4_hi16(w[1]), w4_hi16(w[2]), w4_hi16(w[3])};
-          *reinterpret_cast<v4i *>(&Bs[st][((2 * q) * BN + tt * 64 + i) * 16]) = lo;
-          *reinterpret_cast<v4i *>(&Bs[st][((2 * q + 1) * BN + tt * 64 + i) * 16]) = hi;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < W8_CH; ++e) {
-          const int c = e * 256 + tid;
-          const int p = c / 64, i = c % 64;
-          *reinterpret_cast<v4i *>(&Bs[st][(p * BN + tt * 64 + i) * 16]) = rb[tt][e];
-        }
-      }
-    }
-  };
+  // write the staged column into LDS buffer st
+#define AQ_STORE_COLUMN(st)                                                                    \
+  do {                                                                                         \
+    int8_t *As_ = As[(st)];                                                                    \
+    int8_t *Bs_ = Bs[(st)];                                                                    \
+    _Pragma("unroll") for (int it = 0; it < A_CH; ++it)                                        \
+      *reinterpret_cast<v4i *>(As_ + a_dst[it]) = ra[it];                                      \
+    _Pragma("unroll") for (int tt = 0; tt < WN; ++tt) {                                        \
+      if (ld_idx[tt] < 0) continue;                                                            \
+      if (ld_is4[tt]) {                                                                        \
+        _Pragma("unroll") for (int e = 0; e < B4_CH; ++e) {                                    \
+          const int c = e * NT + tid;                                                          \
+          if (c < W4N) {                                                                       \
+            const int q = c / 64, i = c % 64;                                                  \
+            const v4i w = rb[tt][e];                                                           \
+            *reinterpret_cast<v4i *>(Bs_ + ((2 * q) * BN + tt * 64 + i) * 16) =                \
+                v4i{w4_lo16(w[0]), w4_lo16(w[1]), w4_lo16(w[2]), w4_lo16(w[3])};             \
+            *reinterpret_cast<v4i *>(Bs_ + ((2 * q + 1) * BN + tt * 64 + i) * 16) =            \
+                v4i{w4_hi16(w[0]), w4_hi16(w[1]), w4_hi16(w[2]), w4_hi16(w[3])};             \
+          }                                                                                    \
+        }                                                                                      \
+      } else {                                                                                 \
+        _Pragma("unroll") for (int e = 0; e < B8_CH; ++e) {                                    \
+          const int c = e * NT + tid;                                                          \
+          if (c < W8N) {                                                                       \
+            const int p = c / 64, i = c % 64;                                                  \
+            *reinterpret_cast<v4i *>(Bs_ + (p * BN + tt * 64 + i) * 16) = rb[tt][e];           \
+          }                                                                                    \
+        }                                                                                      \
+      }                                                                                        \
+    }                                                                                          \
+  } while (0)
 
-  v16i acc[2][2];
   float F[2][2][16];
 #pragma unroll
   for (int fm = 0; fm < 2; ++fm)
@@ -172,81 +210,87 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) F[fm][fn][e] = 0.f;
 
-  auto compute_col = [&](int st, int j) {
-#pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < 2; ++fn)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[fm][fn][e] = 0;
-    const int h = lane >> 5;
-#pragma unroll
-    for (int u = 0; u < KSTEPS; ++u) {
-      const int p = 2 * u + h;
-      v4i af[2], bf[2];
-#pragma unroll
-      for (int fm = 0; fm < 2; ++fm) {
-        const int row = wm * 64 + fm * 32 + (lane & 31);
-        const int sw = p ^ ((row >> 1) & (NP - 1));
-        af[fm] = *reinterpret_cast<const v4i *>(&As[st][row * BK + sw * 16]);
-      }
-#pragma unroll
-      for (int fn = 0; fn < 2; ++fn) {
-        const int n = wn * 64 + fn * 32 + (lane & 31);
-        bf[fn] = *reinterpret_cast<const v4i *>(&Bs[st][(p * BN + n) * 16]);
-      }
-#pragma unroll
-      for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < 2; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
-    }
-    if constexpr (PARTIALS) {
-      // C layout of the 32x32 MFMA: column (output n) = lane & 31,
-      // row (token) = 8 (e / 4) + 4 (lane >> 5) + (e & 3).
-#pragma unroll
-      for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < 2; ++fn)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int m = m0 + wm * 64 + fm * 32 + 8 * (e / 4) + 4 * h + (e & 3);
-            const size_t n = (size_t)rw * 64 + fn * 32 + (lane & 31);
-            if (m < a.M) {
-              const int v = acc[fm][fn][e];
-              a.P[((size_t)m * a.N + n) * a.C + j] = cur_lab ? (v >> 4) : v;
-            }
-          }
-    } else {
-#pragma unroll
-      for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < 2; ++fn)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            F[fm][fn][e] = fmaf((float)acc[fm][fn][e], cur_sc[fn], F[fm][fn][e]);
-    }
-  };
-
-  load_col(0);
-  store_col(0);
-  cur_lab = lab[wn]; cur_idx = idx[wn]; cur_sc[0] = scl[0]; cur_sc[1] = scl[1];
+  AQ_LOAD_COLUMN(0);
+  AQ_STORE_COLUMN(0);
+  int cur_is4 = ld_is4[wn], cur_idx = wave_live ? ld_idx[wn] : -1;
+  float cur_sc0 = ld_is4[wn] ? ld_sc0 * 0.0625f : ld_sc0;
+  float cur_sc1 = ld_is4[wn] ? ld_sc1 * 0.0625f : ld_sc1;
   __syncthreads();
-  for (int j = 0; j < a.C; ++j) {
-    const int st = j & 1;
-    const bool more = j + 1 < a.C;
-    if (more) load_col(j + 1);
-    if (wave_live && cur_idx >= 0) compute_col(st, j);
-    if (more) {
-      store_col(st ^ 1);
-      cur_lab = lab[wn]; cur_idx = idx[wn]; cur_sc[0] = scl[0]; cur_sc[1] = scl[1];
-    }
+
+#define AQ_COLUMN_BODY(jarg, ST_) \
+    const int jc_ = (jarg); \
+    const bool more = jc_ + 1 < a.C; \
+    if (more) AQ_LOAD_COLUMN(jc_ + 1); \
+ \
+    if (cur_idx >= 0) { \
+      const int8_t *As_ = As[ST_]; \
+      const int8_t *Bs_ = Bs[ST_]; \
+      v16i acc[2][2]; \
+_Pragma("unroll") \
+      for (int fm = 0; fm < 2; ++fm) \
+_Pragma("unroll") \
+        for (int fn = 0; fn < 2; ++fn) acc[fm][fn] = v16i{0}; \
+_Pragma("unroll") \
+      for (int u = 0; u < KSTEPS; ++u) { \
+        const v4i a0 = *reinterpret_cast<const v4i *>(As_ + af_off[0][u]); \
+        const v4i a1 = *reinterpret_cast<const v4i *>(As_ + af_off[1][u]); \
+        const v4i b0 = *reinterpret_cast<const v4i *>(Bs_ + bf_off[0][u]); \
+        const v4i b1 = *reinterpret_cast<const v4i *>(Bs_ + bf_off[1][u]); \
+        acc[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b0, acc[0][0], 0, 0, 0); \
+        acc[0][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b1, acc[0][1], 0, 0, 0); \
+        acc[1][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b0, acc[1][0], 0, 0, 0); \
+        acc[1][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b1, acc[1][1], 0, 0, 0); \
+      } \
+      if constexpr (PARTIALS) { \
+        /* 32x32 MFMA result: column (output n) = lane & 31, */ \
+        /* row (token) = 8 (e / 4) + 4 (lane >> 5) + (e & 3). */ \
+_Pragma("unroll") \
+        for (int fm = 0; fm < 2; ++fm) \
+_Pragma("unroll") \
+          for (int fn = 0; fn < 2; ++fn) \
+_Pragma("unroll") \
+            for (int e = 0; e < 16; ++e) { \
+              const int m = m0 + wm * 64 + fm * 32 + 8 * (e / 4) + 4 * h + (e & 3); \
+              const size_t n = (size_t)rw * 64 + fn * 32 + (lane & 31); \
+              if (m < a.M) { \
+                const int v = acc[fm][fn][e]; \
+                a.P[((size_t)m * a.N + n) * a.C + jc_] = cur_is4 ? (v >> 4) : v; \
+              } \
+            } \
+      } else { \
+_Pragma("unroll") \
+        for (int fm = 0; fm < 2; ++fm) \
+_Pragma("unroll") \
+          for (int e = 0; e < 16; ++e) { \
+            F[fm][0][e] = fmaf((float)acc[fm][0][e], cur_sc0, F[fm][0][e]); \
+            F[fm][1][e] = fmaf((float)acc[fm][1][e], cur_sc1, F[fm][1][e]); \
+          } \
+      } \
+    } \
+ \
+    if (more) { \
+      AQ_STORE_COLUMN(ST_ ^ 1); \
+      cur_is4 = ld_is4[wn]; \
+      cur_idx = wave_live ? ld_idx[wn] : -1; \
+      cur_sc0 = ld_is4[wn] ? ld_sc0 * 0.0625f : ld_sc0; \
+      cur_sc1 = ld_is4[wn] ? ld_sc1 * 0.0625f : ld_sc1; \
+    } \
     __syncthreads();
+
+  for (int j = 0; j < a.C; j += 2) {
+    {
+      AQ_COLUMN_BODY(j, 0)
+    }
+    if (j + 1 < a.C) {
+      AQ_COLUMN_BODY(j + 1, 1)
+    }
   }
+#undef AQ_COLUMN_BODY
+#undef AQ_LOAD_COLUMN
+#undef AQ_STORE_COLUMN
 
   if constexpr (!PARTIALS) {
     if (!wave_live) return;
-    const int h = lane >> 5;
 #pragma unroll
     for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
@@ -265,18 +309,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int BK>
-void launch_bk(bool partials, dim3 grid, hipStream_t stream, const PrefillArgs &args) {
+template <int BK, int WM, int WN>
+void launch_cfg(bool partials, hipStream_t stream, const PrefillArgs &args) {
+  const dim3 grid(args.MB * args.NB);
+  const dim3 block(64 * WM * WN);
   if (partials)
-    hipLaunchKernelGGL((prefill_kernel<BK, true>), grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<BK, WM, WN, true>), grid, block, 0, stream, args);
   else
-    hipLaunchKernelGGL((prefill_kernel<BK, false>), grid, dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<BK, WM, WN, false>), grid, block, 0, stream, args);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx, int M,
                           const float *bias, float *Y, int32_t *P, hipStream_t stream) {
+  constexpr int WM = 2, WN = 2;
   PrefillArgs args;
   args.labels = w.labels; args.off4 = w.off4; args.off8 = w.off8;
   args.w4 = w.w4; args.w8 = w.w8; args.s4 = w.s4; args.s8 = w.s8;
@@ -284,11 +331,10 @@ hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx
   args.N = w.N; args.K = w.K; args.R = w.R; args.C = w.C; args.T4 = w.T4; args.T8 = w.T8;
   args.M = M;
   args.label_words = (w.R * w.C + 31) / 32;
-  args.MB = (M + BM - 1) / BM;
-  args.NB = (w.R + 1) / 2;
-  const dim3 grid(args.MB * args.NB);
-  if (w.bK == 128) launch_bk<128>(P != nullptr, grid, stream, args);
-  else launch_bk<64>(P != nullptr, grid, stream, args);
+  args.MB = (M + 64 * WM - 1) / (64 * WM);
+  args.NB = (w.R + WN - 1) / WN;
+  if (w.bK == 128) launch_cfg<128, WM, WN>(P != nullptr, stream, args);
+  else launch_cfg<64, WM, WN>(P != nullptr, stream, args);
   return hipGetLastError();
 }
 
