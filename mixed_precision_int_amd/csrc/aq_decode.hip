@@ -29,22 +29,26 @@
 // of the row (App. E.1) and both row offsets are fetched with one batch of
 // scalar loads.
 //
-// The INT8 activations of the workgroup's tokens are staged once in LDS
-// (coalesced 16-byte loads issued together with the metadata loads;
-// 16-byte granules XOR-swizzled by token row so that the 16 rows one MFMA
-// operand reads fall in distinct banks); the workgroup barrier that
-// publishes them is taken while the first weight batch is in flight.  When
-// they do not fit, lanes read them from global memory instead.
+// INT8 activations are staged in LDS with coalesced 16-byte loads:
+//   M <= 4 : each wave loads, with every weight batch, the batch's columns of
+//            the M tokens (lane l: 16 bytes at column t0*b_K + 16l) into a
+//            slice of its own, so no workgroup barrier is needed;
+//   M  > 4 : the workgroup stages its 16*MG tokens once (loads issued with
+//            the metadata loads; 16-byte granules XOR-swizzled by token row so
+//            that the 16 rows one MFMA operand reads fall in distinct banks)
+//            and publishes them with one barrier while the first weight batch
+//            is in flight; when they do not fit, lanes read them from global
+//            memory instead.
 //
-// Products:
-//   M <= 4  : v_dot4_i32_i8 on the vector ALU (the pages' one-token decode
-//             uses a 4-way byte dot product, Table 5); a lane accumulates its
-//             32 columns per tile and the four k-groups are summed across
-//             lanes (swizzle / permute) before the split reduction.
-//   M  > 4  : v_mfma_i32_16x16x64_i8 with up to 16 tokens as the A operand and
-//             the 16 weight rows as the B operand, C[token 4g+e][row i16]; at
-//             these token counts the byte dot products would outrun the
-//             vector ALU before HBM.
+// Products (the pages split decode the same way, Table 5):
+//   M = 1 : v_dot4_i32_i8 on the vector ALU (a 4-way byte dot product); a
+//           lane accumulates its 32 columns per tile and the four k-groups
+//           are summed across lanes (swizzle / permute) before the split
+//           reduction;
+//   M > 1 : v_mfma_i32_16x16x64_i8 with up to 16 tokens as the A operand and
+//           the 16 weight rows as the B operand, C[token 4g+e][row i16]; per
+//           extra token the byte dot products would cost the vector ALU and
+//           LDS a full operand pass each.
 // Each tile's INT32 product is rescaled by its per-row FP32 scale into FP32
 // accumulators (eq. 19).  INT4 tiles are widened x16 (see w4_lo16), so their
 // scale is multiplied by the exact factor 1/16.
@@ -56,8 +60,13 @@ namespace aq {
 namespace {
 
 constexpr int kLdsBudget = 160 * 1024;  // LDS per workgroup on gfx950
-constexpr int kValuMaxM = 4;            // largest M on the vector-ALU path
+constexpr int kValuMaxM = 1;            // largest M on the vector-ALU path
+constexpr int kPrivMaxM = 4;            // largest M with per-wave activation slices
+constexpr int kPrivDepth = 8;           // tiles per batch with per-wave activation slices
 enum { kValu = 0, kMfma = 1 };
+// Where the MFMA/VALU activation operands come from: a per-wave LDS slice
+// of the batch, the workgroup's LDS copy of its tokens, or global memory.
+enum { kXPriv = 0, kXShared = 1, kXGlobal = 2 };
 
 struct DecodeArgs {
   const uint8_t *labels;
@@ -111,12 +120,31 @@ __device__ __forceinline__ int sum_kgroups_i(int v) {
   return v;
 }
 
-template <int BK, int MODE, int MG, int WAVES, int RG, int DEPTH, bool XLDS, bool PARTIALS>
+// 16-byte activation operand of step u for a lane of k-group g, from a row
+// of INT8 activations whose column colbase is the tile's first column.  For
+// b_K = 64 INT4 tiles the operand is two 8-byte pieces (low-nibble and
+// high-nibble columns).  With SW >= 0 the row is an LDS row whose 16-byte
+// granules are XOR-swizzled by SW.
+template <int BK>
+__device__ __forceinline__ v4i x_operand(const int8_t *row, int colbase, int g, int u, int is4, int sw) {
+  if (BK == 64 && is4) {
+    const int ca = colbase + 32 * (g >> 1) + 8 * (g & 1);
+    const int cb = ca + 16;
+    const uint2 p0 = load8(row + 16 * ((ca >> 4) ^ sw) + (ca & 15));
+    const uint2 p1 = load8(row + 16 * ((cb >> 4) ^ sw) + (cb & 15));
+    return v4i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y};
+  }
+  const int c = BK == 128 ? colbase + 32 * g + 16 * u : colbase + 16 * g;
+  return load16(row + 16 * ((c >> 4) ^ sw));
+}
+
+template <int BK, int MODE, int MG, int WAVES, int RG, int DEPTH, int XMODE, bool PARTIALS>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) {
   constexpr int KS = BK / 64;    // MFMA steps (16-byte operands per lane) per tile
   constexpr int S = WAVES / RG;  // splits per row group
   constexpr int NT = WAVES * 64;
   constexpr int XU = 8;          // activation granules per thread per staging pass
+  constexpr int XW = DEPTH * BK; // bytes of one token's activations per batch (per-wave slices)
   extern __shared__ __align__(16) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -137,17 +165,23 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
   const uint8_t *__restrict__ w4p = a.w4;
   const uint8_t *__restrict__ w8p = reinterpret_cast<const uint8_t *>(a.w8);
   const int T4 = a.T4, T8 = a.T8;
-  const int kg = K >> 4;                        // 16-byte granules per activation row
-  const int xmask = (kg & 15) == 0 ? 15 : 0;    // granule swizzle (stays inside the row)
-  int8_t *xs = reinterpret_cast<int8_t *>(smem);  // [xrows][K], granules swizzled
-  const int xbytes = ((MODE == kValu ? M : 16 * MG) * K + 15) & ~15;
-  float4 *red = reinterpret_cast<float4 *>(smem + (XLDS ? xbytes : 0));  // [WAVES][MG][64]
+  const int kg = K >> 4;                      // 16-byte granules per activation row
+  const int xmask = (kg & 15) == 0 ? 15 : 0;  // granule swizzle (stays inside the row)
+  // LDS: per-wave slices [WAVES][M][DEPTH*BK], or the block's [16*MG][K]
+  // activations (granules swizzled by row); then the split reduction buffer
+  // [WAVES][MG][64] float4.
+  int8_t *xs = reinterpret_cast<int8_t *>(smem);
+  int8_t *xw = xs + wave * M * XW;
+  const int xbytes = XMODE == kXPriv ? WAVES * M * XW : XMODE == kXShared ? ((16 * MG * K + 15) & ~15) : 0;
+  float4 *red = reinterpret_cast<float4 *>(smem + xbytes);
 
-  // ---- activation staging loads (independent of the metadata), issued first
+  // ---- MFMA path: block activation staging loads (independent of the
+  // metadata), issued first
   v4i xb[XU];
   const int8_t *xsrc = a.qx + (size_t)mbase * K;
-  const int xgran = XLDS ? xrows * kg : 0;
-  if (XLDS) {
+  const bool xstage = XMODE == kXShared;
+  const int xgran = xstage ? xrows * kg : 0;
+  if (xstage) {
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
       if (u * NT < xgran) {  // uniform: only the passes the block needs
@@ -158,11 +192,12 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
   }
 
   // ---- eq. 16 bookkeeping: the row's offsets and label words in one batch
-  // of scalar loads, all issued before the single wait (the empty asm
-  // consumes them, so none is sunk past the others' use).
+  // of scalar loads.  The label window below depends on the offsets (a
+  // guard that valid metadata never trips), so the compiler cannot defer the
+  // offset loads to their later use: all seven share one wait.
   const int tb = r * C;
   const bool fastlab = C <= 128;
-  int o4 = a.off4[r], o8 = a.off8[r];
+  const int o4 = a.off4[r], o8 = a.off8[r];
   uint32_t lw[5];
   {
     const uint32_t *wd = reinterpret_cast<const uint32_t *>(a.labels);
@@ -170,21 +205,18 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
 #pragma unroll
     for (int k = 0; k < 5; ++k) lw[k] = wd[min(w0 + k, last)];
   }
-  asm volatile("" : "+s"(o4), "+s"(o8), "+s"(lw[0]), "+s"(lw[1]), "+s"(lw[2]), "+s"(lw[3]), "+s"(lw[4]));
+  if ((o4 | o8) < 0) lw[4] = 0u;  // negative row offsets: inconsistent metadata
   uint64_t wlo, whi;
   label_window(lw, tb, wlo, whi);
-  int n4;
-  if (fastlab) {
-    n4 = c0 <= 64 ? __popcll(wlo & low_mask(c0))
-                  : __popcll(wlo) + __popcll(whi & low_mask(c0 - 64));
-  } else {
-    n4 = count_int4(a.labels, tb, c0, a.label_words);
-  }
+  int n4 = c0 <= 64 ? __popcll(wlo & low_mask(c0)) : __popcll(wlo) + __popcll(whi & low_mask(c0 - 64));
   int idx4 = o4 + n4;
   int idx8 = o8 + (c0 - n4);
+  if (!fastlab) {  // rows of more than 128 tiles: count from memory
+    n4 = count_int4(a.labels, tb, c0, a.label_words);
+    idx4 = o4 + n4;
+    idx8 = o8 + (c0 - n4);
+  }
 
-  // Activation rows of this lane (global fallback; padding tokens read the
-  // last real row, their outputs are never stored).
   float4 F[MG];
 #pragma unroll
   for (int mg = 0; mg < MG; ++mg) F[mg] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -192,11 +224,13 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
   v4i W[DEPTH][2];
   float SC[DEPTH];
   int live[DEPTH], is4v[DEPTH], jv[DEPTH];
+  v4i xv[kPrivMaxM];  // per-wave slices: this lane's granule of the batch, per token
 
   // Issue the loads of the live tiles among t0 .. t0+DEPTH-1 of the split:
   // the rows' 16-byte panel chunks (two for an INT8 tile at b_K = 128, one
-  // otherwise) and the lane's row scale.  Live tiles are a prefix; the
-  // branches are uniform.
+  // otherwise) and the lane's row scale; with per-wave slices also the
+  // batch's activation columns (lane l: 16 bytes at column t0*BK + 16l of
+  // each token).  Live tiles are a prefix; the branches are uniform.
 #define AQ_DECODE_ISSUE(t0_)                                                                    \
   {                                                                                             \
     const int t0i = (t0_);                                                                      \
@@ -235,12 +269,17 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
         }                                                                                       \
       }                                                                                         \
     }                                                                                           \
+    if (XMODE == kXPriv) {                                                                      \
+      const int col = min(t0i * BK + 16 * lane, K - 16);                                        \
+      _Pragma("unroll") for (int m = 0; m < kPrivMaxM; ++m)                                     \
+        if (m < M) xv[m] = load16(a.qx + (size_t)m * K + col);                                  \
+    }                                                                                           \
   }
 
-  // ---- activations into LDS (their loads were issued with the metadata
-  // batch), then the first weight batch, then one barrier while it is in
-  // flight
-  if (XLDS) {
+  // ---- MFMA path: block activations into LDS (the stores wait for the
+  // staging loads only), then the first weight batch, then one barrier
+  // while that batch is in flight
+  if (xstage) {
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
       const int q = tid + u * NT;
@@ -264,19 +303,20 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
     }
   }
   AQ_DECODE_ISSUE(c0);
-  if (XLDS) {
+  if (xstage) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS writes done; vmcnt left open
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
 
-  // Activation operand of token row t (relative to mbase) at global column
-  // col (16 bytes; for b_K = 64 INT4 two 8-byte halves at col and col + 16).
-#define AQ_XROW_PTR_G(t_) (a.qx + (size_t)(mbase + (t_)) * K)
-
   for (int t0 = c0; t0 < c1; t0 += DEPTH) {
     if (t0 != c0) AQ_DECODE_ISSUE(t0);
+    if (XMODE == kXPriv) {  // the wave's own activation slice; read back by this wave only
+#pragma unroll
+      for (int m = 0; m < kPrivMaxM; ++m)
+        if (m < M && 16 * lane < XW) *reinterpret_cast<v4i *>(xw + m * XW + 16 * lane) = xv[m];
+    }
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       if (!live[d]) continue;
@@ -298,44 +338,20 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
         wop[0] = is4 ? v4i{w4_lo16(w[0]), w4_lo16(w[1]), w4_hi16(w[0]), w4_hi16(w[1])} : w;
       }
       const float sc = is4 ? SC[d] * 0.0625f : SC[d];
-      // column of step u's 16 bytes (b_K = 64 INT4: first 8-byte half)
-      const int colbase = jt * BK;
-#define AQ_XCOL(u_) (BK == 128 ? colbase + 32 * g + 16 * (u_)                                  \
-                               : (is4 ? colbase + 32 * (g >> 1) + 8 * (g & 1) : colbase + 16 * g))
-#define AQ_XLOAD(dst_, trow_, u_)                                                               \
-  {                                                                                             \
-    const int trw = (trow_);                                                                    \
-    const int col = AQ_XCOL(u_);                                                                \
-    if (XLDS) {                                                                                 \
-      const int8_t *xr = xs + trw * K;                                                          \
-      const int sw = trw & xmask;                                                               \
-      if (BK == 64 && is4) {                                                                    \
-        const int cga = col >> 4, cgb = (col + 16) >> 4, in = col & 15;                         \
-        const uint2 p0 = *reinterpret_cast<const uint2 *>(xr + 16 * (cga ^ sw) + in);          \
-        const uint2 p1 = *reinterpret_cast<const uint2 *>(xr + 16 * (cgb ^ sw) + in);          \
-        dst_ = v4i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y};                                 \
-      } else {                                                                                  \
-        dst_ = *reinterpret_cast<const v4i *>(xr + 16 * ((col >> 4) ^ sw));                    \
-      }                                                                                         \
-    } else {                                                                                    \
-      const int8_t *xr = AQ_XROW_PTR_G(trw);                                                    \
-      if (BK == 64 && is4) {                                                                    \
-        const uint2 p0 = load8(xr + col), p1 = load8(xr + col + 16);                            \
-        dst_ = v4i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y};                                 \
-      } else {                                                                                  \
-        dst_ = load16(xr + col);                                                                \
-      }                                                                                         \
-    }                                                                                           \
-  }
       if (MODE == kMfma) {
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg) {
+          // token row of this lane; padding tokens read the last real row,
+          // their outputs are never stored
           const int trow = min(mg * 16 + i16, xrows - 1);
+          const int8_t *xr = XMODE == kXPriv ? xw + trow * XW
+                           : XMODE == kXShared ? xs + trow * K : xsrc + (size_t)trow * K;
+          const int xcol = XMODE == kXPriv ? d * BK : jt * BK;
+          const int sw = XMODE == kXShared ? (trow & xmask) : 0;
           v4i acc = {0, 0, 0, 0};
 #pragma unroll
           for (int u = 0; u < KS; ++u) {
-            v4i xop;
-            AQ_XLOAD(xop, trow, u);
+            const v4i xop = x_operand<BK>(xr, xcol, g, u, is4, sw);
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(xop, wop[u], acc, 0, 0, 0);
           }
           if constexpr (PARTIALS) {
@@ -354,16 +370,15 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
           }
         }
       } else {
-        // vector ALU: tokens 0 .. min(M, 4)-1, each lane its 16*KS*... columns
-        int acc[4];
+        // vector ALU: the one token, this lane's 16*KS columns
+        int acc[kValuMaxM];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < kValuMaxM; ++m) {
           acc[m] = 0;
           if (m < M) {
 #pragma unroll
             for (int u = 0; u < KS; ++u) {
-              v4i xop;
-              AQ_XLOAD(xop, m, u);
+              const v4i xop = x_operand<BK>(xw + m * XW, d * BK, g, u, is4, 0);
 #pragma unroll
               for (int e = 0; e < 4; ++e) acc[m] = __builtin_amdgcn_sdot4(wop[u][e], xop[e], acc[m], false);
             }
@@ -372,7 +387,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
         if constexpr (PARTIALS) {
           const size_t n = (size_t)r * 64 + rg * 16 + i16;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
+          for (int m = 0; m < kValuMaxM; ++m) {
             if (m < M) {
               const int v = sum_kgroups_i(acc[m]);
               if (g == 0) a.P[((size_t)m * a.N + n) * C + jt] = is4 ? (v >> 4) : v;
@@ -380,25 +395,14 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
           }
         } else {
           F[0].x = fmaf((float)acc[0], sc, F[0].x);
-          F[0].y = fmaf((float)acc[1], sc, F[0].y);
-          F[0].z = fmaf((float)acc[2], sc, F[0].z);
-          F[0].w = fmaf((float)acc[3], sc, F[0].w);
         }
       }
-#undef AQ_XLOAD
-#undef AQ_XCOL
     }
   }
 #undef AQ_DECODE_ISSUE
-#undef AQ_XROW_PTR_G
 
   if constexpr (!PARTIALS) {
-    if (MODE == kValu) {  // sum the four k-groups of each row
-      F[0].x = sum_kgroups(F[0].x);
-      F[0].y = sum_kgroups(F[0].y);
-      F[0].z = sum_kgroups(F[0].z);
-      F[0].w = sum_kgroups(F[0].w);
-    }
+    if (MODE == kValu) F[0].x = sum_kgroups(F[0].x);  // sum the four k-groups of each row
     // ordered split reduction through LDS
     if (S > 1) {
 #pragma unroll
@@ -446,28 +450,41 @@ void launch_one(Kern kern, dim3 grid, dim3 block, size_t lds, hipStream_t stream
   hipLaunchKernelGGL(kern, grid, block, lds, stream, args);
 }
 
-template <int BK, int MODE, int MG, int WAVES, int DEPTH, bool XLDS, bool PARTIALS>
+template <int BK, int MODE, int MG, int WAVES, int DEPTH, int XMODE, bool PARTIALS>
 void launch_rg(int RG, int R, int mchunks, size_t lds, hipStream_t stream, const DecodeArgs &args) {
   const dim3 block(WAVES * 64);
   switch (RG) {
-    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XLDS, PARTIALS>, dim3(R, mchunks), block, lds, stream, args); break;
-    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XLDS, PARTIALS>, dim3(R * 2, mchunks), block, lds, stream, args); break;
-    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XLDS, PARTIALS>, dim3(R * 4, mchunks), block, lds, stream, args); break;
+    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS>, dim3(R, mchunks), block, lds, stream, args); break;
+    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS>, dim3(R * 2, mchunks), block, lds, stream, args); break;
+    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS>, dim3(R * 4, mchunks), block, lds, stream, args); break;
   }
 }
 
-template <int BK, bool XLDS, bool PARTIALS>
-void launch_mg(int mode, int MG, int RG, int R, int mchunks, size_t lds, hipStream_t stream,
-               const DecodeArgs &args) {
+template <int BK, bool PARTIALS>
+void launch_mode(int mode, int xmode, int MG, int RG, int R, int mchunks, size_t lds, hipStream_t stream,
+                 const DecodeArgs &args) {
   if (mode == kValu) {
-    launch_rg<BK, kValu, 1, 16, 8, true, PARTIALS>(RG, R, 1, lds, stream, args);
+    launch_rg<BK, kValu, 1, 16, kPrivDepth, kXPriv, PARTIALS>(RG, R, 1, lds, stream, args);
+    return;
+  }
+  if (xmode == kXPriv) {
+    launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS>(RG, R, 1, lds, stream, args);
+    return;
+  }
+  if (xmode == kXShared) {
+    switch (MG) {
+      case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
+      case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
+      case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
+      default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
+    }
     return;
   }
   switch (MG) {
-    case 1: launch_rg<BK, kMfma, 1, 16, 8, XLDS, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
-    case 2: launch_rg<BK, kMfma, 2, 16, 6, XLDS, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
-    case 3: launch_rg<BK, kMfma, 3, 8, 6, XLDS, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
-    default: launch_rg<BK, kMfma, 4, 8, 6, XLDS, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
+    case 1: launch_rg<BK, kMfma, 1, 16, 8, kXGlobal, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
+    case 2: launch_rg<BK, kMfma, 2, 16, 6, kXGlobal, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
+    case 3: launch_rg<BK, kMfma, 3, 8, 6, kXGlobal, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
+    default: launch_rg<BK, kMfma, 4, 8, 6, kXGlobal, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
   }
 }
 
@@ -521,30 +538,28 @@ hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx,
   int RG = S > 0 ? waves / S : decode_rowgroups(w, M);
   if (RG != 1 && RG != 2 && RG != 4) RG = decode_rowgroups(w, M);
   const int mchunks = decode_mchunks(M);
-  // LDS: staged activations (when they fit) + split-reduction buffer
+  // Products: vector ALU for one token, MFMA otherwise.  Activations: a
+  // per-wave LDS slice of each batch for M <= 4 (no workgroup barrier),
+  // else the block's [16*MG][K] tokens in LDS when they fit, else global.
   const size_t red = (size_t)waves * MG * 64 * sizeof(float4);
-  int mode = M <= kValuMaxM ? kValu : kMfma;
-  const size_t xrows = mode == kValu ? (size_t)M : (size_t)16 * MG;
-  const size_t xbytes = (xrows * (size_t)w.K + 15) & ~(size_t)15;
-  const bool xlds = xbytes + red <= (size_t)kLdsBudget;
-  if (mode == kValu && !xlds) mode = kMfma;  // very long rows: global activation reads
-  const size_t lds = (mode == kValu || xlds) ? xbytes + red : red;
-  if (P) {
-    if (w.bK == 128) {
-      if (xlds) launch_mg<128, true, true>(mode, MG, RG, w.R, mchunks, lds, stream, args);
-      else launch_mg<128, false, true>(mode, MG, RG, w.R, mchunks, lds, stream, args);
-    } else {
-      if (xlds) launch_mg<64, true, true>(mode, MG, RG, w.R, mchunks, lds, stream, args);
-      else launch_mg<64, false, true>(mode, MG, RG, w.R, mchunks, lds, stream, args);
-    }
+  const int mode = M <= kValuMaxM ? kValu : kMfma;
+  int xmode;
+  size_t xbytes;
+  if (M <= kPrivMaxM) {
+    xmode = kXPriv;
+    xbytes = (size_t)waves * M * kPrivDepth * w.bK;
   } else {
-    if (w.bK == 128) {
-      if (xlds) launch_mg<128, true, false>(mode, MG, RG, w.R, mchunks, lds, stream, args);
-      else launch_mg<128, false, false>(mode, MG, RG, w.R, mchunks, lds, stream, args);
-    } else {
-      if (xlds) launch_mg<64, true, false>(mode, MG, RG, w.R, mchunks, lds, stream, args);
-      else launch_mg<64, false, false>(mode, MG, RG, w.R, mchunks, lds, stream, args);
-    }
+    xbytes = ((size_t)16 * MG * w.K + 15) & ~(size_t)15;
+    xmode = xbytes + red <= (size_t)kLdsBudget ? kXShared : kXGlobal;
+    if (xmode == kXGlobal) xbytes = 0;
+  }
+  const size_t lds = xbytes + red;
+  if (w.bK == 128) {
+    if (P) launch_mode<128, true>(mode, xmode, MG, RG, w.R, mchunks, lds, stream, args);
+    else launch_mode<128, false>(mode, xmode, MG, RG, w.R, mchunks, lds, stream, args);
+  } else {
+    if (P) launch_mode<64, true>(mode, xmode, MG, RG, w.R, mchunks, lds, stream, args);
+    else launch_mode<64, false>(mode, xmode, MG, RG, w.R, mchunks, lds, stream, args);
   }
   return hipGetLastError();
 }

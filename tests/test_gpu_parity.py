@@ -40,6 +40,9 @@ def test_small_workload_with_bias():
     (320, 1024, 128, 65),    # M spans two 64-token decode passes
     (256, 512, 128, 130),    # M spans two 128-token prefill blocks, ragged
     (512, 1536, 128, 200),
+    (256, 1536, 128, 3),     # 2..4 tokens: per-wave activation slices with MFMA
+    (64, 8448, 64, 2),       # 132 tile columns: labels counted from memory
+    (128, 10240, 128, 7),    # 16 tokens x K too large for LDS: global activation reads
 ])
 def test_ragged_shapes(N, K, bK, M):
     W, z, X = _ragged(N, K, bK, M, seed=N * 7 + K + M)
