@@ -13,9 +13,18 @@ One step = one pass of the whole hot path over one batch of synthetic input:
             Qwen3-4B-shaped projections (qkv 6144x2560, o 2560x4096,
             gate_up 19456x2560, down 2560x9728; 30% INT8 tiles in bands) at
             M = 2048 tokens.
-Inputs are resident in HBM before the timed region.  W warm-up steps, then K
-timed steps between device synchronizations; HIP events recorded on the
-launch stream time each segment and each linear call.
+Inputs are resident in HBM before the timed region.
+
+Timed region: W warm-up steps, then K steps whose launches are all enqueued
+while a GPU spin kernel holds the stream (the hold is sized from the
+measured host enqueue time, and the line reports whether the host stayed
+ahead), so the device runs the steps back to back as a captured runtime
+would; the pages time theirs under CUDA Graph, Table 22.  The region is
+bracketed by device synchronizations.  HIP events between the groups of
+each step (decode activation quantization, the 12 decode linears, prefill
+activation quantization, the 4 prefill linears) time the segments and the
+back-to-back linear calls; a linear kernel's average duration is its group's
+span over the number of calls.  ms_per_step is the events' span over K.
 
 The JSON line: value = decode HBM GB/s over the decode segment (algorithmic
 bytes: packed weights with per-row scales, labels, row offsets, INT8
@@ -107,56 +116,55 @@ def setup(aq, gen, torch):
     return dec, ws, pre
 
 
-class Recorder:
-    """HIP events on the launch stream around segments and calls."""
-
-    def __init__(self, torch, enabled):
-        self.torch, self.enabled = torch, enabled
-        self.calls = {"decode": [], "prefill": []}   # (start, end, units)
-        self.segs = {"decode": [], "prefill": []}
-
-    def ev(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    def totals(self, kind):
-        self.torch.cuda.synchronize()
-        seg_ms = sum(a.elapsed_time(b) for a, b in self.segs[kind])
-        call_ms = sum(a.elapsed_time(b) for a, b, _ in self.calls[kind])
-        units = sum(u for _, _, u in self.calls[kind])
-        return seg_ms, call_ms, units, len(self.calls[kind])
+def decode_quant(aq, dec):
+    """Activation quantization of the 12 decode calls (4 projections x 3 M)."""
+    for M in DECODE_M:
+        for proj, copies, xs, bufs in dec:
+            qx, sx, _ = bufs[M]
+            aq.aq_quant_act(xs[M], qx, sx)
 
 
-def run_step(aq, i, dec, ws, pre, rec: Recorder | None):
-    ws_bytes = ws.numel()
-    # ---- decode segment
-    s0 = rec.ev() if rec else None
+def decode_linears(aq, i, dec, ws):
+    """The 12 decode linear calls; step i reads weight copies 3i .. 3i+2 (mod 24)."""
     for mi, M in enumerate(DECODE_M):
         c = (i * len(DECODE_M) + mi) % N_COPIES
         for proj, copies, xs, bufs in dec:
             qx, sx, Y = bufs[M]
-            aq.aq_quant_act(xs[M], qx, sx)
-            pw = copies[c]
-            if rec:
-                a = rec.ev()
-            aq.aq_linear_decode(pw, qx, sx, None, 0, Y, ws)
-            if rec:
-                rec.calls["decode"].append((a, rec.ev(), linear_bytes(pw.plan, M)))
-    if rec:
-        s1 = rec.ev()
-        rec.segs["decode"].append((s0, s1))
-    # ---- prefill segment
+            aq.aq_linear_decode(copies[c], qx, sx, None, 0, Y, ws)
+
+
+def prefill_quant(aq, pre):
     for proj, pw, x, (qx, sx, Y) in pre:
         aq.aq_quant_act(x, qx, sx)
-        if rec:
-            a = rec.ev()
+
+
+def prefill_linears(aq, pre):
+    for proj, pw, x, (qx, sx, Y) in pre:
         aq.aq_linear_prefill(pw, qx, sx, None, Y)
-        if rec:
-            rec.calls["prefill"].append((a, rec.ev(), 2 * PREFILL_M * pw.plan.N * pw.plan.K))
-    if rec:
-        rec.segs["prefill"].append((s1, rec.ev()))
-    del ws_bytes
+
+
+def run_step(aq, i, dec, ws, pre):
+    decode_quant(aq, dec)
+    decode_linears(aq, i, dec, ws)
+    prefill_quant(aq, pre)
+    prefill_linears(aq, pre)
+
+
+def step_bytes_ops(dec, pre):
+    dbytes = sum(linear_bytes(copies[0].plan, M) for M in DECODE_M for _, copies, _, _ in dec)
+    pops = sum(2 * PREFILL_M * pw.plan.N * pw.plan.K for _, pw, _, _ in pre)
+    return dbytes, pops
+
+
+def sleep_cycles_per_us(torch):
+    """Rate of torch.cuda._sleep (a spinning kernel), measured with HIP events."""
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    torch.cuda._sleep(20_000_000)
+    b.record()
+    torch.cuda.synchronize()
+    return 20_000_000 / (a.elapsed_time(b) * 1e3)
 
 
 def cpu_baseline(budget_s: float):
@@ -223,19 +231,45 @@ def main():
     aq.lib()
     dec, ws, pre = setup(aq, gen, torch)
 
+    t_host = 0.0
     for i in range(args.warmup):
-        run_step(aq, i, dec, ws, pre, None)
-    torch.cuda.synchronize()
+        t = time.perf_counter()
+        run_step(aq, i, dec, ws, pre)
+        t_host = max(t_host, time.perf_counter() - t)   # host enqueue time of one step
+        torch.cuda.synchronize()
 
-    rec = Recorder(torch, True)
+    # ---- timed region: K steps enqueued behind a GPU hold, so the device
+    # runs them back to back; HIP events between the groups of each step
+    K = args.steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4 * K + 1)]
+    hold_us = 2.0 * t_host * 1e6 * (K + 1) + 2000.0
+    cyc = sleep_cycles_per_us(torch)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        run_step(aq, args.warmup + i, dec, ws, pre, rec)
+    torch.cuda._sleep(int(hold_us * cyc))
+    evs[0].record()
+    for i in range(K):
+        decode_quant(aq, dec)
+        evs[4 * i + 1].record()
+        decode_linears(aq, args.warmup + i, dec, ws)
+        evs[4 * i + 2].record()
+        prefill_quant(aq, pre)
+        evs[4 * i + 3].record()
+        prefill_linears(aq, pre)
+        evs[4 * i + 4].record()
+    t_enq = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    dseg, dcall, dbytes, ncalls_d = rec.totals("decode")
-    pseg, pcall, pops, ncalls_p = rec.totals("prefill")
+    el = lambda a, b: evs[a].elapsed_time(evs[b])  # noqa: E731  (ms)
+    dseg = sum(el(4 * i, 4 * i + 2) for i in range(K))
+    dcall = sum(el(4 * i + 1, 4 * i + 2) for i in range(K))
+    pseg = sum(el(4 * i + 2, 4 * i + 4) for i in range(K))
+    pcall = sum(el(4 * i + 3, 4 * i + 4) for i in range(K))
+    gpu_ms = el(0, 4 * K)
+    ncalls_d = K * len(DECODE_M) * len(dec)
+    ncalls_p = K * len(pre)
+    dbytes1, pops1 = step_bytes_ops(dec, pre)
+    dbytes, pops = dbytes1 * K, pops1 * K
     decode_gbs = dbytes / (dseg * 1e-3) / 1e9
     prefill_tops = pops / (pseg * 1e-3) / 1e12
     dk_gbs = dbytes / (dcall * 1e-3) / 1e9
@@ -247,7 +281,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "ms_per_step": round(gpu_ms / args.steps, 4),
+        "wall_ms_incl_hold": round(wall * 1e3, 2),
+        "host_enqueued_ahead": bool(t_enq * 1e6 < hold_us),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
