@@ -1,12 +1,15 @@
 // Per-token INT8 activation quantization (AlignQuant App. B.3: preparation
 // computes in FP64 and stores signed INT8 codes with FP32 scales; rounding
-// per App. B.2 eq. 5).  One workgroup of 256 threads per token row:
-//   pass 1: |x| max over the row (float4 loads, wavefront butterfly, then
-//           the four wave results through LDS);
-//   pass 2: codes = clip(rint(x / s), -128, 127) with s in FP64, 16 codes per
-//           thread per step written as one 16-byte store.
-// The row is read twice; the second read hits the cache for the row sizes of
-// the workloads (<= 70 KB per row).
+// per App. B.2 eq. 5).
+//
+// One workgroup per token row.  The row is read once into registers (NV
+// float4 per thread, coalesced 16-byte loads), its |x| maximum is reduced
+// across the wavefront with DPP row permutes and one ds_swizzle, then across
+// the waves through LDS; each thread then writes the INT8 codes of its own
+// float4 groups as 4-byte stores.  Decode-sized batches (few rows) take
+// 1024 threads per row so that each lane divides few elements; prefill-sized
+// batches take 256 threads per row and fill the chip with rows.  Rows longer
+// than the register-resident variants cover fall back to a two-pass loop.
 
 #include "aq_device.h"
 #include "aq_internal.h"
@@ -14,52 +17,144 @@
 namespace aq {
 namespace {
 
-__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, double s) {
-  const float in[4] = {a, b, c, d};
-  uint32_t w = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    double q = rint((double)in[e] / s);
-    q = fmin(fmax(q, -128.0), 127.0);
-    w |= ((uint32_t)((int)q & 0xFF)) << (8 * e);
-  }
-  return w;
+// code = clip(rint(x / s), -128, 127), FP64 division (correctly rounded),
+// rint ties to even.
+__device__ __forceinline__ uint32_t code_of(float x, double s) {
+  double q = rint((double)x / s);
+  q = fmin(fmax(q, -128.0), 127.0);
+  return (uint32_t)((int)q & 0xFF);
 }
 
-__global__ __launch_bounds__(256) void quant_act_kernel(const float *__restrict__ X, int K,
-                                                        int8_t *__restrict__ qx,
-                                                        float *__restrict__ sx) {
-  const size_t m = blockIdx.x;
-  const float4 *row = reinterpret_cast<const float4 *>(X + m * K);
-  float amax = 0.0f;
-  for (int c = threadIdx.x; c < K / 4; c += 256) {
-    const float4 v = row[c];
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  __shared__ float red[4];
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = amax;
+__device__ __forceinline__ uint32_t codes4(const float4 &v, double s) {
+  return code_of(v.x, s) | (code_of(v.y, s) << 8) | (code_of(v.z, s) << 16) |
+         (code_of(v.w, s) << 24);
+}
+
+// Bits of |x|: for non-negative IEEE floats the unsigned order of the bit
+// patterns is the numeric order, so the maximum is an integer max.
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+__device__ __forceinline__ uint32_t abs_bits4(const float4 &v) {
+  return max(max(abs_bits(v.x), abs_bits(v.y)), max(abs_bits(v.z), abs_bits(v.w)));
+}
+
+// Maximum over the 64 lanes of a wavefront, returned uniform.  DPP within
+// rows of 16 lanes (quad xor 1, quad xor 2, half-row mirror, row mirror),
+// ds_swizzle across the two rows of each 32-lane half, then the two halves.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+  return max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+             (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+}
+
+// Row maximum across the T/64 waves of the workgroup.
+template <int T>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+  __shared__ uint32_t red[T / 64];
+  v = wave_max_u32(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  uint32_t r = red[0];
+#pragma unroll
+  for (int w = 1; w < T / 64; ++w) r = max(r, red[w]);
+  return r;
+}
 
-  const double s = fmax((double)amax / 127.0, 1e-12);
-  if (threadIdx.x == 0) sx[m] = (float)s;
+// Scale of the App. B.3 rule: s = max(max|x| / 127, 1e-12), FP64.
+__device__ __forceinline__ double row_scale(uint32_t amax_bits) {
+  return fmax((double)__uint_as_float(amax_bits) / 127.0, 1e-12);
+}
 
-  uint4 *out = reinterpret_cast<uint4 *>(qx + m * K);
-  for (int c = threadIdx.x; c < K / 16; c += 256) {
-    const float4 a = row[4 * c + 0], b = row[4 * c + 1], d = row[4 * c + 2], e = row[4 * c + 3];
-    out[c] = make_uint4(quant4(a.x, a.y, a.z, a.w, s), quant4(b.x, b.y, b.z, b.w, s),
-                        quant4(d.x, d.y, d.z, d.w, s), quant4(e.x, e.y, e.z, e.w, s));
+template <int T, int NV>
+__global__ __launch_bounds__(T) void quant_act_kernel(const float *__restrict__ X, int K,
+                                                      int8_t *__restrict__ qx,
+                                                      float *__restrict__ sx) {
+  const size_t m = blockIdx.x;
+  const int n4 = K >> 2;
+  const float4 *row = reinterpret_cast<const float4 *>(X + m * K);
+  float4 v[NV];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = threadIdx.x + i * T;
+    v[i] = c < n4 ? row[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    amax = max(amax, abs_bits4(v[i]));
   }
+  const double s = row_scale(block_max_u32<T>(amax));
+  if (threadIdx.x == 0) sx[m] = (float)s;
+  uint32_t *out = reinterpret_cast<uint32_t *>(qx + m * K);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = threadIdx.x + i * T;
+    if (c < n4) out[c] = codes4(v[i], s);
+  }
+}
+
+// Any row length (K a multiple of 64): two passes over the row.
+__global__ __launch_bounds__(256) void quant_act_loop_kernel(const float *__restrict__ X, int K,
+                                                             int8_t *__restrict__ qx,
+                                                             float *__restrict__ sx) {
+  const size_t m = blockIdx.x;
+  const int n4 = K >> 2;
+  const float4 *row = reinterpret_cast<const float4 *>(X + m * K);
+  uint32_t amax = 0;
+  for (int c = threadIdx.x; c < n4; c += 256) amax = max(amax, abs_bits4(row[c]));
+  const double s = row_scale(block_max_u32<256>(amax));
+  if (threadIdx.x == 0) sx[m] = (float)s;
+  uint32_t *out = reinterpret_cast<uint32_t *>(qx + m * K);
+  for (int c = threadIdx.x; c < n4; c += 256) out[c] = codes4(row[c], s);
+}
+
+template <int T, int NV>
+hipError_t launch_rows(const float *X, int M, int K, int8_t *qx, float *sx, hipStream_t stream) {
+  hipLaunchKernelGGL((quant_act_kernel<T, NV>), dim3(M), dim3(T), 0, stream, X, K, qx, sx);
+  return hipGetLastError();
+}
+
+// Register-resident variants: float4 groups per thread.
+template <int T>
+hipError_t launch_t(int nv, const float *X, int M, int K, int8_t *qx, float *sx,
+                    hipStream_t stream) {
+  switch (nv) {
+    case 1: return launch_rows<T, 1>(X, M, K, qx, sx, stream);
+    case 2: return launch_rows<T, 2>(X, M, K, qx, sx, stream);
+    case 3: return launch_rows<T, 3>(X, M, K, qx, sx, stream);
+    case 4: return launch_rows<T, 4>(X, M, K, qx, sx, stream);
+    case 5: return launch_rows<T, 5>(X, M, K, qx, sx, stream);
+    case 6: return launch_rows<T, 6>(X, M, K, qx, sx, stream);
+    case 8: return launch_rows<T, 8>(X, M, K, qx, sx, stream);
+    case 12: return launch_rows<T, 12>(X, M, K, qx, sx, stream);
+    case 16: return launch_rows<T, 16>(X, M, K, qx, sx, stream);
+    case 20: return launch_rows<T, 20>(X, M, K, qx, sx, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int round_nv(int need) {
+  static const int kNV[] = {1, 2, 3, 4, 5, 6, 8, 12, 16, 20};
+  for (int v : kNV)
+    if (v >= need) return v;
+  return 0;
 }
 
 }  // namespace
 
 hipError_t launch_quant_act(const float *X, int M, int K, int8_t *qx, float *sx,
                             hipStream_t stream) {
-  hipLaunchKernelGGL(quant_act_kernel, dim3(M), dim3(256), 0, stream, X, K, qx, sx);
+  const int n4 = K / 4;
+  // Few rows: a wide workgroup per row keeps the per-lane FP64 work short.
+  if (M < 256) {
+    const int nv = round_nv((n4 + 1023) / 1024);
+    if (nv && nv <= 8) return launch_t<1024>(nv, X, M, K, qx, sx, stream);
+  } else {
+    const int nv = round_nv((n4 + 255) / 256);
+    if (nv) return launch_t<256>(nv, X, M, K, qx, sx, stream);
+  }
+  hipLaunchKernelGGL(quant_act_loop_kernel, dim3(M), dim3(256), 0, stream, X, K, qx, sx);
   return hipGetLastError();
 }
 

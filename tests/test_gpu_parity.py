@@ -5,7 +5,8 @@ import pytest
 import torch
 
 import mixed_precision_int_amd as aq
-from tests.parity import Case, say
+from oracle import aq_oracle as O
+from tests.parity import Case, say, to_dev
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
@@ -135,3 +136,31 @@ def test_repeated_calls_split_independent():
     d = gen.llama3b_decode("qkv", 4)
     c = Case(d["W"], d["zmap"], d["X"], name="splits")
     c.check_all(splits=(4, 8, 16, 0), phases=("decode",))
+
+
+@pytest.mark.parametrize("M,K", [
+    (1, 64),        # one float4 group per lane on a few lanes, most lanes idle
+    (3, 3072),      # 1024-thread rows, 3 groups on some lanes
+    (16, 8192),
+    (5, 17408),     # 1024-thread rows, 5 groups per lane (the longest register variant used)
+    (2, 40960),     # few rows too long for the 1024-thread variants: two-pass loop
+    (256, 2560),    # 256-thread rows
+    (300, 17408),   # 256-thread rows, 17 groups rounded up to 20
+    (256, 81984),   # rows too long for the 256-thread variants: two-pass loop
+])
+def test_quant_act_variants(M, K):
+    """Activation codes and scales bit-exact on every launch variant, with a
+    zero row, a row whose maximum is negative and a row of ties."""
+    rng = np.random.default_rng(M * 131 + K)
+    X = gen.acts_outliers(rng, M, K, max(1, K // 100), 30.0)
+    X[0, :] = 0.0
+    if M > 1:
+        X[1, :] = -np.abs(X[1, :])
+    if M > 2:
+        X[2, :] = np.resize(np.array([127.0, -0.5, 2.5, -127.0, 1.5], np.float32), K)
+    qx_ref, sx_ref = O.quant_act(X)
+    qx, sx = aq.aq_quant_act(to_dev(X))
+    torch.cuda.synchronize()
+    say(f"  quant_act M={M} K={K}")
+    assert np.array_equal(qx.cpu().numpy().astype(np.int64), qx_ref)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.astype(np.float32).view(np.uint32))
