@@ -45,6 +45,12 @@ def seed_for(config: int, layer: int = 0, proj: str | int = 0) -> int:
     return 1000 * config + 16 * layer + pid
 
 
+def act_seed(config: int, layer: int = 0, proj: str | int = 0, salt: int = 0) -> int:
+    """Seed of one activation input (a batch or prefill chunk `salt`):
+    disjoint from every weight seed, which stay below 10^6."""
+    return 1_000_000 * (1 + salt) + seed_for(config, layer, proj)
+
+
 def count_from_fraction(frac: float, T: int) -> int:
     """Number of INT8 tiles for a fraction: nearest integer, ties to even."""
     return int(round(frac * T))
