@@ -6,9 +6,10 @@ Bar (stated once here, used by every GPU test):
     activation codes, FP32 activation-scale bits, INT32 tile products;
   * outputs (FP32 epilogue vs the FP64 oracle):
       (i)  normwise   max|Y - y| <= 1e-4 * max|y|
-      (ii) componentwise |Y - y| <= 1e-4 * sum_j |s_x s_W P_j| + 1e-30
-    An FP32 evaluation of eq. 19 with C tile terms errs by at most about
-    (C + 2) * 2^-24 * sum_j |term_j|, far inside (ii) for C <= 200.
+      (ii) componentwise |Y - y| <= 1e-4 * (sum_j |s_x s_W P_j| + |bias_n|) + 1e-30
+    An FP32 evaluation of eq. 19 with C tile terms and the bias errs by at
+    most about (C + 3) * 2^-24 * (sum_j |term_j| + |bias_n|), far inside (ii)
+    for C <= 200.
 """
 from __future__ import annotations
 
@@ -99,6 +100,8 @@ class Case:
             r["P_rows"] = P
             r["y_rows"] = O.linear_from_partials(P, r["sx"][rows], r["sW"], self.bias)
             r["c_rows"] = O.abs_contrib(P, r["sx"][rows], r["sW"])
+            if self.bias is not None:
+                r["c_rows"] = r["c_rows"] + np.abs(self.bias.astype(np.float64))[None, :]
             r["rows"] = rows
         return r
 
