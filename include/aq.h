@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AQ_ABI_VERSION 1
+#define AQ_ABI_VERSION 2
 
 typedef enum aq_status {
   AQ_OK = 0,
@@ -146,10 +146,14 @@ aq_status aq_pack_weights(const float *W, const uint8_t *labels_host, aq_packed 
 aq_status aq_quant_act(const float *X, int M, int K, int8_t *qx, float *sx, void *stream);
 
 /* Device workspace, in bytes, that aq_linear_decode (phase 0) or
- * aq_linear_prefill (phase 1) needs for M rows with the given decode split
- * (0 = adaptive).  0 means no workspace is needed (the case for both phases
- * in this version; the arguments are kept so that callers size and pass a
- * workspace uniformly). */
+ * aq_linear_prefill / aq_linear_tile_partials with phase 1 need for M rows
+ * with the given decode split (0 = adaptive).  0 means no workspace is
+ * needed.  Decode never needs one in this version.  Prefill needs one for a
+ * long prompt (M >= 1024) on a projection that holds INT4 tiles: the
+ * temporary INT8 operand of App. E.3 (Prefill), N*K bytes of INT8 tiles in
+ * logical tile order, rounded up to 256, plus 4*N*(K/bK) bytes of scales.
+ * The caller owns the workspace; its contents need no initialization and are
+ * overwritten by every call that uses it. */
 size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split);
 
 /* Split count that aq_linear_decode uses for `split` = 0: the number of
@@ -181,17 +185,25 @@ aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx
 
 /* Compute-bound phase (Sec. 3.3 "Prefill weight reuse"; App. E.3): the same
  * Y as aq_linear_decode, computed with INT8 matrix-core (MFMA) tiles that
- * reuse each weight tile across many activation rows.  Same arguments; the
- * workspace may be NULL when aq_workspace_bytes(W, M, 1, 0) is 0.  Any
- * M >= 1 is accepted. */
+ * reuse each weight tile across many activation rows.  Short prompts
+ * (M < 1024) widen the mixed tiles on chip.  Long prompts (M >= 1024, with
+ * M*K and N*K below 2^31) first prepare the selected weights as INT8 tiles
+ * in logical tile order, once per call, in the workspace (App. E.3
+ * Prefill), then run the GEMM over them; a projection without INT4 tiles
+ * already stores its W8 buffer in that order and needs no workspace.
+ *   ws    device workspace of at least aq_workspace_bytes(W, M, 1, 0) bytes,
+ *         16-byte aligned (NULL when that is 0), else AQ_ERR_WORKSPACE
+ * Other arguments as aq_linear_decode.  Any M >= 1 is accepted. */
 aq_status aq_linear_prefill(const aq_packed *W, const int8_t *qx, const float *sx, int M,
                             const float *bias, float *Y, void *ws, size_t ws_bytes, void *stream);
 
 /* Debug: the INT32 tile products P[m, n, j] of eq. 19 (the parenthesized
  * product, before any scaling), written to P as INT32 [M][N][C] row-major,
- * computed by the decode (phase 0) or prefill (phase 1) kernels themselves. */
+ * computed by the decode (phase 0) or prefill (phase 1) kernels themselves,
+ * on the same route aq_linear_prefill takes for M rows.
+ *   ws    phase 1: workspace as for aq_linear_prefill (phase 0: unused) */
 aq_status aq_linear_tile_partials(const aq_packed *W, const int8_t *qx, int M, int phase,
-                                  int32_t *P, void *stream);
+                                  int32_t *P, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

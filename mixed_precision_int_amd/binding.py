@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
         "aq_decode_split": (i32, [ctypes.POINTER(AqPacked), i32]),
         "aq_linear_decode": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp, sz, vp]),
         "aq_linear_prefill": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
-        "aq_linear_tile_partials": (i32, [ctypes.POINTER(AqPacked), vp, i32, i32, vp, vp]),
+        "aq_linear_tile_partials": (i32, [ctypes.POINTER(AqPacked), vp, i32, i32, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -230,24 +230,35 @@ def aq_linear_decode(pw: PackedWeights, qx, sx, bias=None, split: int = 0, out=N
     return out
 
 
-def aq_linear_prefill(pw: PackedWeights, qx, sx, bias=None, out=None, stream=None):
-    """Prefill-phase linear (INT8 MFMA): FP32 Y [M, N]."""
+def _workspace(pw: PackedWeights, M: int, phase: int, ws, device):
+    import torch
+    need = aq_workspace_bytes(pw, M, phase, 0)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
+
+
+def aq_linear_prefill(pw: PackedWeights, qx, sx, bias=None, out=None, ws=None, stream=None):
+    """Prefill-phase linear (INT8 MFMA): FP32 Y [M, N].  A long prompt on a
+    projection with INT4 tiles needs a workspace (allocated here if not given)."""
     import torch
     M = qx.shape[0]
     if out is None:
         out = torch.empty((M, pw.N), dtype=torch.float32, device=qx.device)
+    ws, ws_bytes = _workspace(pw, M, AQ_PHASE_PREFILL, ws, qx.device)
     _check(lib().aq_linear_prefill(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias),
-                                   _ptr(out), None, 0, _stream(stream)), "aq_linear_prefill")
+                                   _ptr(out), _ptr(ws), ws_bytes, _stream(stream)), "aq_linear_prefill")
     return out
 
 
-def aq_linear_tile_partials(pw: PackedWeights, qx, phase: int, out=None, stream=None):
+def aq_linear_tile_partials(pw: PackedWeights, qx, phase: int, out=None, ws=None, stream=None):
     """INT32 tile products P [M, N, C] computed by the decode or prefill kernels."""
     import torch
     M = qx.shape[0]
     C = pw.plan.C
     if out is None:
         out = torch.empty((M, pw.N, C), dtype=torch.int32, device=qx.device)
+    ws, ws_bytes = (None, 0) if phase != AQ_PHASE_PREFILL else _workspace(pw, M, phase, ws, qx.device)
     _check(lib().aq_linear_tile_partials(ctypes.byref(pw.desc), _ptr(qx), M, phase, _ptr(out),
-                                         _stream(stream)), "aq_linear_tile_partials")
+                                         _ptr(ws), ws_bytes, _stream(stream)), "aq_linear_tile_partials")
     return out

@@ -59,6 +59,26 @@ int effective_split(const aq::PackedView &v, int M, int split) {
   return split > 0 ? split : aq::decode_split(v, M);
 }
 
+aq_status check_workspace(void *ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return AQ_OK;
+  if (!ws || ws_bytes < need) return AQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return AQ_ERR_ALIGN;
+  return AQ_OK;
+}
+
+// Prefill dispatch (Y, or INT32 products into P when P != nullptr).
+hipError_t run_prefill(const aq::PackedView &v, const int8_t *qx, const float *sx, int M,
+                       const float *bias, float *Y, int32_t *P, void *ws, hipStream_t s) {
+  if (!aq::prefill_long(v, M)) return aq::launch_prefill(v, qx, sx, M, bias, Y, P, s);
+  const int8_t *E = v.w8;
+  const float *Es = v.s8;
+  if (v.T4 > 0) {
+    const hipError_t e = aq::launch_expand(v, ws, s, &E, &Es);
+    if (e != hipSuccess) return e;
+  }
+  return aq::launch_prefill_dense(E, Es, v.N, v.K, v.bK, qx, sx, M, bias, Y, P, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,8 +196,9 @@ int aq_decode_split(const aq_packed *W, int M) {
 
 size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split) {
   if (check_packed(W) != AQ_OK || M <= 0) return 0;
-  if (phase != AQ_PHASE_DECODE) return 0;
   const aq::PackedView v = aq::view_of(*W);
+  if (phase == AQ_PHASE_PREFILL) return aq::prefill_workspace_bytes(v, M);
+  if (phase != AQ_PHASE_DECODE) return 0;
   if (split < 0 || (split > 0 && !aq::decode_split_supported(M, split))) return 0;
   return aq::decode_workspace_bytes(v, M, effective_split(v, M, split));
 }
@@ -193,10 +214,8 @@ aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx
   if (split < 0 || (split > 0 && !aq::decode_split_supported(M, split))) return AQ_ERR_ARG;
   const int S = effective_split(v, M, split);
   const size_t need = aq::decode_workspace_bytes(v, M, S);
-  if (need > 0) {
-    if (!ws || ws_bytes < need) return AQ_ERR_WORKSPACE;
-    if (!aligned16(ws)) return AQ_ERR_ALIGN;
-  }
+  st = check_workspace(ws, ws_bytes, need);
+  if (st != AQ_OK) return st;
   return aq::launch_decode(v, qx, sx, M, bias, Y, S, ws, nullptr,
                            static_cast<hipStream_t>(stream)) == hipSuccess
              ? AQ_OK
@@ -205,20 +224,21 @@ aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx
 
 aq_status aq_linear_prefill(const aq_packed *W, const int8_t *qx, const float *sx, int M,
                             const float *bias, float *Y, void *ws, size_t ws_bytes, void *stream) {
-  (void)ws;
-  (void)ws_bytes;
   aq_status st = check_packed(W);
   if (st != AQ_OK) return st;
   st = check_linear_io(W, qx, sx, M, bias, Y);
   if (st != AQ_OK || M == 0) return st;
-  return aq::launch_prefill(aq::view_of(*W), qx, sx, M, bias, Y, nullptr,
-                            static_cast<hipStream_t>(stream)) == hipSuccess
+  const aq::PackedView v = aq::view_of(*W);
+  st = check_workspace(ws, ws_bytes, aq::prefill_workspace_bytes(v, M));
+  if (st != AQ_OK) return st;
+  return run_prefill(v, qx, sx, M, bias, Y, nullptr, ws, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
              ? AQ_OK
              : AQ_ERR_HIP;
 }
 
 aq_status aq_linear_tile_partials(const aq_packed *W, const int8_t *qx, int M, int phase,
-                                  int32_t *P, void *stream) {
+                                  int32_t *P, void *ws, size_t ws_bytes, void *stream) {
   aq_status st = check_packed(W);
   if (st != AQ_OK) return st;
   if (phase != AQ_PHASE_DECODE && phase != AQ_PHASE_PREFILL) return AQ_ERR_ARG;
@@ -228,11 +248,15 @@ aq_status aq_linear_tile_partials(const aq_packed *W, const int8_t *qx, int M, i
   if (!aligned16(qx) || !aligned4(P)) return AQ_ERR_ALIGN;
   const aq::PackedView v = aq::view_of(*W);
   if ((long long)M * v.N * v.C > (1LL << 40)) return AQ_ERR_SHAPE;
+  if (phase == AQ_PHASE_PREFILL) {
+    st = check_workspace(ws, ws_bytes, aq::prefill_workspace_bytes(v, M));
+    if (st != AQ_OK) return st;
+  }
   hipError_t e = phase == AQ_PHASE_DECODE
                      ? aq::launch_decode(v, qx, nullptr, M, nullptr, nullptr, 1, nullptr, P,
                                          static_cast<hipStream_t>(stream))
-                     : aq::launch_prefill(v, qx, nullptr, M, nullptr, nullptr, P,
-                                          static_cast<hipStream_t>(stream));
+                     : run_prefill(v, qx, nullptr, M, nullptr, nullptr, P, ws,
+                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? AQ_OK : AQ_ERR_HIP;
 }
 

@@ -47,6 +47,33 @@ hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx,
 hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx, int M,
                           const float *bias, float *Y, int32_t *P, hipStream_t stream);
 
+// Long-prefill GEMM over INT8 tiles in logical tile order: E holds tile
+// (r, j) at (r*C + j) * 64*bK bytes (b_K/16 panels of [64][16]) and Es its
+// 64 FP32 row scales at (r*C + j) * 64.  P != nullptr writes INT32 products.
+hipError_t launch_prefill_dense(const int8_t *E, const float *Es, int N, int K, int bK,
+                                const int8_t *qx, const float *sx, int M, const float *bias,
+                                float *Y, int32_t *P, hipStream_t stream);
+
+// Temporary INT8 operand of long prefill: bytes of the buffer (INT8 tiles in
+// logical order, then FP32 scales), and the launch that fills it from the
+// packed model; *E / *Es receive the two parts inside ws.
+size_t expand_bytes(const PackedView &w);
+hipError_t launch_expand(const PackedView &w, void *ws, hipStream_t stream, const int8_t **E,
+                         const float **Es);
+
+// Prefill routing: prompts of at least kLongPrefillM rows run the GEMM over
+// INT8 tiles in logical order (the packed W8 buffer itself when the map has
+// no INT4 tile, else the temporary buffer); shorter ones prepare the mixed
+// tiles on chip.  The dense GEMM addresses operands with 32-bit offsets.
+constexpr int kLongPrefillM = 1024;
+inline bool prefill_long(const PackedView &w, int M) {
+  return M >= kLongPrefillM && (long long)M * w.K < (1LL << 31) &&
+         (long long)w.N * w.K < (1LL << 31);
+}
+inline size_t prefill_workspace_bytes(const PackedView &w, int M) {
+  return prefill_long(w, M) && w.T4 > 0 ? expand_bytes(w) : 0;
+}
+
 // Adaptive decode split (host heuristic), the split values the kernel
 // supports for M tokens, and the workspace a split needs (none).
 int decode_split(const PackedView &w, int M);

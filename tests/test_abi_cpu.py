@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(aqlib):
 
 
 def test_abi_version_and_status_strings(aqlib):
-    assert B.aq_abi_version() == 1
+    assert B.aq_abi_version() == 2
     for code in list(B.STATUS) + [-99]:
         assert aqlib.aq_status_string(code)
 
@@ -77,8 +77,8 @@ def decode(d, qx=FAKE, sx=FAKE, M=4, bias=None, Y=FAKE, split=1, ws=None, ws_byt
     return B.lib().aq_linear_decode(ctypes.byref(d), qx, sx, M, bias, Y, split, ws, ws_bytes, None)
 
 
-def prefill(d, qx=FAKE, sx=FAKE, M=4, bias=None, Y=FAKE):
-    return B.lib().aq_linear_prefill(ctypes.byref(d), qx, sx, M, bias, Y, None, 0, None)
+def prefill(d, qx=FAKE, sx=FAKE, M=4, bias=None, Y=FAKE, ws=None, ws_bytes=0):
+    return B.lib().aq_linear_prefill(ctypes.byref(d), qx, sx, M, bias, Y, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("over,code", [
@@ -108,6 +108,29 @@ def test_io_rejected(aqlib):
     assert decode(d) == -5                                       # labels read as 32-bit words
 
 
+def test_long_prefill_workspace(aqlib):
+    """A long prompt on a projection with INT4 tiles needs the temporary INT8
+    operand (App. E.3): N*K bytes rounded up to 256, then 4*N*C bytes of
+    scales; a missing, short or misaligned workspace is rejected on the host."""
+    ws = B.lib().aq_workspace_bytes
+    for N, K, bK in [(256, 512, 128), (19456, 2560, 128), (192, 640, 64)]:
+        R, C = N // 64, K // bK
+        d = fake_packed(N=N, K=K, bK=bK, T4=R * C - 1, T8=1)
+        need = ((N * K + 255) // 256) * 256 + 4 * N * C
+        assert ws(ctypes.byref(d), 1024, 1, 0) == need
+        assert ws(ctypes.byref(d), 8192, 1, 0) == need
+        assert ws(ctypes.byref(d), 1023, 1, 0) == 0          # short prompt: on-chip widening
+        d8 = fake_packed(N=N, K=K, bK=bK, T4=0, T8=R * C)
+        assert ws(ctypes.byref(d8), 4096, 1, 0) == 0         # W8 already in logical order
+        assert prefill(d, M=1024) == -6
+        assert prefill(d, M=1024, ws=FAKE, ws_bytes=need - 1) == -6
+        assert prefill(d, M=1024, ws=FAKE + 4, ws_bytes=need) == -5
+        assert B.lib().aq_linear_tile_partials(ctypes.byref(d), FAKE, 1024, 1, FAKE, None, 0, None) == -6
+    # beyond 32-bit operand offsets the long route is not taken
+    d = fake_packed(N=64, K=1 << 20, bK=128, T4=(1 << 13) - 1, T8=1)
+    assert ws(ctypes.byref(d), 4096, 1, 0) == 0
+
+
 def test_quant_act_and_partials_rejected(aqlib):
     L = B.lib()
     assert L.aq_quant_act(FAKE, 4, 100, FAKE, FAKE, None) == -2     # K % 64
@@ -116,9 +139,9 @@ def test_quant_act_and_partials_rejected(aqlib):
     assert L.aq_quant_act(None, 4, 128, FAKE, FAKE, None) == -1
     assert L.aq_quant_act(FAKE + 4, 4, 128, FAKE, FAKE, None) == -5
     d = fake_packed()
-    assert L.aq_linear_tile_partials(ctypes.byref(d), FAKE, 4, 2, FAKE, None) == -8
-    assert L.aq_linear_tile_partials(ctypes.byref(d), None, 4, 0, FAKE, None) == -1
-    assert L.aq_linear_tile_partials(ctypes.byref(d), FAKE, 0, 1, FAKE, None) == 0
+    assert L.aq_linear_tile_partials(ctypes.byref(d), FAKE, 4, 2, FAKE, None, 0, None) == -8
+    assert L.aq_linear_tile_partials(ctypes.byref(d), None, 4, 0, FAKE, None, 0, None) == -1
+    assert L.aq_linear_tile_partials(ctypes.byref(d), FAKE, 0, 1, FAKE, None, 0, None) == 0
 
 
 def test_pack_rejects_label_mismatch(aqlib):

@@ -164,3 +164,28 @@ def test_quant_act_variants(M, K):
     say(f"  quant_act M={M} K={K}")
     assert np.array_equal(qx.cpu().numpy().astype(np.int64), qx_ref)
     assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K,bK,M,kind", [
+    (256, 512, 128, 1030, "mixed"),     # 4 tile columns: only the guarded tail of the column loop
+    (192, 1536, 128, 1024, "mixed"),    # 3 tile rows (partial N block), 12 columns = 2 unrolled groups
+    (320, 2560, 128, 1100, "mixed"),    # 20 columns: 3 groups + a 2-column tail; ragged M
+    (128, 128, 128, 1024, "mixed"),     # a single tile column
+    (256, 640, 64, 1040, "mixed"),      # 64 x 64 tiles
+    (256, 1024, 128, 2048, "all_int4"),
+    (256, 1024, 128, 1536, "all_int8"), # W8 already in logical order: no temporary buffer
+])
+def test_long_prefill_temporary_int8(N, K, bK, M, kind):
+    """Prompts of >= 1024 rows: the selected weights are expanded once per
+    call to INT8 tiles in logical order and the GEMM runs over them (App. E.3
+    Prefill); tile products on every row and outputs against the oracle."""
+    rng = np.random.default_rng(N + K + M)
+    W = gen.weights(rng, N, K)
+    R, C = N // 64, K // bK
+    z = {"mixed": gen.map_uniform(rng, R, C, 0.4), "all_int4": np.full((R, C), 4),
+         "all_int8": np.full((R, C), 8)}[kind]
+    X = gen.acts_heavy_tail(rng, M, K)
+    bias = rng.standard_normal(N).astype(np.float32)
+    need = aq.aq_workspace_bytes(Case(W, z, X, 64, bK).gpu_pack(), M, aq.AQ_PHASE_PREFILL)
+    assert (need == 0) == (kind == "all_int8")
+    Case(W, z, X, 64, bK, bias=bias, name=f"long{N}x{K}/bK{bK}/M{M}/{kind}").check_all(phases=("prefill",))
