@@ -15,7 +15,7 @@ cut into equal b_N x b_K tiles, R = N / b_N tile rows, C = K / b_K tile
 columns, T = R*C.  z[r, j] in {4, 8} is the precision map.
 
 Readings taken where the pages are silent or are overridden by the task
-statement (each one is listed with its justification in the design doc):
+statement:
   * weight scale: one FP32 scale per (output row n, tile column j), absmax rule
     s = max(absmax / q_max, 1e-12) computed in FP64 (App. B.2 eq. 5 and the
     1e-12 floor of eq. 6);
