@@ -76,6 +76,8 @@ hipError_t run_prefill(const aq::PackedView &v, const int8_t *qx, const float *s
     const hipError_t e = aq::launch_expand(v, ws, s, &E, &Es);
     if (e != hipSuccess) return e;
   }
+  if (aq::prefill_big_fits(v.N, v.K, v.bK, M))
+    return aq::launch_prefill_big(E, Es, v.N, v.K, qx, sx, M, bias, Y, P, s);
   return aq::launch_prefill_dense(E, Es, v.N, v.K, v.bK, qx, sx, M, bias, Y, P, s);
 }
 

@@ -54,6 +54,15 @@ hipError_t launch_prefill_dense(const int8_t *E, const float *Es, int N, int K, 
                                 const int8_t *qx, const float *sx, int M, const float *bias,
                                 float *Y, int32_t *P, hipStream_t stream);
 
+// Persistent 256 x 256-tile variant of the long-prefill GEMM (b_K = 128,
+// N >= 6144, at least one tile per compute unit, M*N < 2^29); same operands;
+// P != nullptr writes INT32 products instead of Y.
+int compute_units();
+bool prefill_big_fits(int N, int K, int bK, int M);
+hipError_t launch_prefill_big(const int8_t *E, const float *Es, int N, int K, const int8_t *qx,
+                              const float *sx, int M, const float *bias, float *Y, int32_t *P,
+                              hipStream_t stream);
+
 // Temporary INT8 operand of long prefill: bytes of the buffer (INT8 tiles in
 // logical order, then FP32 scales), and the launch that fills it from the
 // packed model; *E / *Es receive the two parts inside ws.

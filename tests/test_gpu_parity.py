@@ -189,3 +189,17 @@ def test_long_prefill_temporary_int8(N, K, bK, M, kind):
     need = aq.aq_workspace_bytes(Case(W, z, X, 64, bK).gpu_pack(), M, aq.AQ_PHASE_PREFILL)
     assert (need == 0) == (kind == "all_int8")
     Case(W, z, X, 64, bK, bias=bias, name=f"long{N}x{K}/bK{bK}/M{M}/{kind}").check_all(phases=("prefill",))
+
+
+def test_long_prefill_persistent_tiles_ragged():
+    """The persistent 256 x 256-tile kernel (taken when the prompt yields at
+    least one tile per compute unit): 257 tile rows (the last N block holds
+    one), 1040 tokens (the last M block holds 16), two tile columns, a bias;
+    tile products on every row and outputs against the oracle."""
+    N, K, M = 16448, 256, 1040
+    rng = np.random.default_rng(77)
+    W = gen.weights(rng, N, K)
+    z = gen.map_uniform(rng, N // 64, K // 128, 0.35)
+    X = gen.acts_heavy_tail(rng, M, K)
+    bias = rng.standard_normal(N).astype(np.float32)
+    Case(W, z, X, 64, 128, bias=bias, name="persistent16448x256/M1040").check_all(phases=("prefill",))
