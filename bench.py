@@ -65,6 +65,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes three times (the "
+                         "known-size reference for the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar="CSV",
+                    help="print the per-launch HBM traffic summary from four rocprofv3 counter "
+                         "CSVs: bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -156,6 +162,72 @@ def step_bytes_ops(dec, pre):
     return dbytes, pops
 
 
+# ---------------------------------------------------------------- HBM traffic
+# The roofline's traffic figure comes from rocprofv3 counter runs whose summary
+# is committed under profiles/ (with the commands that made it); it is
+# reported only while the kernel sources still hash to what was profiled.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_llama3b_decode_qwen4b_prefill.md")
+KERNEL_SOURCES = {
+    "decode": ["aq_decode.hip", "aq_device.h"],
+    "prefill": ["aq_expand.hip", "aq_prefill_dense.hip", "aq_prefill_big.hip", "aq_device.h"],
+}
+
+
+def sources_sha(kind: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "mixed_precision_int_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic() -> dict:
+    """{kind: bytes per launch} from the committed counter summary, for the
+    kinds whose kernel sources are unchanged since it was taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        blob = json.loads(text.split("```json")[1].split("```")[0])
+    except (OSError, IndexError, ValueError):
+        return {}
+    out = {}
+    for kind, rec in blob.get("kernels", {}).items():
+        if kind in KERNEL_SOURCES and rec.get("sources_sha") == sources_sha(kind):
+            out[kind] = rec["hbm_bytes_per_call"]
+    return out
+
+
+def traffic_summary(paths) -> dict:
+    """Per-call HBM bytes of the decode and prefill linears from the counter
+    CSVs of a bench run (every dispatch of the run, warm-up included,
+    averaged per call), each counter scaled by bytes / counter of a plain
+    copy of known size."""
+    import csv
+
+    def read(path):
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(open(path))]
+
+    def copy_factor(path, nbytes):
+        vals = sorted(v for name, v in read(path) if "copy" in name.lower() or "elementwise" in name.lower())
+        return nbytes / (vals[len(vals) // 2] * 1024.0)
+
+    cal_bytes = int(os.environ.get("AQ_COPY_MB", "512")) << 20
+    f_fetch, f_write = copy_factor(paths[2], cal_bytes), copy_factor(paths[3], cal_bytes)
+    kinds = {"decode": (("decode_kernel",), ("decode_kernel",)),
+             "prefill": (("prefill_dense_kernel", "prefill_big_kernel", "prefill_kernel", "expand_kernel"),
+                         ("prefill_dense_kernel", "prefill_big_kernel", "prefill_kernel"))}
+    res = {}
+    for kind, (members, calls) in kinds.items():
+        fetch = sum(v for n, v in read(paths[0]) if any(k in n for k in members)) * 1024.0 * f_fetch
+        write = sum(v for n, v in read(paths[1]) if any(k in n for k in members)) * 1024.0 * f_write
+        ncalls = max(1, sum(1 for n, _ in read(paths[0]) if any(k in n for k in calls)))
+        res[kind] = dict(hbm_bytes_per_call=int((fetch + write) / ncalls),
+                         fetch_bytes_per_call=int(fetch / ncalls), write_bytes_per_call=int(write / ncalls),
+                         calls=ncalls, sources_sha=sources_sha(kind))
+    return dict(copy_calibration=dict(bytes=cal_bytes, fetch_factor=round(f_fetch, 4),
+                                      write_factor=round(f_write, 4)), kernels=res)
+
+
 def sleep_cycles_per_us(torch):
     """Rate of torch.cuda._sleep (a spinning kernel), measured with HIP events."""
     torch.cuda.synchronize()
@@ -217,6 +289,9 @@ def cpu_baseline(budget_s: float):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        print(json.dumps(traffic_summary(args.traffic_summary), indent=1))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a "
@@ -228,6 +303,15 @@ def main():
     from workloads import gen
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}))
+        return
     aq.lib()
     dec, ws, pre = setup(aq, gen, torch)
 
@@ -274,6 +358,7 @@ def main():
     prefill_tops = pops / (pseg * 1e-3) / 1e12
     dk_gbs = dbytes / (dcall * 1e-3) / 1e9
     pk_tops = pops / (pcall * 1e-3) / 1e12
+    traffic = load_traffic()
     out = {
         "metric": METRIC,
         "value": round(decode_gbs, 2),
@@ -304,7 +389,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dk_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic.get("decode"),
+            "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes_per_call": dbytes1 // (len(DECODE_M) * len(dec)),
             "avg_call_us": round(dcall * 1e3 / max(ncalls_d, 1), 3),
             "bytes_per_step": dbytes // args.steps,
         },
@@ -318,7 +405,8 @@ def main():
                 "peak": INT8_PEAK_TOPS,
                 "unit": "TOPS",
                 "frac": round(pk_tops / INT8_PEAK_TOPS, 4),
-                "traffic": None,
+                "traffic": traffic.get("prefill"),
+                "traffic_unit": "HBM bytes per call",
                 "avg_call_us": round(pcall * 1e3 / max(ncalls_p, 1), 3),
             },
         },
