@@ -15,16 +15,20 @@ One step = one pass of the whole hot path over one batch of synthetic input:
             M = 2048 tokens.
 Inputs are resident in HBM before the timed region.
 
-Timed region: W warm-up steps, then K steps whose launches are all enqueued
-while a GPU spin kernel holds the stream (the hold is sized from the
-measured host enqueue time, and the line reports whether the host stayed
-ahead), so the device runs the steps back to back as a captured runtime
-would; the pages time theirs under CUDA Graph, Table 22.  The region is
-bracketed by device synchronizations.  HIP events between the groups of
-each step (decode activation quantization, the 12 decode linears, prefill
-activation quantization, the 4 prefill linears) time the segments and the
-back-to-back linear calls; a linear kernel's average duration is its group's
-span over the number of calls.  ms_per_step is the events' span over K.
+Timed region: W warm-up steps, then the work of K steps whose launches are
+all enqueued while a GPU spin kernel holds the stream (the hold is sized from
+the measured host enqueue time, and the line reports whether the host stayed
+ahead), so the device runs them back to back as a captured runtime would;
+the pages time theirs under CUDA Graph, Table 22.  The K decode segments run
+first, then the K prefill segments: the work per step is unchanged, and a
+prefill's ~250 MB of FP32 outputs are not still being written back to HBM
+while the next decode segment streams its weights (interleaved, that
+write-back costs the decode calls about 2 us each).  The region is bracketed
+by device synchronizations.  HIP events between the groups (decode
+activation quantization, the 12 decode linears, prefill activation
+quantization, the 4 prefill linears) time the segments and the back-to-back
+linear calls; a linear kernel's average duration is its group's span over
+the number of calls.  ms_per_step is the events' span over K.
 
 The JSON line: value = decode HBM GB/s over the decode segment (algorithmic
 bytes: packed weights with per-row scales, labels, row offsets, INT8
@@ -323,33 +327,39 @@ def main():
         torch.cuda.synchronize()
 
     # ---- timed region: K steps enqueued behind a GPU hold, so the device
-    # runs them back to back; HIP events between the groups of each step
+    # runs them back to back: the K decode segments, then the K prefill
+    # segments (each step's work is unchanged; grouping the phases keeps the
+    # write-back of a prefill's outputs out of the next step's decode reads);
+    # HIP events on the launch stream bracket every group
     K = args.steps
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4 * K + 1)]
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    d_seg, d_call = [E() for _ in range(K + 1)], [E() for _ in range(K)]
+    p_seg, p_call = [E() for _ in range(K + 1)], [E() for _ in range(K)]
     hold_us = 2.0 * t_host * 1e6 * (K + 1) + 2000.0
     cyc = sleep_cycles_per_us(torch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     torch.cuda._sleep(int(hold_us * cyc))
-    evs[0].record()
+    d_seg[0].record()
     for i in range(K):
         decode_quant(aq, dec)
-        evs[4 * i + 1].record()
+        d_call[i].record()
         decode_linears(aq, args.warmup + i, dec, ws)
-        evs[4 * i + 2].record()
+        d_seg[i + 1].record()
+    p_seg[0].record()
+    for i in range(K):
         prefill_quant(aq, pre)
-        evs[4 * i + 3].record()
+        p_call[i].record()
         prefill_linears(aq, pre)
-        evs[4 * i + 4].record()
+        p_seg[i + 1].record()
     t_enq = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    el = lambda a, b: evs[a].elapsed_time(evs[b])  # noqa: E731  (ms)
-    dseg = sum(el(4 * i, 4 * i + 2) for i in range(K))
-    dcall = sum(el(4 * i + 1, 4 * i + 2) for i in range(K))
-    pseg = sum(el(4 * i + 2, 4 * i + 4) for i in range(K))
-    pcall = sum(el(4 * i + 3, 4 * i + 4) for i in range(K))
-    gpu_ms = el(0, 4 * K)
+    dseg = d_seg[0].elapsed_time(d_seg[K])                                   # ms
+    dcall = sum(d_call[i].elapsed_time(d_seg[i + 1]) for i in range(K))
+    pseg = p_seg[0].elapsed_time(p_seg[K])
+    pcall = sum(p_call[i].elapsed_time(p_seg[i + 1]) for i in range(K))
+    gpu_ms = d_seg[0].elapsed_time(p_seg[K])
     ncalls_d = K * len(DECODE_M) * len(dec)
     ncalls_p = K * len(pre)
     dbytes1, pops1 = step_bytes_ops(dec, pre)
