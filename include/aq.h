@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AQ_ABI_VERSION 2
+#define AQ_ABI_VERSION 3
 
 typedef enum aq_status {
   AQ_OK = 0,
@@ -148,35 +148,52 @@ aq_status aq_quant_act(const float *X, int M, int K, int8_t *qx, float *sx, void
 /* Device workspace, in bytes, that aq_linear_decode (phase 0) or
  * aq_linear_prefill / aq_linear_tile_partials with phase 1 need for M rows
  * with the given decode split (0 = adaptive).  0 means no workspace is
- * needed.  Decode never needs one in this version.  Prefill needs one for a
- * long prompt (M >= 1024) on a projection that holds INT4 tiles: the
- * temporary INT8 operand of App. E.3 (Prefill), N*K bytes of INT8 tiles in
- * logical tile order, rounded up to 256, plus 4*N*(K/bK) bytes of scales.
- * The caller owns the workspace; its contents need no initialization and are
- * overwritten by every call that uses it. */
+ * needed.  The caller owns the workspace (16-byte aligned).
+ *   Decode needs one when the call divides each row block's input columns
+ *   into Z > 1 workgroup chunks (App. E.3 split-K across workgroups), which
+ *   it does when the staged INT8 activations of all K columns would not fit
+ *   in on-chip memory (large M*K).  Its first 256 KiB hold arrival counters
+ *   (one 32-bit counter per row block and chunk of up to 64 tokens, at most
+ *   65536 per launch;
+ *   calls with more take several launches), the rest the chunks' FP32 sums.
+ *   The counters must be zero before the first decode call that uses the
+ *   workspace (e.g. a zero-filled allocation); every decode call leaves them
+ *   zero, so one workspace serves calls of any projection.  Decode calls
+ *   that share a workspace must not run concurrently.
+ *   Prefill needs one for a long prompt (M >= 1024) on a projection that
+ *   holds INT4 tiles: the temporary INT8 operand of App. E.3 (Prefill), N*K
+ *   bytes of INT8 tiles in logical tile order, rounded up to 256, plus
+ *   4*N*(K/bK) bytes of scales; its contents need no initialization and are
+ *   overwritten by every call that uses it. */
 size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split);
 
 /* Split count that aq_linear_decode uses for `split` = 0: the number of
- * input-column groups each 16-row output group is divided into (adaptive,
- * chosen from the projection geometry). */
+ * input-column groups each 16-row output group is divided into inside one
+ * workgroup (adaptive, chosen from the projection geometry and M). */
 int aq_decode_split(const aq_packed *W, int M);
 
 /* Memory-bound phase (Sec. 3.3 "Decode parallelism"; App. E.3 Table 5):
  *   Y[m,n] = sx[m] * sum_j sW[n,j] * P[m,n,j]  (+ bias[n]),
  * P[m,n,j] the INT32 product of the INT8 activation codes and the tile's
  * codes widened to INT8 (eq. 19).  Work is spread over output features and
- * input-column groups: each 16-row output group is divided into S splits,
- * split s covering input-tile columns floor(C*s/S) .. floor(C*(s+1)/S)-1,
- * and the FP32 partials of the splits are summed in increasing s (App. E.3)
- * inside the same kernel launch.
+ * input-column groups: the columns of each 16-row output group are cut into
+ * Z workgroup chunks of S splits each, split s of the Z*S covering
+ * input-tile columns floor(C*s/(Z*S)) .. floor(C*(s+1)/(Z*S))-1, and the
+ * FP32 partials of the splits are summed in increasing s (App. E.3): inside
+ * a workgroup through on-chip memory, across chunks by the workgroup that
+ * finishes its row block last, all in one kernel launch.  Z = 1 unless
+ * aq_workspace_bytes(W, M, 0, split) is non-zero.
  *   qx    device INT8 [M][K] (from aq_quant_act);  sx device FP32 [M]
  *   bias  device FP32 [N] or NULL
  *   Y     device FP32 [M][N] row-major (written, not accumulated)
  *   split 0 = adaptive (aq_decode_split); otherwise S, which must be one of
- *         Wv, Wv/2, Wv/4 with Wv = 16 when M <= 32 and 8 above (other
- *         values return AQ_ERR_ARG)
+ *         Wv, Wv/2, Wv/4 with Wv = 16 when M <= 32 or when the
+ *         projection's packed tiles exceed 16 MB, else 8 (other values
+ *         return AQ_ERR_ARG); Z is then the fewest chunks whose
+ *         activations fit on chip
  *   ws    device workspace of at least aq_workspace_bytes(W, M, 0, split)
- *         bytes (currently 0: NULL is accepted)
+ *         bytes, 16-byte aligned, counters zero (NULL when that is 0), else
+ *         AQ_ERR_WORKSPACE
  * Any M >= 1 is accepted (tokens are processed 64 at a time); M == 0 is a
  * no-op. */
 aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx, int M,

@@ -213,16 +213,39 @@ def aq_decode_split(pw: PackedWeights, M: int) -> int:
     return int(lib().aq_decode_split(ctypes.byref(pw.desc), M))
 
 
+# Decode workspaces, one per (device, stream), grown on demand.  Allocated
+# zeroed; every decode call leaves its arrival counters at zero again, so a
+# workspace is reused by the calls of its stream (which never overlap).
+_DECODE_WS: dict = {}
+
+
+def decode_workspace(nbytes: int, device, stream=None):
+    """A zero-initialized decode workspace of at least nbytes for the stream."""
+    import torch
+    st = torch.cuda.current_stream(device) if stream is None else stream
+    key = (str(torch.device(device)), st.cuda_stream)
+    ws = _DECODE_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            st.synchronize()  # the old buffer may still be in use on its stream
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        torch.cuda.current_stream(device).synchronize()
+        _DECODE_WS[key] = ws
+    return ws
+
+
 def aq_linear_decode(pw: PackedWeights, qx, sx, bias=None, split: int = 0, out=None, ws=None,
                      stream=None):
-    """Decode-phase linear: FP32 Y [M, N]."""
+    """Decode-phase linear: FP32 Y [M, N].  A call that cuts the input columns
+    into workgroup chunks needs a workspace whose counters are zero; without
+    `ws` the stream's cached one is used."""
     import torch
     M = qx.shape[0]
     if out is None:
         out = torch.empty((M, pw.N), dtype=torch.float32, device=qx.device)
     need = aq_workspace_bytes(pw, M, AQ_PHASE_DECODE, split)
     if ws is None and need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=qx.device)  # counters start at zero
+        ws = decode_workspace(need, qx.device, stream)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().aq_linear_decode(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias),
                                   _ptr(out), split, _ptr(ws), ws_bytes, _stream(stream)),

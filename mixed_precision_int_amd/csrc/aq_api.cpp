@@ -55,10 +55,6 @@ aq_status check_linear_io(const aq_packed *W, const int8_t *qx, const float *sx,
   return AQ_OK;
 }
 
-int effective_split(const aq::PackedView &v, int M, int split) {
-  return split > 0 ? split : aq::decode_split(v, M);
-}
-
 aq_status check_workspace(void *ws, size_t ws_bytes, size_t need) {
   if (need == 0) return AQ_OK;
   if (!ws || ws_bytes < need) return AQ_ERR_WORKSPACE;
@@ -201,8 +197,8 @@ size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split) {
   const aq::PackedView v = aq::view_of(*W);
   if (phase == AQ_PHASE_PREFILL) return aq::prefill_workspace_bytes(v, M);
   if (phase != AQ_PHASE_DECODE) return 0;
-  if (split < 0 || (split > 0 && !aq::decode_split_supported(M, split))) return 0;
-  return aq::decode_workspace_bytes(v, M, effective_split(v, M, split));
+  if (split < 0 || (split > 0 && !aq::decode_split_supported(v, M, split))) return 0;
+  return aq::decode_workspace_bytes(v, M, split);
 }
 
 aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx, int M,
@@ -213,12 +209,11 @@ aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx
   st = check_linear_io(W, qx, sx, M, bias, Y);
   if (st != AQ_OK || M == 0) return st;
   const aq::PackedView v = aq::view_of(*W);
-  if (split < 0 || (split > 0 && !aq::decode_split_supported(M, split))) return AQ_ERR_ARG;
-  const int S = effective_split(v, M, split);
-  const size_t need = aq::decode_workspace_bytes(v, M, S);
-  st = check_workspace(ws, ws_bytes, need);
+  if (split < 0 || (split > 0 && !aq::decode_split_supported(v, M, split))) return AQ_ERR_ARG;
+  if (!aq::decode_plan_ok(aq::plan_decode(v, M, split), v)) return AQ_ERR_SHAPE;
+  st = check_workspace(ws, ws_bytes, aq::decode_workspace_bytes(v, M, split));
   if (st != AQ_OK) return st;
-  return aq::launch_decode(v, qx, sx, M, bias, Y, S, ws, nullptr,
+  return aq::launch_decode(v, qx, sx, M, bias, Y, split, ws, nullptr,
                            static_cast<hipStream_t>(stream)) == hipSuccess
              ? AQ_OK
              : AQ_ERR_HIP;
@@ -253,9 +248,11 @@ aq_status aq_linear_tile_partials(const aq_packed *W, const int8_t *qx, int M, i
   if (phase == AQ_PHASE_PREFILL) {
     st = check_workspace(ws, ws_bytes, aq::prefill_workspace_bytes(v, M));
     if (st != AQ_OK) return st;
+  } else if (!aq::decode_plan_ok(aq::plan_decode(v, M, 0), v)) {
+    return AQ_ERR_SHAPE;
   }
   hipError_t e = phase == AQ_PHASE_DECODE
-                     ? aq::launch_decode(v, qx, nullptr, M, nullptr, nullptr, 1, nullptr, P,
+                     ? aq::launch_decode(v, qx, nullptr, M, nullptr, nullptr, 0, nullptr, P,
                                          static_cast<hipStream_t>(stream))
                      : run_prefill(v, qx, nullptr, M, nullptr, nullptr, P, ws,
                                    static_cast<hipStream_t>(stream));

@@ -63,10 +63,11 @@ constexpr int kLdsBudget = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kValuMaxM = 1;            // largest M on the vector-ALU path
 constexpr int kPrivMaxM = 4;            // largest M with per-wave activation slices
 constexpr int kPrivDepth = 8;           // tiles per batch with per-wave activation slices
+constexpr int kDecodeCounters = 65536;  // arrival counters at the head of a decode workspace
 enum { kValu = 0, kMfma = 1 };
 // Where the MFMA/VALU activation operands come from: a per-wave LDS slice
-// of the batch, the workgroup's LDS copy of its tokens, or global memory.
-enum { kXPriv = 0, kXShared = 1, kXGlobal = 2 };
+// of the batch, or the workgroup's LDS copy of its tokens' chunk columns.
+enum { kXPriv = 0, kXShared = 1 };
 
 struct DecodeArgs {
   const uint8_t *labels;
@@ -79,9 +80,33 @@ struct DecodeArgs {
   float *Y;
   int32_t *P;
   int N, K, R, C, T4, T8, M, label_words;
+  // input-column chunks per row block (one workgroup each), the LDS row
+  // stride of staged activations, and the workspace of chunked calls:
+  // arrival counters [row block][token chunk], then FP32 sums
+  // [row group][token chunk][chunk z][MG][64 lanes] float4
+  int Z, ychunks, xstride;
+  uint32_t *cnt;
+  float4 *part;
 };
 
 __device__ __forceinline__ v4i load16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
+
+// Device-coherent FP32x4 store / load (agent-scope relaxed atomics, one per
+// element): visible across the whole GPU without cache maintenance.
+__device__ __forceinline__ void store_coherent(float4 *p, float4 v) {
+  float *q = reinterpret_cast<float *>(p);
+  __hip_atomic_store(q + 0, v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, v.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 2, v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 3, v.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 load_coherent(const float4 *p) {
+  const float *q = reinterpret_cast<const float *>(p);
+  return make_float4(__hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                     __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                     __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                     __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
 __device__ __forceinline__ uint2 load8(const void *p) { return *reinterpret_cast<const uint2 *>(p); }
 
 // Labels of tiles tb .. tb+127 (bit k = tile tb + k) from five whole words
@@ -151,34 +176,47 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int blocks_per_row = 4 / RG;
-  const int r = blockIdx.x / blocks_per_row;
+  const int Z = a.Z, Y = a.ychunks;
+  // flat workgroup id = (row block * Y + token chunk) * Z + column chunk:
+  // the workgroups that read the same weights are dispatched together
+  const int zc = blockIdx.x % Z;        // input-column chunk of this workgroup
+  const int yc = (blockIdx.x / Z) % Y;  // token chunk
+  const int bx = blockIdx.x / (Z * Y);  // row block
+  const int r = bx / blocks_per_row;
   const int rgl = wave % RG;  // row group inside the block
-  const int rg = (blockIdx.x % blocks_per_row) * RG + rgl;
-  const int sp = wave / RG;   // split of this wave
+  const int rg = (bx % blocks_per_row) * RG + rgl;
+  const int sp = wave / RG;   // split of this wave inside the workgroup
   const int C = a.C, K = a.K, M = a.M;
-  const int c0 = (C * sp) / S;
-  const int c1 = (C * (sp + 1)) / S;
-  const int mbase = blockIdx.y * 16 * MG;
+  // global split zc*S + sp of Z*S: tile columns floor(C*s/(Z*S)) ..
+  const int ST = Z * S;
+  const int ca = (int)(((long long)C * zc) / Z);  // first column of the chunk
+  const int c0 = (int)(((long long)C * (zc * S + sp)) / ST);
+  const int c1 = (int)(((long long)C * (zc * S + sp + 1)) / ST);
+  const int mbase = yc * 16 * MG;
   const int xrows = MODE == kValu ? M : min(M - mbase, 16 * MG);  // token rows of this block
   const int g = lane >> 4, i16 = lane & 15;
   const int rowoff = rg * 256 + i16 * 16;  // this lane's row inside a 1 KB panel
   const uint8_t *__restrict__ w4p = a.w4;
   const uint8_t *__restrict__ w8p = reinterpret_cast<const uint8_t *>(a.w8);
   const int T4 = a.T4, T8 = a.T8;
-  const int kg = K >> 4;                      // 16-byte granules per activation row
-  const int xmask = (kg & 15) == 0 ? 15 : 0;  // granule swizzle (stays inside the row)
-  // LDS: per-wave slices [WAVES][M][DEPTH*BK], or the block's [16*MG][K]
-  // activations (granules swizzled by row); then the split reduction buffer
-  // [WAVES][MG][64] float4.
+  // Staged activations: the chunk's columns ca*BK .. cb*BK of each token row,
+  // kg 16-byte granules, at a row stride (xstride) that is a multiple of
+  // 256 bytes, granule q of row t stored at q ^ (t & 15): the 16 token rows
+  // one MFMA operand reads fall in distinct banks.
+  const int cb = (int)(((long long)C * (zc + 1)) / Z);
+  const int kg = (cb - ca) * (BK / 16);
+  const int xst = a.xstride;
+  // LDS: per-wave slices [WAVES][M][DEPTH*BK], or the block's [16*MG] token
+  // rows; the split reduction buffer [WAVES][MG][64] float4 follows the
+  // slices and reuses the token rows once every wave is done with them.
   int8_t *xs = reinterpret_cast<int8_t *>(smem);
   int8_t *xw = xs + wave * M * XW;
-  const int xbytes = XMODE == kXPriv ? WAVES * M * XW : XMODE == kXShared ? ((16 * MG * K + 15) & ~15) : 0;
-  float4 *red = reinterpret_cast<float4 *>(smem + xbytes);
+  float4 *red = reinterpret_cast<float4 *>(smem + (XMODE == kXPriv ? WAVES * M * XW : 0));
 
   // ---- MFMA path: block activation staging loads (independent of the
   // metadata), issued first
   v4i xb[XU];
-  const int8_t *xsrc = a.qx + (size_t)mbase * K;
+  const int8_t *xsrc = a.qx + (size_t)mbase * K + (size_t)ca * BK;
   const bool xstage = XMODE == kXShared;
   const int xgran = xstage ? xrows * kg : 0;
   if (xstage) {
@@ -186,7 +224,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
     for (int u = 0; u < XU; ++u) {
       if (u * NT < xgran) {  // uniform: only the passes the block needs
         const int q = min(tid + u * NT, xgran - 1);
-        xb[u] = load16(xsrc + (size_t)q * 16);
+        const int row = q / kg, cg = q - row * kg;
+        xb[u] = load16(xsrc + (size_t)row * K + 16 * cg);
       }
     }
   }
@@ -285,19 +324,23 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
       const int q = tid + u * NT;
       if (u * NT < xgran && q < xgran) {
         const int row = q / kg, cg = q - row * kg;
-        *reinterpret_cast<v4i *>(xs + row * K + 16 * (cg ^ (row & xmask))) = xb[u];
+        *reinterpret_cast<v4i *>(xs + row * xst + 16 * (cg ^ (row & 15))) = xb[u];
       }
     }
     for (int q0 = XU * NT; q0 < xgran; q0 += XU * NT) {  // large blocks only
       v4i xt[XU];
 #pragma unroll
-      for (int u = 0; u < XU; ++u) xt[u] = load16(xsrc + (size_t)min(q0 + tid + u * NT, xgran - 1) * 16);
+      for (int u = 0; u < XU; ++u) {
+        const int q = min(q0 + tid + u * NT, xgran - 1);
+        const int row = q / kg, cg = q - row * kg;
+        xt[u] = load16(xsrc + (size_t)row * K + 16 * cg);
+      }
 #pragma unroll
       for (int u = 0; u < XU; ++u) {
         const int q = q0 + tid + u * NT;
         if (q < xgran) {
           const int row = q / kg, cg = q - row * kg;
-          *reinterpret_cast<v4i *>(xs + row * K + 16 * (cg ^ (row & xmask))) = xt[u];
+          *reinterpret_cast<v4i *>(xs + row * xst + 16 * (cg ^ (row & 15))) = xt[u];
         }
       }
     }
@@ -344,10 +387,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
           // token row of this lane; padding tokens read the last real row,
           // their outputs are never stored
           const int trow = min(mg * 16 + i16, xrows - 1);
-          const int8_t *xr = XMODE == kXPriv ? xw + trow * XW
-                           : XMODE == kXShared ? xs + trow * K : xsrc + (size_t)trow * K;
-          const int xcol = XMODE == kXPriv ? d * BK : jt * BK;
-          const int sw = XMODE == kXShared ? (trow & xmask) : 0;
+          const int8_t *xr = XMODE == kXPriv ? xw + trow * XW : xs + trow * xst;
+          const int xcol = XMODE == kXPriv ? d * BK : (jt - ca) * BK;
+          const int sw = XMODE == kXShared ? (trow & 15) : 0;
           v4i acc = {0, 0, 0, 0};
 #pragma unroll
           for (int u = 0; u < KS; ++u) {
@@ -405,20 +447,62 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
     if (MODE == kValu) F[0].x = sum_kgroups(F[0].x);  // sum the four k-groups of each row
     // ordered split reduction through LDS
     if (S > 1) {
+      if (XMODE == kXShared) __syncthreads();  // every wave is done with the token rows
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg) red[(wave * MG + mg) * 64 + lane] = F[mg];
       __syncthreads();
-      if (sp != 0) return;
+      if (sp == 0) {
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) {
+          float4 v = red[(rgl * MG + mg) * 64 + lane];
+#pragma unroll 4
+          for (int ss = 1; ss < S; ++ss) {
+            const float4 p = red[((ss * RG + rgl) * MG + mg) * 64 + lane];
+            v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+          }
+          F[mg] = v;
+        }
+      }
+    }
+    if (Z > 1) {
+      // Chunked K: the workgroup's sum goes to slot zc of its row group; the
+      // workgroup that completes the row block's set of Z (arrival counter,
+      // reset by that workgroup) adds the slots in increasing zc, which
+      // continues the increasing split order across workgroups.
+      //   The slots are written and read with device-coherent accesses only
+      // (agent-scope atomic stores and loads), so the hand-over needs no
+      // cache-wide write-back or invalidation: each writing wave waits until
+      // its stores have completed before the barrier that precedes the
+      // counter increment, and the last workgroup reads the slots only after
+      // its increment has returned.
+      float4 *pp = a.part + ((size_t)(r * 4 + rg) * Y + yc) * Z * MG * 64 + lane;
+      if (sp == 0) {
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) store_coherent(pp + ((size_t)zc * MG + mg) * 64, F[mg]);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();
+      uint32_t *flag = reinterpret_cast<uint32_t *>(smem);  // LDS is free again
+      if (tid == 0) {
+        uint32_t *cp = a.cnt + (size_t)bx * Y + yc;
+        const uint32_t prev = __hip_atomic_fetch_add(cp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t last = prev == (uint32_t)(Z - 1) ? 1u : 0u;
+        if (last) __hip_atomic_store(cp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+      }
+      __syncthreads();
+      if (*flag == 0u || sp != 0) return;
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg) {
-        float4 v = red[(rgl * MG + mg) * 64 + lane];
-#pragma unroll 4
-        for (int ss = 1; ss < S; ++ss) {
-          const float4 p = red[((ss * RG + rgl) * MG + mg) * 64 + lane];
+        float4 v = load_coherent(pp + mg * 64);
+        for (int z = 1; z < Z; ++z) {
+          const float4 p = load_coherent(pp + ((size_t)z * MG + mg) * 64);
           v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
         }
         F[mg] = v;
       }
+    } else if (sp != 0) {
+      return;
     }
     const size_t n = (size_t)r * 64 + rg * 16 + i16;
     const float b = a.bias ? a.bias[n] : 0.0f;
@@ -450,81 +534,171 @@ void launch_one(Kern kern, dim3 grid, dim3 block, size_t lds, hipStream_t stream
   hipLaunchKernelGGL(kern, grid, block, lds, stream, args);
 }
 
+// Grid: row blocks (4R/RG) x token chunks (args.ychunks) x column chunks
+// (Z), flattened with the column chunks fastest.
 template <int BK, int MODE, int MG, int WAVES, int DEPTH, int XMODE, bool PARTIALS>
-void launch_rg(int RG, int R, int mchunks, size_t lds, hipStream_t stream, const DecodeArgs &args) {
+void launch_rg(const DecodePlan &p, int R, hipStream_t stream, const DecodeArgs &args) {
   const dim3 block(WAVES * 64);
-  switch (RG) {
-    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS>, dim3(R, mchunks), block, lds, stream, args); break;
-    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS>, dim3(R * 2, mchunks), block, lds, stream, args); break;
-    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS>, dim3(R * 4, mchunks), block, lds, stream, args); break;
+  const int zy = p.Z * args.ychunks;
+  switch (p.RG) {
+    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS>, dim3(R * zy), block, p.lds, stream, args); break;
+    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS>, dim3(R * 2 * zy), block, p.lds, stream, args); break;
+    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS>, dim3(R * 4 * zy), block, p.lds, stream, args); break;
   }
 }
 
 template <int BK, bool PARTIALS>
-void launch_mode(int mode, int xmode, int MG, int RG, int R, int mchunks, size_t lds, hipStream_t stream,
-                 const DecodeArgs &args) {
-  if (mode == kValu) {
-    launch_rg<BK, kValu, 1, 16, kPrivDepth, kXPriv, PARTIALS>(RG, R, 1, lds, stream, args);
+void launch_mode(const DecodePlan &p, int R, hipStream_t stream, const DecodeArgs &args) {
+  if (p.mode == kValu) {
+    launch_rg<BK, kValu, 1, 16, kPrivDepth, kXPriv, PARTIALS>(p, R, stream, args);
     return;
   }
-  if (xmode == kXPriv) {
-    launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS>(RG, R, 1, lds, stream, args);
+  if (p.xmode == kXPriv) {
+    launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS>(p, R, stream, args);
     return;
   }
-  if (xmode == kXShared) {
-    switch (MG) {
-      case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
-      case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
-      case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
-      default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
-    }
-    return;
-  }
-  switch (MG) {
-    case 1: launch_rg<BK, kMfma, 1, 16, 8, kXGlobal, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
-    case 2: launch_rg<BK, kMfma, 2, 16, 6, kXGlobal, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
-    case 3: launch_rg<BK, kMfma, 3, 8, 6, kXGlobal, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
-    default: launch_rg<BK, kMfma, 4, 8, 6, kXGlobal, PARTIALS>(RG, R, mchunks, lds, stream, args); break;
+  switch (p.MG) {
+    case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, PARTIALS>(p, R, stream, args); break;
+    case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, PARTIALS>(p, R, stream, args); break;
+    case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, PARTIALS>(p, R, stream, args); break;
+    default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, PARTIALS>(p, R, stream, args); break;
   }
 }
 
-}  // namespace
+// Packed tiles of more than 16 MB: a projection too large to stay in the
+// on-chip caches between calls.
+bool streams_from_hbm(const PackedView &w) {
+  return (long long)w.T4 * 64 * w.bK / 2 + (long long)w.T8 * 64 * w.bK > (16LL << 20);
+}
 
-int decode_mgroups(int M) { return M >= 49 ? 4 : (M + 15) / 16; }
-
-int decode_mchunks(int M) {
-  const int MG = decode_mgroups(M);
+// Token groups of 16 per workgroup, waves per workgroup, token chunks.  Up
+// to 64 tokens share one pass over the weights; on projections that stream
+// from HBM, groups of at most 32 tokens (16 waves, one token chunk after
+// another) measure faster at M = 33..128 than 48 or 64 tokens on 8 waves.
+int mgroups(const PackedView &w, int M) {
+  const int g = M >= 49 ? 4 : (M + 15) / 16;
+  return streams_from_hbm(w) && g > 2 ? 2 : g;
+}
+int waves_of(const PackedView &w, int M) { return mgroups(w, M) <= 2 ? 16 : 8; }
+int mchunks_of(const PackedView &w, int M) {
+  const int MG = mgroups(w, M);
   return (M + 16 * MG - 1) / (16 * MG);
 }
 
-int decode_waves(int M) { return decode_mgroups(M) <= 2 ? 16 : 8; }
+// LDS row stride of one token's chunk of cz tile columns.
+int chunk_stride(int cz, int bK) { return ((cz * bK + 255) / 256) * 256; }
 
-// Row groups per workgroup: the fewest that still let the whole grid
-// (4R/RG workgroups, one per CU at this occupancy) run in a single round on
-// the 256 CUs; more row groups per workgroup means fewer, longer splits.
-int decode_rowgroups(const PackedView &w, int M) {
-  (void)M;
+// Bytes of the staged token rows of a chunk of cz columns.
+size_t chunk_lds(int MG, int cz, int bK) { return (size_t)16 * MG * chunk_stride(cz, bK); }
+
+// Fewest chunks whose token rows fit in LDS.
+int chunks_to_fit(const PackedView &w, int MG) {
+  for (int z = 1; z < w.C; ++z)
+    if (chunk_lds(MG, (w.C + z - 1) / z, w.bK) <= (size_t)kLdsBudget) return z;
+  return w.C;
+}
+
+// Row groups per workgroup without chunking: the fewest that still let the
+// whole grid (4R/RG workgroups, one per CU at this occupancy) run in a single
+// round on the 256 CUs; more row groups per workgroup means fewer, longer
+// splits.
+int rowgroups_unchunked(const PackedView &w) {
   const int cus = 256;
   if (4 * w.R <= cus) return 1;
   if (2 * w.R <= cus) return 2;
   return 4;
 }
 
-int decode_split(const PackedView &w, int M) {
-  return decode_waves(M) / decode_rowgroups(w, M);
+// Adaptive row groups and chunks for the shared-activation MFMA path.
+// When the tokens' activations over all K fit in LDS the call is not
+// chunked (the row-group rule above).  Otherwise the workgroup takes a whole
+// 64-row tile row (RG = 4: every staged activation byte feeds 64 weight rows)
+// and the columns are cut into the fewest chunks that fit.  Measured on the
+// 3B-14B projection shapes at M = 8..64: more chunks (to occupy more CUs)
+// lose, since every chunked workgroup adds a serial stage-load-store-count
+// chain, and fewer row groups per workgroup lose to the extra activation
+// staging.
+void choose_chunks(const PackedView &w, int M, int MG, int *RG, int *Z) {
+  (void)M;
+  const int zfit = chunks_to_fit(w, MG);
+  if (zfit == 1) {
+    *RG = rowgroups_unchunked(w);
+    *Z = 1;
+  } else {
+    *RG = 4;
+    *Z = zfit;
+  }
 }
 
-bool decode_split_supported(int M, int S) {
-  const int W = decode_waves(M);
+}  // namespace
+
+DecodePlan plan_decode(const PackedView &w, int M, int split) {
+  DecodePlan p;
+  p.MG = mgroups(w, M);
+  p.waves = waves_of(w, M);
+  p.mchunks = mchunks_of(w, M);
+  p.mode = M <= kValuMaxM ? kValu : kMfma;
+  p.Z = 1;
+  p.ylaunch = p.mchunks;
+  p.xstride = 0;
+  p.ws_bytes = 0;
+  p.cnt_bytes = 0;
+  const size_t red = (size_t)p.waves * p.MG * 64 * sizeof(float4);
+  // Products: vector ALU for one token, MFMA otherwise.  Activations: a
+  // per-wave LDS slice of each batch for M <= 4 (no workgroup barrier),
+  // else the block's 16*MG token rows over its chunk of columns.
+  if (M <= kPrivMaxM) {
+    p.xmode = kXPriv;
+    p.RG = split > 0 ? p.waves / split : rowgroups_unchunked(w);
+    p.lds = (size_t)p.waves * M * kPrivDepth * w.bK + red;
+    p.mchunks = 1;
+  } else {
+    p.xmode = kXShared;
+    if (split > 0) {
+      p.RG = p.waves / split;
+      p.Z = chunks_to_fit(w, p.MG);
+    } else {
+      choose_chunks(w, M, p.MG, &p.RG, &p.Z);
+    }
+    const int cz = (w.C + p.Z - 1) / p.Z;
+    p.xstride = chunk_stride(cz, w.bK);
+    const size_t xb = chunk_lds(p.MG, cz, w.bK);
+    p.lds = xb > red ? xb : red;  // the reduction buffer reuses the token rows
+    if (p.Z > 1) {
+      // counters at a fixed place and size, so that calls of any layout can
+      // share one workspace; more token chunks than counters allow take
+      // several launches along the token axis
+      const int blocks = w.R * 4 / p.RG;
+      p.ylaunch = p.mchunks < kDecodeCounters / blocks ? p.mchunks : kDecodeCounters / blocks;
+      p.cnt_bytes = (size_t)kDecodeCounters * 4;
+      p.ws_bytes = p.cnt_bytes + (size_t)w.R * 4 * p.ylaunch * p.Z * p.MG * 64 * sizeof(float4);
+    }
+  }
+  p.S = p.waves / p.RG;
+  if (p.mode == kValu || p.xmode == kXPriv) p.ylaunch = 1;
+  return p;
+}
+
+bool decode_plan_ok(const DecodePlan &p, const PackedView &w) {
+  return p.Z == 1 || w.R * 4 / p.RG <= kDecodeCounters;
+}
+
+int decode_split(const PackedView &w, int M) { return plan_decode(w, M, 0).S; }
+
+bool decode_split_supported(const PackedView &w, int M, int S) {
+  const int W = waves_of(w, M);
   return S == W || S == W / 2 || S == W / 4;
 }
 
-size_t decode_workspace_bytes(const PackedView &, int, int) { return 0; }
+size_t decode_workspace_bytes(const PackedView &w, int M, int split) {
+  return plan_decode(w, M, split).ws_bytes;
+}
 
 hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx, int M,
-                         const float *bias, float *Y, int S, void *ws, int32_t *P,
+                         const float *bias, float *Y, int split, void *ws, int32_t *P,
                          hipStream_t stream) {
-  (void)ws;
+  const DecodePlan p = plan_decode(w, M, split);
+  if (!decode_plan_ok(p, w) || p.ylaunch < 1) return hipErrorInvalidValue;
   DecodeArgs args;
   args.labels = w.labels; args.off4 = w.off4; args.off8 = w.off8;
   args.w4 = w.w4; args.w8 = w.w8; args.s4 = w.s4; args.s8 = w.s8;
@@ -532,36 +706,35 @@ hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx,
   args.Y = Y; args.P = P;
   args.N = w.N; args.K = w.K; args.R = w.R; args.C = w.C; args.T4 = w.T4; args.T8 = w.T8;
   args.M = M; args.label_words = (w.R * w.C + 31) / 32;
-  const int MG = decode_mgroups(M);
-  const int waves = decode_waves(M);
-  // split S (waves per row group) selects the row groups per workgroup
-  int RG = S > 0 ? waves / S : decode_rowgroups(w, M);
-  if (RG != 1 && RG != 2 && RG != 4) RG = decode_rowgroups(w, M);
-  const int mchunks = decode_mchunks(M);
-  // Products: vector ALU for one token, MFMA otherwise.  Activations: a
-  // per-wave LDS slice of each batch for M <= 4 (no workgroup barrier),
-  // else the block's [16*MG][K] tokens in LDS when they fit, else global.
-  const size_t red = (size_t)waves * MG * 64 * sizeof(float4);
-  const int mode = M <= kValuMaxM ? kValu : kMfma;
-  int xmode;
-  size_t xbytes;
-  if (M <= kPrivMaxM) {
-    xmode = kXPriv;
-    xbytes = (size_t)waves * M * kPrivDepth * w.bK;
-  } else {
-    xbytes = ((size_t)16 * MG * w.K + 15) & ~(size_t)15;
-    xmode = xbytes + red <= (size_t)kLdsBudget ? kXShared : kXGlobal;
-    if (xmode == kXGlobal) xbytes = 0;
+  args.Z = p.Z;
+  args.xstride = p.xstride;
+  args.cnt = nullptr;
+  args.part = nullptr;
+  if (p.Z > 1 && !P) {  // the products need no chunk sums
+    args.cnt = static_cast<uint32_t *>(ws);
+    args.part = reinterpret_cast<float4 *>(static_cast<uint8_t *>(ws) + p.cnt_bytes);
   }
-  const size_t lds = xbytes + red;
-  if (w.bK == 128) {
-    if (P) launch_mode<128, true>(mode, xmode, MG, RG, w.R, mchunks, lds, stream, args);
-    else launch_mode<128, false>(mode, xmode, MG, RG, w.R, mchunks, lds, stream, args);
-  } else {
-    if (P) launch_mode<64, true>(mode, xmode, MG, RG, w.R, mchunks, lds, stream, args);
-    else launch_mode<64, false>(mode, xmode, MG, RG, w.R, mchunks, lds, stream, args);
+  // token ranges of ylaunch chunks of 16*MG tokens, one launch each
+  const int mstep = p.ylaunch * 16 * p.MG;
+  for (int m0 = 0; m0 < M; m0 += mstep) {
+    DecodeArgs la = args;
+    la.M = M - m0 < mstep ? M - m0 : mstep;
+    la.qx = qx + (size_t)m0 * w.K;
+    if (sx) la.sx = sx + m0;
+    if (Y) la.Y = Y + (size_t)m0 * w.N;
+    if (P) la.P = P + (size_t)m0 * w.N * w.C;
+    la.ychunks = p.mode == kValu || p.xmode == kXPriv ? 1 : (la.M + 16 * p.MG - 1) / (16 * p.MG);
+    if (w.bK == 128) {
+      if (P) launch_mode<128, true>(p, w.R, stream, la);
+      else launch_mode<128, false>(p, w.R, stream, la);
+    } else {
+      if (P) launch_mode<64, true>(p, w.R, stream, la);
+      else launch_mode<64, false>(p, w.R, stream, la);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace aq

@@ -38,11 +38,14 @@ inline PackedView view_of(const aq_packed &p) {
 hipError_t launch_pack(const float *W, const aq_packed &out, hipStream_t stream);
 hipError_t launch_quant_act(const float *X, int M, int K, int8_t *qx, float *sx,
                             hipStream_t stream);
-// Decode: one launch; S input-column groups per output row group are
-// reduced through LDS in increasing order.  P != nullptr selects the debug
-// mode that writes INT32 tile products instead (Y unused).
+// Decode: one launch; the input-column splits of each output row group are
+// reduced in increasing order, through LDS inside a workgroup and, when the
+// plan cuts the columns into Z > 1 workgroup chunks, through the workspace
+// (ws, decode_workspace_bytes bytes, counters zero on entry and on exit).
+// split 0 = adaptive.  P != nullptr selects the debug mode that writes
+// INT32 tile products instead (Y and ws unused).
 hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx, int M,
-                         const float *bias, float *Y, int S, void *ws, int32_t *P,
+                         const float *bias, float *Y, int split, void *ws, int32_t *P,
                          hipStream_t stream);
 hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx, int M,
                           const float *bias, float *Y, int32_t *P, hipStream_t stream);
@@ -83,10 +86,25 @@ inline size_t prefill_workspace_bytes(const PackedView &w, int M) {
   return prefill_long(w, M) && w.T4 > 0 ? expand_bytes(w) : 0;
 }
 
-// Adaptive decode split (host heuristic), the split values the kernel
-// supports for M tokens, and the workspace a split needs (none).
+// Launch plan of one decode call: products on the vector ALU or MFMA, where
+// the activation operands live, token groups of 16 per workgroup, waves,
+// row groups RG and splits S = waves / RG per workgroup, input-column
+// chunks Z (one workgroup each), token chunks, dynamic LDS bytes, the LDS
+// row stride of staged activations, and the workspace (arrival counters,
+// then FP32 chunk sums) that Z > 1 needs.
+// A chunked call's workspace starts with a fixed 256 KiB of arrival
+// counters (one per row block and token chunk of a launch); token chunks
+// beyond that take further launches of ylaunch chunks each.
+struct DecodePlan {
+  int mode, xmode, MG, waves, RG, S, Z, mchunks, ylaunch, xstride;
+  size_t lds, cnt_bytes, ws_bytes;
+};
+// split = 0: adaptive; otherwise S, one of the supported values.
+DecodePlan plan_decode(const PackedView &w, int M, int split);
+// false when a chunked plan has more row blocks than arrival counters
+bool decode_plan_ok(const DecodePlan &p, const PackedView &w);
 int decode_split(const PackedView &w, int M);
-bool decode_split_supported(int M, int S);
-size_t decode_workspace_bytes(const PackedView &w, int M, int S);
+bool decode_split_supported(const PackedView &w, int M, int S);
+size_t decode_workspace_bytes(const PackedView &w, int M, int split);
 
 }  // namespace aq

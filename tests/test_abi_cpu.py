@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(aqlib):
 
 
 def test_abi_version_and_status_strings(aqlib):
-    assert B.aq_abi_version() == 2
+    assert B.aq_abi_version() == 3
     for code in list(B.STATUS) + [-99]:
         assert aqlib.aq_status_string(code)
 
@@ -129,6 +129,30 @@ def test_long_prefill_workspace(aqlib):
     # beyond 32-bit operand offsets the long route is not taken
     d = fake_packed(N=64, K=1 << 20, bK=128, T4=(1 << 13) - 1, T8=1)
     assert ws(ctypes.byref(d), 4096, 1, 0) == 0
+
+
+def test_decode_chunk_workspace(aqlib):
+    """Decode cuts the input columns into workgroup chunks when the tokens'
+    activations for all K would not fit on chip; such a call needs a
+    workspace (arrival counters, then FP32 chunk sums) and is rejected on the
+    host without one."""
+    ws = B.lib().aq_workspace_bytes
+    big = fake_packed(N=256, K=65536, T4=4 * 512 - 3, T8=3)
+    for M in (5, 16, 33, 64, 100):
+        need = ws(ctypes.byref(big), M, 0, 0)
+        # the counters sit in a fixed 256 KiB head, then the FP32 chunk sums
+        assert need > 256 * 1024 and need % 16 == 0, (M, need)
+        assert decode(big, M=M, split=0) == -6
+        assert decode(big, M=M, split=0, ws=FAKE, ws_bytes=need - 1) == -6
+        assert decode(big, M=M, split=0, ws=FAKE + 4, ws_bytes=need) == -5
+        for sp in ((16, 8, 4) if M <= 32 else (8, 4, 2)):
+            assert ws(ctypes.byref(big), M, 0, sp) > 0
+    # one token, or few tokens: per-wave activation slices, no chunks
+    for M in (1, 4):
+        assert ws(ctypes.byref(big), M, 0, 0) == 0
+    # activations fit and the grid already fills the device: no chunks
+    wide = fake_packed(N=19456, K=2560, T4=304 * 20 - 7, T8=7)
+    assert ws(ctypes.byref(wide), 16, 0, 0) == 0
 
 
 def test_quant_act_and_partials_rejected(aqlib):

@@ -43,7 +43,7 @@ def test_small_workload_with_bias():
     (512, 1536, 128, 200),
     (256, 1536, 128, 3),     # 2..4 tokens: per-wave activation slices with MFMA
     (64, 8448, 64, 2),       # 132 tile columns: labels counted from memory
-    (128, 10240, 128, 7),    # 16 tokens x K too large for LDS: global activation reads
+    (128, 10240, 128, 7),    # 16 tokens x K too large for LDS: column chunks
 ])
 def test_ragged_shapes(N, K, bK, M):
     W, z, X = _ragged(N, K, bK, M, seed=N * 7 + K + M)
@@ -189,6 +189,102 @@ def test_long_prefill_temporary_int8(N, K, bK, M, kind):
     need = aq.aq_workspace_bytes(Case(W, z, X, 64, bK).gpu_pack(), M, aq.AQ_PHASE_PREFILL)
     assert (need == 0) == (kind == "all_int8")
     Case(W, z, X, 64, bK, bias=bias, name=f"long{N}x{K}/bK{bK}/M{M}/{kind}").check_all(phases=("prefill",))
+
+
+@pytest.mark.parametrize("N,K,bK,M,kind", [
+    (256, 8192, 128, 64, "mixed"),      # 64 tokens x 8192 columns: several chunks
+    (192, 5120, 128, 37, "mixed"),      # ragged tokens: 3 groups of 16, last partial
+    (320, 17408, 128, 33, "mixed"),     # 136 tile columns: labels counted from memory
+    (128, 8192, 64, 20, "mixed"),       # 64 x 64 tiles
+    (128, 4096, 128, 100, "mixed"),     # two 64-token chunks along the grid's y
+    (256, 6144, 128, 48, "all_int4"),
+    (256, 6144, 128, 48, "all_int8"),
+])
+def test_decode_chunked_columns(N, K, bK, M, kind):
+    """Decode with the input columns cut into workgroup chunks (staged
+    activations of all K would not fit on chip, or the grid would leave CUs
+    idle): FP32 chunk sums through the workspace, added in increasing chunk
+    order by the row block's last workgroup.  Tile products, outputs for the
+    adaptive and every explicit split, and bitwise-repeatable outputs (the
+    arrival counters are left at zero by every call)."""
+    rng = np.random.default_rng(N + 3 * K + M)
+    W = gen.weights(rng, N, K)
+    R, C = N // 64, K // bK
+    z = {"mixed": gen.map_uniform(rng, R, C, 0.3), "all_int4": np.full((R, C), 4),
+         "all_int8": np.full((R, C), 8)}[kind]
+    X = gen.acts_outliers(rng, M, K, 5, 25.0)
+    bias = rng.standard_normal(N).astype(np.float32)
+    c = Case(W, z, X, 64, bK, bias=bias, name=f"chunked{N}x{K}/bK{bK}/M{M}/{kind}")
+    Wv = 16 if M <= 32 else 8
+    out = c.check_all(phases=("decode",), splits=(0, Wv, Wv // 2, Wv // 4))
+    assert aq.aq_workspace_bytes(c.pw, M, aq.AQ_PHASE_DECODE) > 0
+    bias_d = to_dev(bias)
+    for s in (0, Wv // 4):
+        again = aq.aq_linear_decode(c.pw, c.qx_d, c.sx_d, bias_d, split=s)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int32), out[f"decode{s}"].view(torch.int32)), s
+
+
+def test_decode_chunked_interleaved_calls():
+    """Back-to-back decode calls on one stream and one workspace, cycling
+    through projections whose chunk layouts differ (chunk counts, row
+    blocks, token groups): every output of every call matches the oracle.
+    A chunk sum read before its writer's store is visible device-wide, or an
+    arrival counter not left at zero, returns another call's data."""
+    shapes = [(6144, 4096, 64), (4096, 14336, 64), (2048, 8192, 40), (1024, 17408, 33)]
+    cases = []
+    for i, (N, K, M) in enumerate(shapes):
+        rng = np.random.default_rng(900 + i)
+        W = gen.weights(rng, N, K)
+        z = gen.map_uniform(rng, N // 64, K // 128, 0.3)
+        X = gen.acts_outliers(rng, M, K, 4, 20.0)
+        c = Case(W, z, X, name=f"interleaved{N}x{K}/M{M}")
+        ref = c.ref(np.arange(M))
+        c.gpu_pack()
+        c.gpu_quant()
+        assert aq.aq_workspace_bytes(c.pw, M, aq.AQ_PHASE_DECODE) > 0, c.name
+        cases.append((c, ref))
+    outs = []
+    for rep in range(12):
+        for c, _ in cases:
+            outs.append((c, aq.aq_linear_decode(c.pw, c.qx_d, c.sx_d)))
+    torch.cuda.synchronize()
+    from tests.parity import assert_output_close
+    refs = {id(c): r for c, r in cases}
+    for k, (c, Y) in enumerate(outs):
+        r = refs[id(c)]
+        assert_output_close(Y.cpu().numpy(), r["y_rows"], r["c_rows"], f"{c.name}/call{k}")
+
+
+def test_decode_chunked_many_token_chunks():
+    """More row blocks x token chunks than a decode workspace has arrival
+    counters (65536): the call runs as several launches along the token
+    axis.  N = 65536 (1024 row blocks), K = 4096, M = 4160 tokens (65 chunks
+    of 64); outputs on three tile rows x six tokens that span both launches
+    against the oracle."""
+    N, K, M = 65536, 4096, 4160
+    R, C = N // 64, K // 128
+    rng = np.random.default_rng(4242)
+    zmap = gen.map_uniform(rng, R, C, 0.3)
+    W = gen.device_weights(N, K, 4243)
+    pw = aq.aq_pack_weights(W, aq.aq_labels_from_map(zmap.astype(np.uint8)), 64, 128)
+    X = gen.device_acts_outliers(M, K, 4244)
+    qx, sx = aq.aq_quant_act(X)
+    Y = aq.aq_linear_decode(pw, qx, sx)
+    torch.cuda.synchronize()
+    tile_rows = np.array([0, 333, R - 1])
+    cols = np.concatenate([np.arange(64 * r, 64 * r + 64) for r in tile_rows])
+    tokens = np.array([0, 63, 64, 4095, 4096, M - 1])
+    W_sub = W[torch.from_numpy(cols).cuda()].cpu().numpy()
+    X_rows = X[torch.from_numpy(tokens).cuda()].cpu().numpy()
+    Y_g = Y[torch.from_numpy(tokens).cuda()][:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    del W, Y
+    codes, sW = O.quant_weights(W_sub, zmap[tile_rows], 64, 128)
+    qx_ref, sx_ref = O.quant_act(X_rows)
+    P = O.tile_partials(qx_ref, codes, 128)
+    from tests.parity import assert_output_close
+    assert_output_close(Y_g, O.linear_from_partials(P, sx_ref, sW), O.abs_contrib(P, sx_ref, sW),
+                        "many-token-chunks")
 
 
 def test_long_prefill_persistent_tiles_ragged():
