@@ -90,8 +90,9 @@ def clone_packed(aq, pw):
     """A second device copy of a packed projection (same bytes)."""
     t = {k: getattr(pw, k).clone() for k in ("labels", "row_off4", "row_off8", "w4", "w8", "s4", "s8")}
     d = aq.AqPacked(pw.plan.N, pw.plan.K, pw.plan.bN, pw.plan.bK, pw.plan.T4, pw.plan.T8,
-                    *(t[k].data_ptr() for k in ("labels", "row_off4", "row_off8", "w4", "w8", "s4", "s8")))
-    return aq.PackedWeights(plan=pw.plan, labels_host=pw.labels_host, desc=d, **t)
+                    *(t[k].data_ptr() for k in ("labels", "row_off4", "row_off8", "w4", "w8", "s4", "s8")),
+                    pw.desc.meta_host)
+    return aq.PackedWeights(plan=pw.plan, labels_host=pw.labels_host, desc=d, meta_host=pw.meta_host, **t)
 
 
 def setup(aq, gen, torch):

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AQ_ABI_VERSION 3
+#define AQ_ABI_VERSION 4
 
 typedef enum aq_status {
   AQ_OK = 0,
@@ -83,11 +83,20 @@ typedef struct aq_plan {
   size_t offs_bytes;      /* 4*(R+1), for each of row_off4 and row_off8      */
   size_t w4_bytes, w8_bytes;  /* T4*bN*bK/2 and T8*bN*bK                     */
   size_t s4_bytes, s8_bytes;  /* 4*T4*bN and 4*T8*bN                         */
+  size_t meta_bytes;      /* 24*R when C <= 128, else 0: host metadata image */
 } aq_plan;
 
 /* A packed projection: geometry plus device buffers sized by aq_plan.
  * aq_pack_weights writes the buffers; the linear entry points only read
- * them.  w4/s4 may be NULL when T4 == 0, w8/s8 when T8 == 0. */
+ * them.  w4/s4 may be NULL when T4 == 0, w8/s8 when T8 == 0.
+ * meta_host (optional, host memory, meta_bytes, 4-byte aligned, NULL if
+ * unused): aq_pack_weights fills it with a host copy of the metadata, one
+ * record of six 32-bit words per tile row r: row_off4[r], row_off8[r], then
+ * the labels of tiles (r, 0 .. C-1) as 128 bits, LSB first (zero beyond C).
+ * While it is set and the image is at most 3584 bytes (R <= 149),
+ * aq_linear_decode passes it inside the kernel arguments, so no workgroup
+ * waits on a metadata load before its first weight loads.  It must stay
+ * valid and unchanged while decode calls are issued. */
 typedef struct aq_packed {
   int32_t N, K, bN, bK, T4, T8;
   uint8_t *labels;        /* device, labels_alloc (4-byte aligned)          */
@@ -97,6 +106,7 @@ typedef struct aq_packed {
   int8_t *w8;             /* device, w8_bytes                               */
   float *s4;              /* device, T4*bN                                  */
   float *s8;              /* device, T8*bN                                  */
+  uint32_t *meta_host;    /* host, meta_bytes, optional                     */
 } aq_packed;
 
 /* Phase selector for aq_workspace_bytes / aq_linear_tile_partials. */
@@ -133,7 +143,8 @@ aq_status aq_plan_pack(int N, int K, int bN, int bK, const uint8_t *labels_host,
  *               aq_plan_pack.  labels (zero-padded to labels_alloc) and row
  *               offsets are copied in from the host; this call synchronizes
  *               `stream` once after those copies, so the host copy may be
- *               reused when it returns.
+ *               reused when it returns.  out->meta_host, when set, receives
+ *               the host metadata image (see aq_packed).
  */
 aq_status aq_pack_weights(const float *W, const uint8_t *labels_host, aq_packed *out, void *stream);
 

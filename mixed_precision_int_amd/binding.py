@@ -42,7 +42,8 @@ class AqPlan(ctypes.Structure):
                 ("labels_bytes", ctypes.c_size_t), ("labels_alloc", ctypes.c_size_t),
                 ("offs_bytes", ctypes.c_size_t),
                 ("w4_bytes", ctypes.c_size_t), ("w8_bytes", ctypes.c_size_t),
-                ("s4_bytes", ctypes.c_size_t), ("s8_bytes", ctypes.c_size_t)]
+                ("s4_bytes", ctypes.c_size_t), ("s8_bytes", ctypes.c_size_t),
+                ("meta_bytes", ctypes.c_size_t)]
 
 
 class AqPacked(ctypes.Structure):
@@ -50,7 +51,7 @@ class AqPacked(ctypes.Structure):
                 ("bK", ctypes.c_int32), ("T4", ctypes.c_int32), ("T8", ctypes.c_int32),
                 ("labels", ctypes.c_void_p), ("row_off4", ctypes.c_void_p),
                 ("row_off8", ctypes.c_void_p), ("w4", ctypes.c_void_p), ("w8", ctypes.c_void_p),
-                ("s4", ctypes.c_void_p), ("s8", ctypes.c_void_p)]
+                ("s4", ctypes.c_void_p), ("s8", ctypes.c_void_p), ("meta_host", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -151,6 +152,7 @@ class PackedWeights:
     s4: object
     s8: object
     desc: AqPacked
+    meta_host: np.ndarray | None = None  # host metadata image (decode passes it inline)
 
     @property
     def N(self):
@@ -176,9 +178,12 @@ def aq_alloc_packed(plan: AqPlan, labels: np.ndarray, device="cuda") -> PackedWe
              row_off8=_dev_bytes(plan.offs_bytes, device), w4=_dev_bytes(plan.w4_bytes, device),
              w8=_dev_bytes(plan.w8_bytes, device), s4=_dev_bytes(plan.s4_bytes, device),
              s8=_dev_bytes(plan.s8_bytes, device))
+    meta = np.zeros(max(int(plan.meta_bytes) // 4, 1), dtype=np.uint32)  # [R][6] when C <= 128
     d = AqPacked(plan.N, plan.K, plan.bN, plan.bK, plan.T4, plan.T8,
-                 *(t[k].data_ptr() for k in ("labels", "row_off4", "row_off8", "w4", "w8", "s4", "s8")))
-    return PackedWeights(plan=plan, labels_host=np.ascontiguousarray(labels, dtype=np.uint8), desc=d, **t)
+                 *(t[k].data_ptr() for k in ("labels", "row_off4", "row_off8", "w4", "w8", "s4", "s8")),
+                 meta.ctypes.data)
+    return PackedWeights(plan=plan, labels_host=np.ascontiguousarray(labels, dtype=np.uint8), desc=d,
+                         meta_host=meta, **t)
 
 
 def aq_pack_weights(W, labels: np.ndarray, bN: int = 64, bK: int = 128, stream=None) -> PackedWeights:

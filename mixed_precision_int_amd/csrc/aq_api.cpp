@@ -38,6 +38,7 @@ aq_status check_packed(const aq_packed *W) {
   if (W->T4 > 0 && (!W->w4 || !W->s4)) return AQ_ERR_NULL;
   if (W->T8 > 0 && (!W->w8 || !W->s8)) return AQ_ERR_NULL;
   if (!aligned4(W->row_off4) || !aligned4(W->row_off8)) return AQ_ERR_ALIGN;
+  if (W->meta_host && !aligned4(W->meta_host)) return AQ_ERR_ALIGN;
   if (W->T4 > 0 && (!aligned16(W->w4) || !aligned16(W->s4))) return AQ_ERR_ALIGN;
   if (W->T8 > 0 && (!aligned16(W->w8) || !aligned16(W->s8))) return AQ_ERR_ALIGN;
   return AQ_OK;
@@ -130,6 +131,7 @@ aq_status aq_plan_pack(int N, int K, int bN, int bK, const uint8_t *labels, aq_p
   p.w8_bytes = B * (size_t)p.T8;
   p.s4_bytes = 4 * (size_t)bN * p.T4;
   p.s8_bytes = 4 * (size_t)bN * p.T8;
+  p.meta_bytes = C <= 128 ? 24 * (size_t)R : 0;
   *out = p;
   return AQ_OK;
 }
@@ -165,6 +167,19 @@ aq_status aq_pack_weights(const float *W, const uint8_t *labels_host, aq_packed 
     for (int j = 0; j < plan.C; ++j) c4 += bit_of(labels_host, r * plan.C + j);
     o4[r + 1] = o4[r] + c4;
     o8[r + 1] = o8[r] + (plan.C - c4);
+  }
+  if (out->meta_host && plan.meta_bytes) {
+    // host image, one 6-word record per tile row: row_off4[r], row_off8[r],
+    // then the labels of the row's C <= 128 tiles as 128 bits, LSB first
+    uint32_t *m = out->meta_host;
+    for (int r = 0; r < plan.R; ++r) {
+      uint32_t *rec = m + 6 * (size_t)r;
+      rec[0] = (uint32_t)o4[r];
+      rec[1] = (uint32_t)o8[r];
+      rec[2] = rec[3] = rec[4] = rec[5] = 0u;
+      for (int j = 0; j < plan.C; ++j)
+        rec[2 + (j >> 5)] |= (uint32_t)bit_of(labels_host, r * plan.C + j) << (j & 31);
+    }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipMemcpyAsync(out->labels, lab.data(), plan.labels_alloc, hipMemcpyHostToDevice, s) !=

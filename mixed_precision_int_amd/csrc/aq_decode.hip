@@ -53,6 +53,8 @@
 // accumulators (eq. 19).  INT4 tiles are widened x16 (see w4_lo16), so their
 // scale is multiplied by the exact factor 1/16.
 
+#include <cstring>
+
 #include "aq_device.h"
 #include "aq_internal.h"
 
@@ -64,6 +66,8 @@ constexpr int kValuMaxM = 1;            // largest M on the vector-ALU path
 constexpr int kPrivMaxM = 4;            // largest M with per-wave activation slices
 constexpr int kPrivDepth = 8;           // tiles per batch with per-wave activation slices
 constexpr int kDecodeCounters = 65536;  // arrival counters at the head of a decode workspace
+constexpr int kInlineWords = 896;       // metadata words that may travel in the kernel arguments
+constexpr int kMetaStride = 6;          // words per tile row in the host metadata image
 enum { kValu = 0, kMfma = 1 };
 // Where the MFMA/VALU activation operands come from: a per-wave LDS slice
 // of the batch, or the workgroup's LDS copy of its tokens' chunk columns.
@@ -88,6 +92,14 @@ struct DecodeArgs {
   uint32_t *cnt;
   float4 *part;
 };
+
+// With INL each tile row's record of the host metadata image (row_off4[r],
+// row_off8[r], then the labels of the row's tiles as 128 bits, LSB first)
+// travels inside the kernel arguments.  The record's place depends only on
+// the workgroup id, so it is fetched with the other arguments and the first
+// weight loads wait for no metadata load of their own.
+template <bool INL> struct DArgs : DecodeArgs {};
+template <> struct DArgs<true> : DecodeArgs { uint32_t meta[kInlineWords]; };
 
 __device__ __forceinline__ v4i load16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
 
@@ -163,8 +175,8 @@ __device__ __forceinline__ v4i x_operand(const int8_t *row, int colbase, int g, 
   return load16(row + 16 * ((c >> 4) ^ sw));
 }
 
-template <int BK, int MODE, int MG, int WAVES, int RG, int DEPTH, int XMODE, bool PARTIALS>
-__global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) {
+template <int BK, int MODE, int MG, int WAVES, int RG, int DEPTH, int XMODE, bool PARTIALS, bool INL>
+__global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) {
   constexpr int KS = BK / 64;    // MFMA steps (16-byte operands per lane) per tile
   constexpr int S = WAVES / RG;  // splits per row group
   constexpr int NT = WAVES * 64;
@@ -176,22 +188,40 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int blocks_per_row = 4 / RG;
-  const int Z = a.Z, Y = a.ychunks;
-  // flat workgroup id = (row block * Y + token chunk) * Z + column chunk:
-  // the workgroups that read the same weights are dispatched together
-  const int zc = blockIdx.x % Z;        // input-column chunk of this workgroup
-  const int yc = (blockIdx.x / Z) % Y;  // token chunk
-  const int bx = blockIdx.x / (Z * Y);  // row block
+  const int Z = a.Z;
+  const int zc = blockIdx.z;  // input-column chunk of this workgroup
+  const int yc = blockIdx.y;  // token chunk
+  const int bx = blockIdx.x;  // row block
   const int r = bx / blocks_per_row;
   const int rgl = wave % RG;  // row group inside the block
   const int rg = (bx % blocks_per_row) * RG + rgl;
   const int sp = wave / RG;   // split of this wave inside the workgroup
+  // the row's metadata record when it travels in the kernel arguments; its
+  // place depends on the workgroup id alone, so these loads go out with the
+  // first argument loads
+  uint32_t rec[kMetaStride];
+  if constexpr (INL) {
+#pragma unroll
+    for (int k = 0; k < kMetaStride; ++k) rec[k] = a.meta[kMetaStride * r + k];
+    // everything the first weight loads need, fetched in that same batch
+    // (the compiler would otherwise load these after the first wait)
+    asm volatile("" ::"s"(a.w4), "s"(a.w8), "s"(a.s4), "s"(a.s8), "s"(a.qx), "s"(a.T4), "s"(a.T8),
+                 "s"(a.C), "s"(a.K), "s"(a.M), "s"(a.Z));
+  }
   const int C = a.C, K = a.K, M = a.M;
-  // global split zc*S + sp of Z*S: tile columns floor(C*s/(Z*S)) ..
-  const int ST = Z * S;
-  const int ca = (int)(((long long)C * zc) / Z);  // first column of the chunk
-  const int c0 = (int)(((long long)C * (zc * S + sp)) / ST);
-  const int c1 = (int)(((long long)C * (zc * S + sp + 1)) / ST);
+  // global split zc*S + sp of Z*S: tile columns floor(C*s/(Z*S)) .. (the
+  // planner keeps C*Z*S below 2^31; one chunk: S is a compile-time divisor)
+  int ca, c0, c1;
+  if (Z == 1) {
+    ca = 0;
+    c0 = (C * sp) / S;
+    c1 = (C * (sp + 1)) / S;
+  } else {
+    const unsigned ST = (unsigned)(Z * S);
+    ca = (int)((unsigned)(C * zc) / (unsigned)Z);  // first column of the chunk
+    c0 = (int)((unsigned)(C * (zc * S + sp)) / ST);
+    c1 = (int)((unsigned)(C * (zc * S + sp + 1)) / ST);
+  }
   const int mbase = yc * 16 * MG;
   const int xrows = MODE == kValu ? M : min(M - mbase, 16 * MG);  // token rows of this block
   const int g = lane >> 4, i16 = lane & 15;
@@ -203,7 +233,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
   // kg 16-byte granules, at a row stride (xstride) that is a multiple of
   // 256 bytes, granule q of row t stored at q ^ (t & 15): the 16 token rows
   // one MFMA operand reads fall in distinct banks.
-  const int cb = (int)(((long long)C * (zc + 1)) / Z);
+  const int cb = Z == 1 ? C : (int)((unsigned)(C * (zc + 1)) / (unsigned)Z);
   const int kg = (cb - ca) * (BK / 16);
   const int xst = a.xstride;
   // LDS: per-wave slices [WAVES][M][DEPTH*BK], or the block's [16*MG] token
@@ -235,18 +265,26 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
   // guard that valid metadata never trips), so the compiler cannot defer the
   // offset loads to their later use: all seven share one wait.
   const int tb = r * C;
-  const bool fastlab = C <= 128;
-  const int o4 = a.off4[r], o8 = a.off8[r];
-  uint32_t lw[5];
-  {
-    const uint32_t *wd = reinterpret_cast<const uint32_t *>(a.labels);
+  const bool fastlab = INL || C <= 128;  // the inline record holds the whole row
+  int o4, o8;
+  uint64_t wlo, whi;
+  if constexpr (INL) {
+    // the row's record (loaded above): offsets, then its labels
+    o4 = (int)rec[0];
+    o8 = (int)rec[1];
+    wlo = (uint64_t)rec[2] | ((uint64_t)rec[3] << 32);
+    whi = (uint64_t)rec[4] | ((uint64_t)rec[5] << 32);
+  } else {
+    uint32_t lw[5];
     const int w0 = tb >> 5, last = a.label_words - 1;
+    o4 = a.off4[r];
+    o8 = a.off8[r];
+    const uint32_t *wd = reinterpret_cast<const uint32_t *>(a.labels);
 #pragma unroll
     for (int k = 0; k < 5; ++k) lw[k] = wd[min(w0 + k, last)];
+    if ((o4 | o8) < 0) lw[4] = 0u;  // negative row offsets: inconsistent metadata
+    label_window(lw, tb, wlo, whi);
   }
-  if ((o4 | o8) < 0) lw[4] = 0u;  // negative row offsets: inconsistent metadata
-  uint64_t wlo, whi;
-  label_window(lw, tb, wlo, whi);
   int n4 = c0 <= 64 ? __popcll(wlo & low_mask(c0)) : __popcll(wlo) + __popcll(whi & low_mask(c0 - 64));
   int idx4 = o4 + n4;
   int idx8 = o8 + (c0 - n4);
@@ -475,7 +513,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
       // its stores have completed before the barrier that precedes the
       // counter increment, and the last workgroup reads the slots only after
       // its increment has returned.
-      float4 *pp = a.part + ((size_t)(r * 4 + rg) * Y + yc) * Z * MG * 64 + lane;
+      float4 *pp = a.part + ((size_t)(r * 4 + rg) * gridDim.y + yc) * Z * MG * 64 + lane;
       if (sp == 0) {
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg) store_coherent(pp + ((size_t)zc * MG + mg) * 64, F[mg]);
@@ -484,7 +522,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
       __syncthreads();
       uint32_t *flag = reinterpret_cast<uint32_t *>(smem);  // LDS is free again
       if (tid == 0) {
-        uint32_t *cp = a.cnt + (size_t)bx * Y + yc;
+        uint32_t *cp = a.cnt + (size_t)bx * gridDim.y + yc;
         const uint32_t prev = __hip_atomic_fetch_add(cp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t last = prev == (uint32_t)(Z - 1) ? 1u : 0u;
         if (last) __hip_atomic_store(cp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -527,42 +565,47 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DecodeArgs a) 
   }
 }
 
-template <typename Kern>
-void launch_one(Kern kern, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const DecodeArgs &args) {
+template <typename Kern, typename Args>
+void launch_one(Kern kern, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const Args &args) {
   if (lds > 64 * 1024) (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(kern, grid, block, lds, stream, args);
 }
 
-// Grid: row blocks (4R/RG) x token chunks (args.ychunks) x column chunks
-// (Z), flattened with the column chunks fastest.
-template <int BK, int MODE, int MG, int WAVES, int DEPTH, int XMODE, bool PARTIALS>
-void launch_rg(const DecodePlan &p, int R, hipStream_t stream, const DecodeArgs &args) {
+// Grid: row blocks (4R/RG) along x, token chunks along y, column chunks
+// along z.
+template <int BK, int MODE, int MG, int WAVES, int DEPTH, int XMODE, bool PARTIALS, bool INL>
+void launch_rg(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL> &args) {
   const dim3 block(WAVES * 64);
-  const int zy = p.Z * args.ychunks;
+  const int y = args.ychunks, z = p.Z;
   switch (p.RG) {
-    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS>, dim3(R * zy), block, p.lds, stream, args); break;
-    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS>, dim3(R * 2 * zy), block, p.lds, stream, args); break;
-    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS>, dim3(R * 4 * zy), block, p.lds, stream, args); break;
+    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS, INL>, dim3(R, y, z), block, p.lds, stream, args); break;
+    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS, INL>, dim3(R * 2, y, z), block, p.lds, stream, args); break;
+    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS, INL>, dim3(R * 4, y, z), block, p.lds, stream, args); break;
   }
 }
 
-template <int BK, bool PARTIALS>
-void launch_mode(const DecodePlan &p, int R, hipStream_t stream, const DecodeArgs &args) {
+template <int BK, bool PARTIALS, bool INL>
+void launch_mode(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL> &args) {
   if (p.mode == kValu) {
-    launch_rg<BK, kValu, 1, 16, kPrivDepth, kXPriv, PARTIALS>(p, R, stream, args);
+    launch_rg<BK, kValu, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL>(p, R, stream, args);
     return;
   }
   if (p.xmode == kXPriv) {
-    launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS>(p, R, stream, args);
+    launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL>(p, R, stream, args);
     return;
   }
   switch (p.MG) {
-    case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, PARTIALS>(p, R, stream, args); break;
-    case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, PARTIALS>(p, R, stream, args); break;
-    case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, PARTIALS>(p, R, stream, args); break;
-    default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, PARTIALS>(p, R, stream, args); break;
+    case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, PARTIALS, INL>(p, R, stream, args); break;
+    case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, PARTIALS, INL>(p, R, stream, args); break;
+    case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, PARTIALS, INL>(p, R, stream, args); break;
+    default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, PARTIALS, INL>(p, R, stream, args); break;
   }
+}
+
+// Whether a call passes the metadata inside the kernel arguments.
+bool inline_meta(const PackedView &w) {
+  return w.meta && w.C <= 128 && kMetaStride * w.R <= kInlineWords;
 }
 
 // Packed tiles of more than 16 MB: a projection too large to stay in the
@@ -676,10 +719,12 @@ DecodePlan plan_decode(const PackedView &w, int M, int split) {
   }
   p.S = p.waves / p.RG;
   if (p.mode == kValu || p.xmode == kXPriv) p.ylaunch = 1;
+  if (p.ylaunch > 65535) p.ylaunch = 65535;  // grid y limit
   return p;
 }
 
 bool decode_plan_ok(const DecodePlan &p, const PackedView &w) {
+  if ((long long)w.C * p.Z * p.S >= (1LL << 31)) return false;  // 32-bit split bounds
   return p.Z == 1 || w.R * 4 / p.RG <= kDecodeCounters;
 }
 
@@ -717,19 +762,26 @@ hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx,
   // token ranges of ylaunch chunks of 16*MG tokens, one launch each
   const int mstep = p.ylaunch * 16 * p.MG;
   for (int m0 = 0; m0 < M; m0 += mstep) {
-    DecodeArgs la = args;
+    DArgs<false> la;
+    static_cast<DecodeArgs &>(la) = args;
     la.M = M - m0 < mstep ? M - m0 : mstep;
     la.qx = qx + (size_t)m0 * w.K;
     if (sx) la.sx = sx + m0;
     if (Y) la.Y = Y + (size_t)m0 * w.N;
     if (P) la.P = P + (size_t)m0 * w.N * w.C;
     la.ychunks = p.mode == kValu || p.xmode == kXPriv ? 1 : (la.M + 16 * p.MG - 1) / (16 * p.MG);
-    if (w.bK == 128) {
-      if (P) launch_mode<128, true>(p, w.R, stream, la);
-      else launch_mode<128, false>(p, w.R, stream, la);
+    if (P) {
+      if (w.bK == 128) launch_mode<128, true, false>(p, w.R, stream, la);
+      else launch_mode<64, true, false>(p, w.R, stream, la);
+    } else if (inline_meta(w)) {
+      DArgs<true> li;
+      static_cast<DecodeArgs &>(li) = la;
+      std::memcpy(li.meta, w.meta, sizeof(uint32_t) * kMetaStride * w.R);
+      if (w.bK == 128) launch_mode<128, false, true>(p, w.R, stream, li);
+      else launch_mode<64, false, true>(p, w.R, stream, li);
     } else {
-      if (P) launch_mode<64, true>(p, w.R, stream, la);
-      else launch_mode<64, false>(p, w.R, stream, la);
+      if (w.bK == 128) launch_mode<128, false, false>(p, w.R, stream, la);
+      else launch_mode<64, false, false>(p, w.R, stream, la);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

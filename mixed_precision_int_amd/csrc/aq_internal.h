@@ -21,6 +21,7 @@ struct PackedView {
   const uint8_t *w4;
   const int8_t *w8;
   const float *s4, *s8;
+  const uint32_t *meta;  // host metadata image, or nullptr
 };
 
 inline PackedView view_of(const aq_packed &p) {
@@ -30,6 +31,7 @@ inline PackedView view_of(const aq_packed &p) {
   v.T4 = p.T4; v.T8 = p.T8;
   v.labels = p.labels; v.off4 = p.row_off4; v.off8 = p.row_off8;
   v.w4 = p.w4; v.w8 = p.w8; v.s4 = p.s4; v.s8 = p.s8;
+  v.meta = p.meta_host;
   return v;
 }
 

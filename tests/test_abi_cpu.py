@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(aqlib):
 
 
 def test_abi_version_and_status_strings(aqlib):
-    assert B.aq_abi_version() == 3
+    assert B.aq_abi_version() == 4
     for code in list(B.STATUS) + [-99]:
         assert aqlib.aq_status_string(code)
 

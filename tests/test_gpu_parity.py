@@ -287,6 +287,38 @@ def test_decode_chunked_many_token_chunks():
                         "many-token-chunks")
 
 
+@pytest.mark.parametrize("N,K,M", [(1024, 4096, 1), (1024, 4096, 4), (1024, 4096, 16), (9536, 2048, 40),
+                                   (576, 16384, 3)])
+def test_decode_inline_metadata(N, K, M):
+    """The host metadata image (one record per tile row: row offsets, then
+    the row's labels as 128 bits) matches the oracle's offsets and labels,
+    and decode gives bitwise the same outputs whether the image travels in
+    the kernel arguments or the metadata is read from device memory."""
+    rng = np.random.default_rng(N + K + M)
+    R, C = N // 64, K // 128
+    W = gen.weights(rng, N, K)
+    z = gen.map_uniform(rng, R, C, 0.35)
+    X = gen.acts_outliers(rng, M, K, 3, 20.0)
+    c = Case(W, z, X, name=f"inline-meta{N}x{K}/M{M}")
+    out = c.check_all(phases=("decode",))
+    meta = c.pw.meta_host.reshape(R, 6)
+    assert np.array_equal(meta[:, 0].astype(np.int64), O.row_offsets(z, 4)[:R])
+    assert np.array_equal(meta[:, 1].astype(np.int64), O.row_offsets(z, 8)[:R])
+    bits = (np.asarray(z) == 4).astype(np.uint64)
+    for r in range(R):
+        want = [int(sum(int(bits[r, j]) << (j - 32 * w) for j in range(32 * w, min(C, 32 * w + 32))))
+                for w in range(4)]
+        assert [int(v) for v in meta[r, 2:]] == want, r
+    saved = c.pw.desc.meta_host
+    try:
+        c.pw.desc.meta_host = None     # device metadata route
+        Y = aq.aq_linear_decode(c.pw, c.qx_d, c.sx_d)
+        torch.cuda.synchronize()
+    finally:
+        c.pw.desc.meta_host = saved
+    assert torch.equal(Y.view(torch.int32), out["decode0"].view(torch.int32))
+
+
 def test_long_prefill_persistent_tiles_ragged():
     """The persistent 256 x 256-tile kernel (taken when the prompt yields at
     least one tile per compute unit): 257 tile rows (the last N block holds
