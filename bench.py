@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes three times (the "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--split-comparison", action="store_true",
+                    help="only time the decode linears of the Llama-3.2-3B shapes with the adaptive "
+                         "split and with every fixed split, and print a markdown table")
     ap.add_argument("--traffic-summary", nargs=4, metavar="CSV",
                     help="print the per-launch HBM traffic summary from four rocprofv3 counter "
                          "CSVs: bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE")
@@ -292,6 +295,42 @@ def cpu_baseline(budget_s: float):
     )
 
 
+def split_comparison(aq, torch, dec, ws, reps: int = 48):
+    """Adaptive against fixed decode splits (the kernel-level analogue of the
+    pages' fixed-vs-adaptive split ablation, Table 22): per call, the average
+    over `reps` back-to-back calls behind a GPU hold, each call on the next
+    of the 24 weight copies; the weight bytes come from HBM."""
+    def timed(calls):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(30_000_000)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for f in calls:
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / len(calls)
+
+    splits = (16, 8, 4)
+    rows = ["| projection | M | adaptive S | adaptive µs | " + " | ".join(f"S = {s} µs" for s in splits)
+            + " | adaptive vs best fixed |", "|---" * (5 + len(splits)) + "|"]
+    for proj, copies, xs, bufs in dec:
+        for M in DECODE_M:
+            qx, sx, Y = bufs[M]
+            aq.aq_quant_act(xs[M], qx, sx)
+            res = {}
+            for s in (0,) + splits:
+                calls = [(lambda c=c, s=s: aq.aq_linear_decode(copies[c % N_COPIES], qx, sx, None, s, Y, ws))
+                         for c in range(reps)]
+                timed(calls[:4])
+                res[s] = timed(calls)
+            best = min(res[s] for s in splits)
+            p = copies[0].plan
+            rows.append(f"| {proj} {p.N}x{p.K} | {M} | {aq.aq_decode_split(copies[0], M)} | {res[0]:.2f} | "
+                        + " | ".join(f"{res[s]:.2f}" for s in splits) + f" | {best / res[0]:.3f} |")
+    print("\n".join(rows))
+
+
 def main():
     args = parse()
     if args.traffic_summary:
@@ -319,6 +358,9 @@ def main():
         return
     aq.lib()
     dec, ws, pre = setup(aq, gen, torch)
+    if args.split_comparison:
+        split_comparison(aq, torch, dec, ws)
+        return
 
     t_host = 0.0
     for i in range(args.warmup):
