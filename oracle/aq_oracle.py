@@ -28,6 +28,10 @@ statement:
         16 bytes; byte b packs q0 = code at k = 32p + b and q1 = code at
         k = 32p + 16 + b as (q0 mod 16) + 16 (q1 mod 16)   (App. E.1 eq. 17).
 
+The pages' own activation quantizer (App. B.3: 64-feature x b_M-row
+groups, the endpoint scale of eq. 6) is here as quant_act_grouped with its
+eq. 19 counterpart; the per-token form above is the default path.
+
 Parity status: every function here is pinned by tests/test_oracle_*.py
 (hand-worked fixtures under tests/golden/, closed forms, brute force and
 invariants).  Parity with numbers printed on the pages is unpinned for the
@@ -181,6 +185,100 @@ def quant_act(X: np.ndarray):
         qx[m] = quantize(row, s, 8)
         sx[m] = np.float32(s)
     return qx, sx
+
+
+# --------------------------------------------------------------------------
+# The pages' activation quantizer (App. B.3 with App. B.2 eq. 5-6)
+# --------------------------------------------------------------------------
+
+ACT_GROUP_K = 64   # App. B.3: one activation scale per 64 features ...
+
+
+def act_group_rows(M: int) -> int:
+    """... and b_M rows: b_M = 1 when M = 1, otherwise 16 (App. B.3)."""
+    return 1 if M == 1 else 16
+
+
+def endpoint_scale(A: np.ndarray, b: int) -> float:
+    """s_0,b(A) = max(max(0, max A) / q_max,b, max(0, -min A) / |q_min,b|,
+    1e-12) in FP64 (App. B.2 eq. 6)."""
+    lo, hi = qrange(b)
+    A64 = np.asarray(A, dtype=np.float64)
+    top = max(0.0, float(np.max(A64))) if A64.size else 0.0
+    bot = max(0.0, -float(np.min(A64))) if A64.size else 0.0
+    return max(top / hi, bot / abs(lo), SCALE_FLOOR)
+
+
+def quant_act_grouped(X: np.ndarray):
+    """The pages' activation quantization (App. B.3): rows are zero-padded to
+    M' = ceil(M / b_M) b_M; every group A of b_M rows x 64 features gets the
+    FP64 scale s = s_0,8(A) of eq. 6 and codes Q_8(A; s) (eq. 5); the stored
+    scale is FP32(s).  Padding rows are zero, so they change no group's
+    maximum or minimum beyond the zeros eq. 6 already includes; the codes of
+    the padding rows are dropped (the output is sliced back to M rows).
+
+    Returns qx int64 [M, K] and sxg float32 [ceil(M / b_M), K / 64], group
+    (g, c) covering rows g b_M .. g b_M + b_M - 1 and features 64c .. 64c+63.
+    """
+    X = np.asarray(X)
+    M, K = X.shape
+    if K % ACT_GROUP_K:
+        raise ValueError("K must be a multiple of 64")
+    bM = act_group_rows(M)
+    G = -(-M // bM)
+    Xp = np.zeros((G * bM, K), dtype=np.float64)
+    Xp[:M] = X
+    qx = np.zeros((G * bM, K), dtype=np.int64)
+    sxg = np.zeros((G, K // ACT_GROUP_K), dtype=np.float32)
+    for g in range(G):
+        for c in range(K // ACT_GROUP_K):
+            rows = slice(g * bM, (g + 1) * bM)
+            cols = slice(c * ACT_GROUP_K, (c + 1) * ACT_GROUP_K)
+            A = Xp[rows, cols]
+            s = endpoint_scale(A, 8)
+            qx[rows, cols] = quantize(A, s, 8)
+            sxg[g, c] = np.float32(s)
+    return qx[:M], sxg
+
+
+def group_partials(qx: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """P[m, n, c] = sum over the 64 features k of activation group c of
+    qx[m, k] * codes[n, k]: eq. 19's integer product per 64-wide column
+    group (a b_K = 128 tile holds two), int64 [M, N, K / 64].  Each product
+    is a float64 matrix product of integers below 2^53, hence exact."""
+    return tile_partials(qx, codes, ACT_GROUP_K)
+
+
+def linear_from_group_partials(P: np.ndarray, sxg: np.ndarray, sW: np.ndarray, bK: int,
+                               bias: np.ndarray | None = None) -> np.ndarray:
+    """y[m, n] = sum_c s^X_{g(m), c} s^W_{n, j(c)} P[m, n, c] (+ bias[n]) in
+    FP64, c in increasing order, g(m) = m // b_M and j(c) = 64 c // b_K the
+    tile column holding group c (App. E.3 eq. 19 with the App. B.3 groups)."""
+    M, N, CG = P.shape
+    bM = act_group_rows(M)
+    sx64 = np.asarray(sxg, dtype=np.float64)[np.arange(M) // bM]     # [M, CG]
+    sW64 = np.asarray(sW, dtype=np.float64)
+    y = np.zeros((M, N), dtype=np.float64)
+    for c in range(CG):
+        j = (c * ACT_GROUP_K) // bK
+        y += (sx64[:, c][:, None] * sW64[None, :, j]) * P[:, :, c].astype(np.float64)
+    if bias is not None:
+        y += np.asarray(bias, dtype=np.float64)[None, :]
+    return y
+
+
+def abs_contrib_grouped(P: np.ndarray, sxg: np.ndarray, sW: np.ndarray, bK: int) -> np.ndarray:
+    """sum_c |s^X_{g(m), c} s^W_{n, j(c)} P[m, n, c]|, the componentwise
+    error scale of an FP32 evaluation of the grouped eq. 19."""
+    M, N, CG = P.shape
+    bM = act_group_rows(M)
+    sx64 = np.asarray(sxg, dtype=np.float64)[np.arange(M) // bM]
+    sW64 = np.asarray(sW, dtype=np.float64)
+    a = np.zeros((M, N), dtype=np.float64)
+    for c in range(CG):
+        j = (c * ACT_GROUP_K) // bK
+        a += np.abs((sx64[:, c][:, None] * sW64[None, :, j]) * P[:, :, c].astype(np.float64))
+    return a
 
 
 # --------------------------------------------------------------------------
