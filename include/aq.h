@@ -233,6 +233,47 @@ aq_status aq_linear_prefill(const aq_packed *W, const int8_t *qx, const float *s
 aq_status aq_linear_tile_partials(const aq_packed *W, const int8_t *qx, int M, int phase,
                                   int32_t *P, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- The pages' activation quantizer (App. B.3) ------------------------
+ * The entry points above scale activations per token (absmax / 127).  These
+ * follow App. B.3 instead: one scale per group of 64 features x b_M rows,
+ * b_M = 1 when M == 1 and 16 otherwise, with the endpoint scale of App. B.2
+ * eq. 6 at 8 bits, and eq. 19 with one activation scale per 64-feature
+ * group (a b_K = 128 tile holds two). */
+
+/* Activation quantization with App. B.3 groups: for each group A of b_M rows
+ * (rows past M are App. B.3's zero padding) and features 64c .. 64c+63,
+ * s = max(max(0, max A) / 127, max(0, -min A) / 128, 1e-12) in FP64 (eq. 6),
+ * codes clip(round_half_even(A / s), -128, 127) in FP64 (eq. 5), stored
+ * scale FP32(s).
+ *   X    device FP32 [M][K], K a multiple of 64
+ *   qx   device INT8 [M][K]
+ *   sxg  device FP32 [ceil(M/b_M)][K/64]: group (g, c) at g*(K/64) + c
+ * M == 0 is a no-op. */
+aq_status aq_quant_act_grouped(const float *X, int M, int K, int8_t *qx, float *sxg, void *stream);
+
+/* aq_linear_decode with App. B.3 activation groups:
+ *   Y[m,n] = sum_c sxg[m / b_M][c] * sW[n, 64c / bK] * P[m,n,c]  (+ bias[n]),
+ * P[m,n,c] the INT32 product over the 64 features of group c, summed in the
+ * same split order.  sxg as written by aq_quant_act_grouped for the same M.
+ * split, ws and errors as aq_linear_decode (the same workspace rule).  The
+ * host metadata image (aq_packed.meta_host) is not used on this route. */
+aq_status aq_linear_decode_grouped(const aq_packed *W, const int8_t *qx, const float *sxg, int M,
+                                   const float *bias, float *Y, int split, void *ws, size_t ws_bytes,
+                                   void *stream);
+
+/* The same product for any prompt length, computed by the decode kernels
+ * (INT8 MFMA over up to 64 tokens per workgroup, token chunks one after
+ * another); identical to aq_linear_decode_grouped with split 0, including
+ * its workspace rule. */
+aq_status aq_linear_prefill_grouped(const aq_packed *W, const int8_t *qx, const float *sxg, int M,
+                                    const float *bias, float *Y, void *ws, size_t ws_bytes,
+                                    void *stream);
+
+/* Debug: the INT32 group products P[m, n, c] of the grouped eq. 19, written
+ * as INT32 [M][N][K/64] row-major by the grouped decode kernels. */
+aq_status aq_linear_tile_partials_grouped(const aq_packed *W, const int8_t *qx, int M, int32_t *P,
+                                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

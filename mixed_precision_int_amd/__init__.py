@@ -17,7 +17,12 @@ from .binding import (  # noqa: F401
     aq_alloc_packed,
     aq_decode_split,
     aq_labels_from_map,
+    act_group_rows,
     aq_linear_decode,
+    aq_linear_decode_grouped,
+    aq_linear_prefill_grouped,
+    aq_linear_tile_partials_grouped,
+    aq_quant_act_grouped,
     aq_linear_prefill,
     aq_linear_tile_partials,
     aq_pack_weights,

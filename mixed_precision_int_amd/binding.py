@@ -26,7 +26,9 @@ STATUS = {0: "AQ_OK", -1: "AQ_ERR_NULL", -2: "AQ_ERR_SHAPE", -3: "AQ_ERR_TILE", 
 # Every symbol include/aq.h declares.
 EXPORTS = ["aq_abi_version", "aq_status_string", "aq_labels_from_map", "aq_plan_pack",
            "aq_pack_weights", "aq_quant_act", "aq_workspace_bytes", "aq_decode_split",
-           "aq_linear_decode", "aq_linear_prefill", "aq_linear_tile_partials"]
+           "aq_linear_decode", "aq_linear_prefill", "aq_linear_tile_partials",
+           "aq_quant_act_grouped", "aq_linear_decode_grouped", "aq_linear_prefill_grouped",
+           "aq_linear_tile_partials_grouped"]
 
 
 class AqError(RuntimeError):
@@ -83,6 +85,10 @@ def lib() -> ctypes.CDLL:
         "aq_linear_decode": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp, sz, vp]),
         "aq_linear_prefill": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
         "aq_linear_tile_partials": (i32, [ctypes.POINTER(AqPacked), vp, i32, i32, vp, vp, sz, vp]),
+        "aq_quant_act_grouped": (i32, [vp, i32, i32, vp, vp, vp]),
+        "aq_linear_decode_grouped": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp, sz, vp]),
+        "aq_linear_prefill_grouped": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
+        "aq_linear_tile_partials_grouped": (i32, [ctypes.POINTER(AqPacked), vp, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -289,4 +295,71 @@ def aq_linear_tile_partials(pw: PackedWeights, qx, phase: int, out=None, ws=None
     ws, ws_bytes = (None, 0) if phase != AQ_PHASE_PREFILL else _workspace(pw, M, phase, ws, qx.device)
     _check(lib().aq_linear_tile_partials(ctypes.byref(pw.desc), _ptr(qx), M, phase, _ptr(out),
                                          _ptr(ws), ws_bytes, _stream(stream)), "aq_linear_tile_partials")
+    return out
+
+
+# ---------------------------------------------------------------- App. B.3 activation groups
+
+def act_group_rows(M: int) -> int:
+    """b_M of App. B.3: 1 for a single token, else 16."""
+    return 1 if M == 1 else 16
+
+
+def aq_quant_act_grouped(X, qx=None, sxg=None, stream=None):
+    """INT8 codes [M, K] and FP32 group scales [ceil(M/b_M), K/64] of device
+    FP32 X [M, K] (one scale per 64 features x b_M rows, eq. 6)."""
+    import torch
+    M, K = X.shape
+    G = -(-M // act_group_rows(M))
+    if qx is None:
+        qx = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if sxg is None:
+        sxg = torch.empty((G, K // 64), dtype=torch.float32, device=X.device)
+    _check(lib().aq_quant_act_grouped(ctypes.c_void_p(X.data_ptr()), M, K, ctypes.c_void_p(qx.data_ptr()),
+                                      ctypes.c_void_p(sxg.data_ptr()), _stream(stream)),
+           "aq_quant_act_grouped")
+    return qx, sxg
+
+
+def aq_linear_decode_grouped(pw: PackedWeights, qx, sxg, bias=None, split: int = 0, out=None, ws=None,
+                             stream=None):
+    """Decode-phase linear with App. B.3 group scales: FP32 Y [M, N]."""
+    import torch
+    M = qx.shape[0]
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=qx.device)
+    need = aq_workspace_bytes(pw, M, AQ_PHASE_DECODE, split)
+    if ws is None and need:
+        ws = decode_workspace(need, qx.device, stream)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().aq_linear_decode_grouped(ctypes.byref(pw.desc), _ptr(qx), _ptr(sxg), M, _ptr(bias),
+                                          _ptr(out), split, _ptr(ws), ws_bytes, _stream(stream)),
+           "aq_linear_decode_grouped")
+    return out
+
+
+def aq_linear_prefill_grouped(pw: PackedWeights, qx, sxg, bias=None, out=None, ws=None, stream=None):
+    """Any-length linear with App. B.3 group scales (the decode kernels)."""
+    import torch
+    M = qx.shape[0]
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=qx.device)
+    need = aq_workspace_bytes(pw, M, AQ_PHASE_DECODE, 0)
+    if ws is None and need:
+        ws = decode_workspace(need, qx.device, stream)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().aq_linear_prefill_grouped(ctypes.byref(pw.desc), _ptr(qx), _ptr(sxg), M, _ptr(bias),
+                                           _ptr(out), _ptr(ws), ws_bytes, _stream(stream)),
+           "aq_linear_prefill_grouped")
+    return out
+
+
+def aq_linear_tile_partials_grouped(pw: PackedWeights, qx, out=None, stream=None):
+    """INT32 group products P [M, N, K/64] of the grouped eq. 19."""
+    import torch
+    M = qx.shape[0]
+    if out is None:
+        out = torch.empty((M, pw.N, pw.K // 64), dtype=torch.int32, device=qx.device)
+    _check(lib().aq_linear_tile_partials_grouped(ctypes.byref(pw.desc), _ptr(qx), M, _ptr(out),
+                                                 _stream(stream)), "aq_linear_tile_partials_grouped")
     return out

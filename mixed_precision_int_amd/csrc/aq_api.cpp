@@ -202,6 +202,18 @@ aq_status aq_quant_act(const float *X, int M, int K, int8_t *qx, float *sx, void
              : AQ_ERR_HIP;
 }
 
+aq_status aq_quant_act_grouped(const float *X, int M, int K, int8_t *qx, float *sxg, void *stream) {
+  if (M < 0 || K <= 0 || K % 64) return AQ_ERR_SHAPE;
+  if (M == 0) return AQ_OK;
+  if (!X || !qx || !sxg) return AQ_ERR_NULL;
+  if (!aligned16(X) || !aligned16(qx) || !aligned4(sxg)) return AQ_ERR_ALIGN;
+  if ((long long)M * K > (1LL << 40) || (M + 15) / 16 > 65535) return AQ_ERR_SHAPE;
+  return aq::launch_quant_act_grouped(X, M, K, qx, sxg, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
 int aq_decode_split(const aq_packed *W, int M) {
   if (check_packed(W) != AQ_OK || M < 0) return 0;
   return aq::decode_split(aq::view_of(*W), M);
@@ -230,6 +242,47 @@ aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx
   if (st != AQ_OK) return st;
   return aq::launch_decode(v, qx, sx, M, bias, Y, split, ws, nullptr,
                            static_cast<hipStream_t>(stream)) == hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
+aq_status aq_linear_decode_grouped(const aq_packed *W, const int8_t *qx, const float *sxg, int M,
+                                   const float *bias, float *Y, int split, void *ws, size_t ws_bytes,
+                                   void *stream) {
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  st = check_linear_io(W, qx, sxg, M, bias, Y);
+  if (st != AQ_OK || M == 0) return st;
+  const aq::PackedView v = aq::view_of(*W);
+  if (split < 0 || (split > 0 && !aq::decode_split_supported(v, M, split))) return AQ_ERR_ARG;
+  if (!aq::decode_plan_ok(aq::plan_decode(v, M, split), v)) return AQ_ERR_SHAPE;
+  st = check_workspace(ws, ws_bytes, aq::decode_workspace_bytes(v, M, split));
+  if (st != AQ_OK) return st;
+  return aq::launch_decode(v, qx, sxg, M, bias, Y, split, ws, nullptr,
+                           static_cast<hipStream_t>(stream), true) == hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
+aq_status aq_linear_prefill_grouped(const aq_packed *W, const int8_t *qx, const float *sxg, int M,
+                                    const float *bias, float *Y, void *ws, size_t ws_bytes,
+                                    void *stream) {
+  return aq_linear_decode_grouped(W, qx, sxg, M, bias, Y, 0, ws, ws_bytes, stream);
+}
+
+aq_status aq_linear_tile_partials_grouped(const aq_packed *W, const int8_t *qx, int M, int32_t *P,
+                                          void *stream) {
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  if (M < 0) return AQ_ERR_SHAPE;
+  if (M == 0) return AQ_OK;
+  if (!qx || !P) return AQ_ERR_NULL;
+  if (!aligned16(qx) || !aligned4(P)) return AQ_ERR_ALIGN;
+  const aq::PackedView v = aq::view_of(*W);
+  if ((long long)M * v.N * (v.K / 64) > (1LL << 40)) return AQ_ERR_SHAPE;
+  if (!aq::decode_plan_ok(aq::plan_decode(v, M, 0), v)) return AQ_ERR_SHAPE;
+  return aq::launch_decode(v, qx, nullptr, M, nullptr, nullptr, 0, nullptr, P,
+                           static_cast<hipStream_t>(stream), true) == hipSuccess
              ? AQ_OK
              : AQ_ERR_HIP;
 }

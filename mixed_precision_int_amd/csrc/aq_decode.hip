@@ -91,6 +91,7 @@ struct DecodeArgs {
   int Z, ychunks, xstride;
   uint32_t *cnt;
   float4 *part;
+  int kg64;  // grouped activation scales: 64-feature groups per row (K/64)
 };
 
 // With INL each tile row's record of the host metadata image (row_off4[r],
@@ -162,8 +163,12 @@ __device__ __forceinline__ int sum_kgroups_i(int v) {
 // b_K = 64 INT4 tiles the operand is two 8-byte pieces (low-nibble and
 // high-nibble columns).  With SW >= 0 the row is an LDS row whose 16-byte
 // granules are XOR-swizzled by SW.
-template <int BK>
+template <int BK, bool GRP>
 __device__ __forceinline__ v4i x_operand(const int8_t *row, int colbase, int g, int u, int is4, int sw) {
+  if (BK == 128 && GRP) {  // step u = 64-feature group u of the tile
+    const int c = colbase + 64 * u + 16 * g;
+    return load16(row + 16 * ((c >> 4) ^ sw));
+  }
   if (BK == 64 && is4) {
     const int ca = colbase + 32 * (g >> 1) + 8 * (g & 1);
     const int cb = ca + 16;
@@ -175,7 +180,8 @@ __device__ __forceinline__ v4i x_operand(const int8_t *row, int colbase, int g, 
   return load16(row + 16 * ((c >> 4) ^ sw));
 }
 
-template <int BK, int MODE, int MG, int WAVES, int RG, int DEPTH, int XMODE, bool PARTIALS, bool INL>
+template <int BK, int MODE, int MG, int WAVES, int RG, int DEPTH, int XMODE, bool PARTIALS, bool INL,
+          bool GRP>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) {
   constexpr int KS = BK / 64;    // MFMA steps (16-byte operands per lane) per tile
   constexpr int S = WAVES / RG;  // splits per row group
@@ -326,7 +332,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
           live[d] = 1;                                                                          \
           is4v[d] = is4;                                                                        \
           jv[d] = jt;                                                                           \
-          if (BK == 128) {                                                                      \
+          if (BK == 128 && GRP) {                                                               \
+            /* step u: columns 64u + 16g ..: INT8 panel 4u + g; INT4 panel */                   \
+            /* 2u + g/2, nibble g % 2 */                                                         \
+            if (is4) {                                                                          \
+              const uint8_t *base = w4p + (size_t)idx * 4096 + (g >> 1) * 1024 + rowoff;        \
+              W[d][0] = load16(base);                                                           \
+              W[d][1] = load16(base + 2048);                                                    \
+            } else {                                                                            \
+              const uint8_t *base = w8p + (size_t)idx * 8192 + g * 1024 + rowoff;               \
+              W[d][0] = load16(base);                                                           \
+              W[d][1] = load16(base + 4096);                                                    \
+            }                                                                                   \
+          } else if (BK == 128) {                                                               \
             if (is4) {                                                                          \
               W[d][0] = load16(w4p + (size_t)idx * 4096 + g * 1024 + rowoff);                   \
             } else {                                                                            \
@@ -405,7 +423,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
       const int is4 = is4v[d];
       // weight operand per step
       v4i wop[KS];
-      if (BK == 128) {
+      if (BK == 128 && GRP) {
+        if (is4) {  // this lane's nibble of both panels
+          const v4i w0 = W[d][0], w1 = W[d][1];
+          const bool hi = (g & 1) != 0;
+          wop[0] = hi ? v4i{w4_hi16(w0[0]), w4_hi16(w0[1]), w4_hi16(w0[2]), w4_hi16(w0[3])}
+                      : v4i{w4_lo16(w0[0]), w4_lo16(w0[1]), w4_lo16(w0[2]), w4_lo16(w0[3])};
+          wop[KS - 1] = hi ? v4i{w4_hi16(w1[0]), w4_hi16(w1[1]), w4_hi16(w1[2]), w4_hi16(w1[3])}
+                           : v4i{w4_lo16(w1[0]), w4_lo16(w1[1]), w4_lo16(w1[2]), w4_lo16(w1[3])};
+        } else {
+          wop[0] = W[d][0];
+          wop[KS - 1] = W[d][1];
+        }
+      } else if (BK == 128) {
         if (is4) {
           const v4i w = W[d][0];
           wop[0] = v4i{w4_lo16(w[0]), w4_lo16(w[1]), w4_lo16(w[2]), w4_lo16(w[3])};
@@ -428,10 +458,45 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
           const int8_t *xr = XMODE == kXPriv ? xw + trow * XW : xs + trow * xst;
           const int xcol = XMODE == kXPriv ? d * BK : (jt - ca) * BK;
           const int sw = XMODE == kXShared ? (trow & 15) : 0;
+          if constexpr (GRP) {
+            // one INT32 product per 64-feature group (step u), each scaled by
+            // its own activation-group scale (token group of 16 rows)
+            v4i accg[KS];
+#pragma unroll
+            for (int u = 0; u < KS; ++u) {
+              const v4i xop = x_operand<BK, GRP>(xr, xcol, g, u, is4, sw);
+              accg[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xop, wop[u], v4i{0, 0, 0, 0}, 0, 0, 0);
+            }
+            if constexpr (PARTIALS) {
+              const size_t n = (size_t)r * 64 + rg * 16 + i16;
+#pragma unroll
+              for (int u = 0; u < KS; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int m = mbase + mg * 16 + 4 * g + e;
+                  if (m < M)
+                    a.P[((size_t)m * a.N + n) * a.kg64 + jt * KS + u] = is4 ? (accg[u][e] >> 4) : accg[u][e];
+                }
+            } else {
+              // a group of padding tokens only (never stored) reads the last
+              // real group's scales
+              const int grp = min(mbase / 16 + mg, (M - 1) / 16);
+              const float *sxr = a.sx + (size_t)grp * a.kg64 + jt * KS;
+#pragma unroll
+              for (int u = 0; u < KS; ++u) {
+                const float c = sc * sxr[u];
+                F[mg].x = fmaf((float)accg[u][0], c, F[mg].x);
+                F[mg].y = fmaf((float)accg[u][1], c, F[mg].y);
+                F[mg].z = fmaf((float)accg[u][2], c, F[mg].z);
+                F[mg].w = fmaf((float)accg[u][3], c, F[mg].w);
+              }
+            }
+            continue;
+          }
           v4i acc = {0, 0, 0, 0};
 #pragma unroll
           for (int u = 0; u < KS; ++u) {
-            const v4i xop = x_operand<BK>(xr, xcol, g, u, is4, sw);
+            const v4i xop = x_operand<BK, GRP>(xr, xcol, g, u, is4, sw);
             acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(xop, wop[u], acc, 0, 0, 0);
           }
           if constexpr (PARTIALS) {
@@ -449,6 +514,28 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
             F[mg].w = fmaf((float)acc[3], sc, F[mg].w);
           }
         }
+      } else if constexpr (GRP) {
+        // vector ALU, one token (its own row group): one product per
+        // 64-feature group (step u)
+        int accg[KS];
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+          accg[u] = 0;
+          const v4i xop = x_operand<BK, GRP>(xw, d * BK, g, u, is4, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) accg[u] = __builtin_amdgcn_sdot4(wop[u][e], xop[e], accg[u], false);
+        }
+        if constexpr (PARTIALS) {
+          const size_t n = (size_t)r * 64 + rg * 16 + i16;
+#pragma unroll
+          for (int u = 0; u < KS; ++u) {
+            const int v = sum_kgroups_i(accg[u]);
+            if (g == 0) a.P[n * a.kg64 + jt * KS + u] = is4 ? (v >> 4) : v;
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < KS; ++u) F[0].x = fmaf((float)accg[u], sc * a.sx[jt * KS + u], F[0].x);
+        }
       } else {
         // vector ALU: the one token, this lane's 16*KS columns
         int acc[kValuMaxM];
@@ -458,7 +545,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
           if (m < M) {
 #pragma unroll
             for (int u = 0; u < KS; ++u) {
-              const v4i xop = x_operand<BK>(xw + m * XW, d * BK, g, u, is4, 0);
+              const v4i xop = x_operand<BK, GRP>(xw + m * XW, d * BK, g, u, is4, 0);
 #pragma unroll
               for (int e = 0; e < 4; ++e) acc[m] = __builtin_amdgcn_sdot4(wop[u][e], xop[e], acc[m], false);
             }
@@ -549,7 +636,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
         const float fv[4] = {F[0].x, F[0].y, F[0].z, F[0].w};
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          if (m < M) a.Y[(size_t)m * a.N + n] = fv[m] * a.sx[m] + b;
+          if (m < M) a.Y[(size_t)m * a.N + n] = GRP ? fv[m] + b : fv[m] * a.sx[m] + b;
       }
     } else {
 #pragma unroll
@@ -558,7 +645,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = mbase + mg * 16 + 4 * g + e;
-          if (m < M) a.Y[(size_t)m * a.N + n] = fv[e] * a.sx[m] + b;
+          if (m < M) a.Y[(size_t)m * a.N + n] = GRP ? fv[e] + b : fv[e] * a.sx[m] + b;
         }
       }
     }
@@ -574,32 +661,32 @@ void launch_one(Kern kern, dim3 grid, dim3 block, size_t lds, hipStream_t stream
 
 // Grid: row blocks (4R/RG) along x, token chunks along y, column chunks
 // along z.
-template <int BK, int MODE, int MG, int WAVES, int DEPTH, int XMODE, bool PARTIALS, bool INL>
+template <int BK, int MODE, int MG, int WAVES, int DEPTH, int XMODE, bool PARTIALS, bool INL, bool GRP>
 void launch_rg(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL> &args) {
   const dim3 block(WAVES * 64);
   const int y = args.ychunks, z = p.Z;
   switch (p.RG) {
-    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS, INL>, dim3(R, y, z), block, p.lds, stream, args); break;
-    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS, INL>, dim3(R * 2, y, z), block, p.lds, stream, args); break;
-    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS, INL>, dim3(R * 4, y, z), block, p.lds, stream, args); break;
+    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS, INL, GRP>, dim3(R, y, z), block, p.lds, stream, args); break;
+    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS, INL, GRP>, dim3(R * 2, y, z), block, p.lds, stream, args); break;
+    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS, INL, GRP>, dim3(R * 4, y, z), block, p.lds, stream, args); break;
   }
 }
 
-template <int BK, bool PARTIALS, bool INL>
+template <int BK, bool PARTIALS, bool INL, bool GRP>
 void launch_mode(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL> &args) {
   if (p.mode == kValu) {
-    launch_rg<BK, kValu, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL>(p, R, stream, args);
+    launch_rg<BK, kValu, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP>(p, R, stream, args);
     return;
   }
   if (p.xmode == kXPriv) {
-    launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL>(p, R, stream, args);
+    launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP>(p, R, stream, args);
     return;
   }
   switch (p.MG) {
-    case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, PARTIALS, INL>(p, R, stream, args); break;
-    case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, PARTIALS, INL>(p, R, stream, args); break;
-    case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, PARTIALS, INL>(p, R, stream, args); break;
-    default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, PARTIALS, INL>(p, R, stream, args); break;
+    case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, PARTIALS, INL, GRP>(p, R, stream, args); break;
+    case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, PARTIALS, INL, GRP>(p, R, stream, args); break;
+    case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, PARTIALS, INL, GRP>(p, R, stream, args); break;
+    default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, PARTIALS, INL, GRP>(p, R, stream, args); break;
   }
 }
 
@@ -741,7 +828,7 @@ size_t decode_workspace_bytes(const PackedView &w, int M, int split) {
 
 hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx, int M,
                          const float *bias, float *Y, int split, void *ws, int32_t *P,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool grouped) {
   const DecodePlan p = plan_decode(w, M, split);
   if (!decode_plan_ok(p, w) || p.ylaunch < 1) return hipErrorInvalidValue;
   DecodeArgs args;
@@ -752,6 +839,7 @@ hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx,
   args.N = w.N; args.K = w.K; args.R = w.R; args.C = w.C; args.T4 = w.T4; args.T8 = w.T8;
   args.M = M; args.label_words = (w.R * w.C + 31) / 32;
   args.Z = p.Z;
+  args.kg64 = w.K / 64;
   args.xstride = p.xstride;
   args.cnt = nullptr;
   args.part = nullptr;
@@ -766,22 +854,30 @@ hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx,
     static_cast<DecodeArgs &>(la) = args;
     la.M = M - m0 < mstep ? M - m0 : mstep;
     la.qx = qx + (size_t)m0 * w.K;
-    if (sx) la.sx = sx + m0;
+    // grouped scales: one row of K/64 per 16 tokens (launches start on a
+    // multiple of 16 tokens; a single token is its own group)
+    if (sx) la.sx = grouped ? sx + (size_t)(m0 / 16) * (w.K / 64) : sx + m0;
     if (Y) la.Y = Y + (size_t)m0 * w.N;
     if (P) la.P = P + (size_t)m0 * w.N * w.C;
     la.ychunks = p.mode == kValu || p.xmode == kXPriv ? 1 : (la.M + 16 * p.MG - 1) / (16 * p.MG);
-    if (P) {
-      if (w.bK == 128) launch_mode<128, true, false>(p, w.R, stream, la);
-      else launch_mode<64, true, false>(p, w.R, stream, la);
+    if (P && grouped) {
+      if (w.bK == 128) launch_mode<128, true, false, true>(p, w.R, stream, la);
+      else launch_mode<64, true, false, true>(p, w.R, stream, la);
+    } else if (P) {
+      if (w.bK == 128) launch_mode<128, true, false, false>(p, w.R, stream, la);
+      else launch_mode<64, true, false, false>(p, w.R, stream, la);
+    } else if (grouped) {
+      if (w.bK == 128) launch_mode<128, false, false, true>(p, w.R, stream, la);
+      else launch_mode<64, false, false, true>(p, w.R, stream, la);
     } else if (inline_meta(w)) {
       DArgs<true> li;
       static_cast<DecodeArgs &>(li) = la;
       std::memcpy(li.meta, w.meta, sizeof(uint32_t) * kMetaStride * w.R);
-      if (w.bK == 128) launch_mode<128, false, true>(p, w.R, stream, li);
-      else launch_mode<64, false, true>(p, w.R, stream, li);
+      if (w.bK == 128) launch_mode<128, false, true, false>(p, w.R, stream, li);
+      else launch_mode<64, false, true, false>(p, w.R, stream, li);
     } else {
-      if (w.bK == 128) launch_mode<128, false, false>(p, w.R, stream, la);
-      else launch_mode<64, false, false>(p, w.R, stream, la);
+      if (w.bK == 128) launch_mode<128, false, false, false>(p, w.R, stream, la);
+      else launch_mode<64, false, false, false>(p, w.R, stream, la);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

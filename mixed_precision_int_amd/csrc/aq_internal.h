@@ -46,9 +46,13 @@ hipError_t launch_quant_act(const float *X, int M, int K, int8_t *qx, float *sx,
 // (ws, decode_workspace_bytes bytes, counters zero on entry and on exit).
 // split 0 = adaptive.  P != nullptr selects the debug mode that writes
 // INT32 tile products instead (Y and ws unused).
+// grouped: sx holds the App. B.3 activation-group scales ([ceil(M/b_M)][K/64],
+// b_M = 1 for M = 1, else 16) and P, when given, is [M][N][K/64].
 hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx, int M,
                          const float *bias, float *Y, int split, void *ws, int32_t *P,
-                         hipStream_t stream);
+                         hipStream_t stream, bool grouped = false);
+hipError_t launch_quant_act_grouped(const float *X, int M, int K, int8_t *qx, float *sxg,
+                                    hipStream_t stream);
 hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx, int M,
                           const float *bias, float *Y, int32_t *P, hipStream_t stream);
 

@@ -109,6 +109,44 @@ __global__ __launch_bounds__(256) void quant_act_loop_kernel(const float *__rest
   for (int c = threadIdx.x; c < n4; c += 256) out[c] = codes4(row[c], s);
 }
 
+// The pages' grouping (App. B.3): one wave per group of 64 features x BM
+// rows (BM = 1 for a single token, else 16; rows past M are the zero
+// padding, which eq. 6's max(0, .) terms already cover).  Lane l holds
+// feature 64c + l of every row of the group; the group's maximum and minimum
+// are reduced across the wave; the scale is eq. 6 at 8 bits,
+// s = max(max(0, max A) / 127, max(0, -min A) / 128, 1e-12) in FP64, and the
+// codes are eq. 5's clip(rint(x / s), -128, 127) in FP64.
+template <int BM>
+__global__ __launch_bounds__(256) void quant_act_grouped_kernel(const float *__restrict__ X, int M,
+                                                                int K, int8_t *__restrict__ qx,
+                                                                float *__restrict__ sxg) {
+  const int lane = threadIdx.x & 63;
+  const int kg = K >> 6;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);  // feature group (wave-uniform)
+  if (c >= kg) return;
+  const int r0 = blockIdx.y * BM;
+  const int nr = min(BM, M - r0);
+  const size_t col = (size_t)c * 64 + lane;
+  float v[BM];
+  float mx = 0.f, mn = 0.f;  // max(0, max A) and -max(0, -min A)
+#pragma unroll
+  for (int r = 0; r < BM; ++r) {
+    v[r] = r < nr ? X[(size_t)(r0 + r) * K + col] : 0.f;
+    mx = fmaxf(mx, v[r]);
+    mn = fminf(mn, v[r]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+    mn = fminf(mn, __shfl_xor(mn, o));
+  }
+  const double s = fmax(fmax((double)mx / 127.0, -(double)mn / 128.0), 1e-12);
+  if (lane == 0) sxg[(size_t)blockIdx.y * kg + c] = (float)s;
+#pragma unroll
+  for (int r = 0; r < BM; ++r)
+    if (r < nr) qx[(size_t)(r0 + r) * K + col] = (int8_t)(code_of(v[r], s) & 0xFF);
+}
+
 template <int T, int NV>
 hipError_t launch_rows(const float *X, int M, int K, int8_t *qx, float *sx, hipStream_t stream) {
   hipLaunchKernelGGL((quant_act_kernel<T, NV>), dim3(M), dim3(T), 0, stream, X, K, qx, sx);
@@ -155,6 +193,18 @@ hipError_t launch_quant_act(const float *X, int M, int K, int8_t *qx, float *sx,
     if (nv) return launch_t<256>(nv, X, M, K, qx, sx, stream);
   }
   hipLaunchKernelGGL(quant_act_loop_kernel, dim3(M), dim3(256), 0, stream, X, K, qx, sx);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_grouped(const float *X, int M, int K, int8_t *qx, float *sxg,
+                                    hipStream_t stream) {
+  const dim3 block(256);
+  const int gx = (K / 64 + 3) / 4;
+  if (M == 1)
+    hipLaunchKernelGGL(quant_act_grouped_kernel<1>, dim3(gx, 1), block, 0, stream, X, M, K, qx, sxg);
+  else
+    hipLaunchKernelGGL(quant_act_grouped_kernel<16>, dim3(gx, (M + 15) / 16), block, 0, stream, X, M, K,
+                       qx, sxg);
   return hipGetLastError();
 }
 

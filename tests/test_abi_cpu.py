@@ -168,6 +168,26 @@ def test_quant_act_and_partials_rejected(aqlib):
     assert L.aq_linear_tile_partials(ctypes.byref(d), FAKE, 0, 1, FAKE, None, 0, None) == 0
 
 
+def test_grouped_entry_points_rejected(aqlib):
+    """The App. B.3 grouped route validates like the per-token one."""
+    L = B.lib()
+    assert L.aq_quant_act_grouped(FAKE, 4, 100, FAKE, FAKE, None) == -2      # K % 64
+    assert L.aq_quant_act_grouped(FAKE, 0, 128, FAKE, FAKE, None) == 0
+    assert L.aq_quant_act_grouped(None, 4, 128, FAKE, FAKE, None) == -1
+    assert L.aq_quant_act_grouped(FAKE, 4, 128, FAKE + 4, FAKE, None) == -5
+    assert L.aq_quant_act_grouped(FAKE, 16 * 65536, 128, FAKE, FAKE, None) == -2  # row groups > 65535
+    d = fake_packed()
+    dg = lambda **k: L.aq_linear_decode_grouped(ctypes.byref(d), k.get("qx", FAKE), FAKE, k.get("M", 4), None,
+                                                FAKE, k.get("split", 0), None, 0, None)
+    assert dg(M=0) == 0 and dg(qx=None) == -1 and dg(qx=FAKE + 1) == -5
+    assert dg(split=3) == -8
+    assert L.aq_linear_prefill_grouped(ctypes.byref(d), FAKE, None, 4, None, FAKE, None, 0, None) == -1
+    assert L.aq_linear_tile_partials_grouped(ctypes.byref(d), FAKE, 0, FAKE, None) == 0
+    assert L.aq_linear_tile_partials_grouped(ctypes.byref(d), None, 4, FAKE, None) == -1
+    big = fake_packed(N=256, K=65536, T4=4 * 512 - 3, T8=3)
+    assert L.aq_linear_decode_grouped(ctypes.byref(big), FAKE, FAKE, 64, None, FAKE, 0, None, 0, None) == -6
+
+
 def test_pack_rejects_label_mismatch(aqlib):
     lab = O.labels_from_map(np.full((4, 4), 4))                    # 16 INT4 tiles
     d = fake_packed(T4=8, T8=8)
