@@ -75,6 +75,10 @@ def parse():
     ap.add_argument("--split-comparison", action="store_true",
                     help="only time the decode linears of the Llama-3.2-3B shapes with the adaptive "
                          "split and with every fixed split, and print a markdown table")
+    ap.add_argument("--grouped", action="store_true",
+                    help="only time the App. B.3 grouped-activation route (quantization + decode on "
+                         "the Llama-3.2-3B shapes, prefill on the Qwen3-4B shapes) beside the per-token "
+                         "route, and print a markdown table")
     ap.add_argument("--traffic-summary", nargs=4, metavar="CSV",
                     help="print the per-launch HBM traffic summary from four rocprofv3 counter "
                          "CSVs: bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE")
@@ -331,6 +335,52 @@ def split_comparison(aq, torch, dec, ws, reps: int = 48):
     print("\n".join(rows))
 
 
+def grouped_comparison(aq, torch, dec, ws, pre, reps: int = 48):
+    """The pages' activation quantizer (App. B.3 groups) against the per-token
+    route: per call, quantization and linear separately, decode on the 24
+    weight copies (HBM-resident weights), prefill on one copy."""
+    def timed(calls):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(30_000_000)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for f in calls:
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / len(calls)
+
+    rows = ["| call | M | per-token quant µs | per-token linear µs | grouped quant µs | grouped linear µs "
+            "| grouped linear rate |", "|---|---|---|---|---|---|---|"]
+    for proj, copies, xs, bufs in dec:
+        for M in DECODE_M:
+            qx, sx, Y = bufs[M]
+            X = xs[M]
+            qg, sg = aq.aq_quant_act_grouped(X)
+            t = [timed([(lambda: aq.aq_quant_act(X, qx, sx))] * 16),
+                 timed([(lambda c=c: aq.aq_linear_decode(copies[c % N_COPIES], qx, sx, None, 0, Y, ws))
+                        for c in range(reps)]),
+                 timed([(lambda: aq.aq_quant_act_grouped(X, qg, sg))] * 16),
+                 timed([(lambda c=c: aq.aq_linear_decode_grouped(copies[c % N_COPIES], qg, sg, None, 0, Y, ws))
+                        for c in range(reps)])]
+            p = copies[0].plan
+            rate = linear_bytes(p, M) / t[3] / 1e3
+            rows.append(f"| decode {proj} {p.N}x{p.K} | {M} | " + " | ".join(f"{v:.2f}" for v in t)
+                        + f" | {rate:.0f} GB/s |")
+    for proj, pw, x, (qx, sx, Y) in pre:
+        qg, sg = aq.aq_quant_act_grouped(x)
+        pws = torch.empty(max(16, aq.aq_workspace_bytes(pw, PREFILL_M, aq.AQ_PHASE_PREFILL)), dtype=torch.uint8,
+                          device=x.device)
+        t = [timed([(lambda: aq.aq_quant_act(x, qx, sx))] * 4),
+             timed([(lambda: aq.aq_linear_prefill(pw, qx, sx, None, Y, pws))] * 4),
+             timed([(lambda: aq.aq_quant_act_grouped(x, qg, sg))] * 4),
+             timed([(lambda: aq.aq_linear_prefill_grouped(pw, qg, sg, None, Y))] * 4)]
+        ops = 2 * PREFILL_M * pw.plan.N * pw.plan.K
+        rows.append(f"| prefill {proj} {pw.plan.N}x{pw.plan.K} | {PREFILL_M} | " + " | ".join(f"{v:.2f}" for v in t)
+                    + f" | {ops / t[3] / 1e6:.0f} TOPS |")
+    print("\n".join(rows))
+
+
 def main():
     args = parse()
     if args.traffic_summary:
@@ -360,6 +410,9 @@ def main():
     dec, ws, pre = setup(aq, gen, torch)
     if args.split_comparison:
         split_comparison(aq, torch, dec, ws)
+        return
+    if args.grouped:
+        grouped_comparison(aq, torch, dec, ws, pre)
         return
 
     t_host = 0.0
