@@ -52,6 +52,45 @@ def pack_model(geometry, maps, weight_fn, bN: int = 64, bK: int = 128, progress=
     return model
 
 
+@dataclass
+class PackedGroup:
+    """Projections that share one input, packed as one (App. E.4): the
+    members' tile rows are concatenated in member order, so eq. 16's row
+    offsets run over the whole group and one quantization of the shared
+    input and one linear call serve every member.  members[i] = (name, n0,
+    n1): member i owns output features n0 .. n1-1 of the group."""
+    packed: PackedWeights
+    members: list
+
+    def slices(self, Y) -> dict:
+        """The members' outputs: views of the group output Y [M, N]."""
+        return {name: Y[:, n0:n1] for name, n0, n1 in self.members}
+
+
+def pack_group(members, weights, maps, bN: int = 64, bK: int = 128) -> PackedGroup:
+    """Pack input-sharing projections as one (App. E.4 grouping).
+
+    members : member names, in the order their rows are concatenated;
+    weights : device FP32 [N_i, K] per member (same K, N_i a multiple of bN);
+    maps    : [N_i/bN, K/bK] precision maps (4 or 8) per member.
+    """
+    import torch
+    if not members or len(members) != len(weights) or len(weights) != len(maps):
+        raise ValueError("one weight matrix and one map per member")
+    K = weights[0].shape[1]
+    if any(w.shape[1] != K or w.shape[0] % bN for w in weights):
+        raise ValueError("members must share K and have whole tile rows")
+    spans, n0 = [], 0
+    for name, w in zip(members, weights):
+        spans.append((name, n0, n0 + w.shape[0]))
+        n0 += w.shape[0]
+    z = np.concatenate([np.asarray(m, dtype=np.uint8) for m in maps], axis=0)
+    W = torch.cat(list(weights), dim=0)
+    pw = aq_pack_weights(W, aq_labels_from_map(z), bN, bK)
+    del W
+    return PackedGroup(packed=pw, members=spans)
+
+
 def tile_row_slices(pw: PackedWeights, tile_rows) -> dict:
     """Host copies of the packed bytes of the given tile rows, concatenated in
     the given order: the W4 and W8 tiles and their scales occupy one

@@ -170,6 +170,46 @@ def quant_weights(W: np.ndarray, zmap: np.ndarray, bN: int, bK: int):
     return codes, sW
 
 
+def mse_scale(A: np.ndarray, b: int) -> float:
+    """s*_b(A) of App. B.2 eq. 7: over the grid s_i = max((1/4 + i/128)
+    s_0,b(A), 1e-12), i = 0 .. 128, the s_i minimizing ||A - s_i Q_b(A; s_i)||^2,
+    the first such i on equal errors (grid order).  FP64; the squared error
+    is summed element by element in index order, each product and sum
+    rounded on its own (no fused multiply-add), so that the choice is fixed
+    to the last bit."""
+    A64 = np.asarray(A, dtype=np.float64).ravel()
+    s0 = endpoint_scale(A64, b)
+    best_s, best_e = None, None
+    for i in range(129):
+        s = max((0.25 + i / 128) * s0, SCALE_FLOOR)
+        d = A64 - s * quantize(A64, s, b).astype(np.float64)
+        e = float(np.cumsum(d * d)[-1]) if d.size else 0.0
+        if best_e is None or e < best_e:
+            best_s, best_e = s, e
+    return best_s
+
+
+def quant_weights_mse(W: np.ndarray, zmap: np.ndarray, bN: int, bK: int):
+    """Per-tile-row weight quantization with the fitted scale of App. B.2
+    eq. 7 (grid around eq. 6's endpoint scale) in place of the absmax scale:
+    for tile (r, j) of precision b and each row n of it, s = s*_b(W[n, tile
+    cols]), codes Q_b(W[n, tile cols]; s), stored scale FP32(s).  Returns
+    codes int64 [N, K] and sW float32 [N, C]."""
+    N, K = W.shape
+    R, C = tile_grid(N, K, bN, bK)
+    codes = np.zeros((N, K), dtype=np.int64)
+    sW = np.zeros((N, C), dtype=np.float32)
+    for r in range(R):
+        for j in range(C):
+            b = int(zmap[r, j])
+            for n in range(r * bN, (r + 1) * bN):
+                seg = np.asarray(W[n, j * bK:(j + 1) * bK], dtype=np.float64)
+                s = mse_scale(seg, b)
+                codes[n, j * bK:(j + 1) * bK] = quantize(seg, s, b)
+                sW[n, j] = np.float32(s)
+    return codes, sW
+
+
 def quant_act(X: np.ndarray):
     """Per-token INT8 activation quantization: for row m,
     s = max(max_k |X[m,k]| / 127, 1e-12) in FP64, qx = Q_8(X[m]; s), and the
