@@ -79,6 +79,10 @@ def parse():
                     help="only time the App. B.3 grouped-activation route (quantization + decode on "
                          "the Llama-3.2-3B shapes, prefill on the Qwen3-4B shapes) beside the per-token "
                          "route, and print a markdown table")
+    ap.add_argument("--pack-and-group", action="store_true",
+                    help="only time packing with absmax vs fitted (eq. 7) scales, and decode of "
+                         "input-sharing projections called separately vs packed as one group (App. E.4), "
+                         "on 8B-class shapes, and print a markdown table")
     ap.add_argument("--traffic-summary", nargs=4, metavar="CSV",
                     help="print the per-launch HBM traffic summary from four rocprofv3 counter "
                          "CSVs: bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE")
@@ -381,6 +385,66 @@ def grouped_comparison(aq, torch, dec, ws, pre, reps: int = 48):
     print("\n".join(rows))
 
 
+def pack_and_group(aq, gen, torch, reps: int = 24):
+    """Pack time with absmax and with eq. 7 fitted scales; decode of the 8B
+    attention inputs (q 4096, k 1024, v 1024 rows) and MLP inputs (gate, up
+    14336 rows each), K = 4096, called per member or as one packed group
+    (App. E.4), each behind one quantization of the shared input."""
+    from mixed_precision_int_amd.model import pack_group
+    dev = torch.device("cuda", 0)
+
+    def span(fn, n):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(30_000_000)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    rows = ["| projection | absmax pack ms | eq. 7 pack ms |", "|---|---|---|"]
+    for N, K in ((4096, 4096), (28672, 4096), (4096, 14336)):
+        rng = np.random.default_rng(N + K)
+        lab = aq.aq_labels_from_map(gen.map_uniform(rng, N // 64, K // 128, 0.3).astype(np.uint8))
+        W = gen.device_weights(N, K, N + K, device=dev)
+        aq.aq_pack_weights(W, lab, 64, 128)
+        aq.aq_pack_weights(W, lab, 64, 128, mse=True)
+        ta = span(lambda: aq.aq_pack_weights(W, lab, 64, 128), 3) / 1e3
+        tm = span(lambda: aq.aq_pack_weights(W, lab, 64, 128, mse=True), 3) / 1e3
+        rows.append(f"| {N}x{K} | {ta:.2f} | {tm:.2f} |")
+        del W
+    rows += ["", "| group | M | members called one by one µs | one grouped call µs |", "|---|---|---|---|"]
+    for names, Ns in ((("q", "k", "v"), (4096, 1024, 1024)), (("gate", "up"), (14336, 14336))):
+        K = 4096
+        rng = np.random.default_rng(len(names))
+        ws = [gen.device_weights(N, K, 50 + i, device=dev) for i, N in enumerate(Ns)]
+        zs = [gen.map_uniform(rng, N // 64, K // 128, 0.3) for N in Ns]
+        members = [aq.aq_pack_weights(w, aq.aq_labels_from_map(z.astype(np.uint8)), 64, 128) for w, z in zip(ws, zs)]
+        grp = pack_group(list(names), ws, zs)
+        del ws
+        for M in (1, 16):
+            x = gen.device_acts_outliers(M, K, seed=7, device=dev)
+            qx, sx = aq.aq_quant_act(x)
+            outs = [torch.empty((M, pw.N), dtype=torch.float32, device=dev) for pw in members]
+            Yg = torch.empty((M, grp.packed.N), dtype=torch.float32, device=dev)
+
+            def separate():
+                aq.aq_quant_act(x, qx, sx)
+                for pw, Y in zip(members, outs):
+                    aq.aq_linear_decode(pw, qx, sx, None, 0, Y)
+
+            def grouped():
+                aq.aq_quant_act(x, qx, sx)
+                aq.aq_linear_decode(grp.packed, qx, sx, None, 0, Yg)
+
+            separate(); grouped()
+            rows.append(f"| {'/'.join(names)} {'+'.join(map(str, Ns))}x{K} | {M} | {span(separate, reps):.2f} | "
+                        f"{span(grouped, reps):.2f} |")
+    print("\n".join(rows))
+
+
 def main():
     args = parse()
     if args.traffic_summary:
@@ -407,6 +471,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n}))
         return
     aq.lib()
+    if args.pack_and_group:
+        pack_and_group(aq, gen, torch)
+        return
     dec, ws, pre = setup(aq, gen, torch)
     if args.split_comparison:
         split_comparison(aq, torch, dec, ws)

@@ -148,6 +148,17 @@ aq_status aq_plan_pack(int N, int K, int bN, int bK, const uint8_t *labels_host,
  */
 aq_status aq_pack_weights(const float *W, const uint8_t *labels_host, aq_packed *out, void *stream);
 
+/* aq_pack_weights with the fitted scale of App. B.2 eq. 7 in place of the
+ * absmax scale: for each tile row segment A (one output row, b_K columns) of
+ * precision b, with s0 = max(max(0, max A) / (2^(b-1) - 1),
+ * max(0, -min A) / 2^(b-1), 1e-12) (eq. 6), the scale is the first of
+ * s_i = max((1/4 + i/128) s0, 1e-12), i = 0 .. 128, minimizing
+ * sum_k (A_k - s_i Q_b(A_k; s_i))^2; FP64, the sum taken in column order
+ * with each product and sum rounded on its own.  Codes Q_b(A; s), stored
+ * scale FP32(s).  Arguments, layout and errors as aq_pack_weights; the
+ * packed format is the same, so every linear entry point reads it. */
+aq_status aq_pack_weights_mse(const float *W, const uint8_t *labels_host, aq_packed *out, void *stream);
+
 /* Per-token INT8 activation quantization (App. B.3 FP64 preparation, eq. 5
  * rounding): for each row m, s = max(max_k |X[m,k]| / 127, 1e-12) in FP64,
  * qx[m,k] = clip(round_half_even(X[m,k] / s), -128, 127) in FP64,

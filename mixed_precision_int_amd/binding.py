@@ -28,7 +28,7 @@ EXPORTS = ["aq_abi_version", "aq_status_string", "aq_labels_from_map", "aq_plan_
            "aq_pack_weights", "aq_quant_act", "aq_workspace_bytes", "aq_decode_split",
            "aq_linear_decode", "aq_linear_prefill", "aq_linear_tile_partials",
            "aq_quant_act_grouped", "aq_linear_decode_grouped", "aq_linear_prefill_grouped",
-           "aq_linear_tile_partials_grouped"]
+           "aq_linear_tile_partials_grouped", "aq_pack_weights_mse"]
 
 
 class AqError(RuntimeError):
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
         "aq_linear_prefill": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
         "aq_linear_tile_partials": (i32, [ctypes.POINTER(AqPacked), vp, i32, i32, vp, vp, sz, vp]),
         "aq_quant_act_grouped": (i32, [vp, i32, i32, vp, vp, vp]),
+        "aq_pack_weights_mse": (i32, [vp, vp, ctypes.POINTER(AqPacked), vp]),
         "aq_linear_decode_grouped": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp, sz, vp]),
         "aq_linear_prefill_grouped": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
         "aq_linear_tile_partials_grouped": (i32, [ctypes.POINTER(AqPacked), vp, i32, vp, vp]),
@@ -192,14 +193,17 @@ def aq_alloc_packed(plan: AqPlan, labels: np.ndarray, device="cuda") -> PackedWe
                          meta_host=meta, **t)
 
 
-def aq_pack_weights(W, labels: np.ndarray, bN: int = 64, bK: int = 128, stream=None) -> PackedWeights:
-    """Quantize and pack W (device FP32 [N, K]) under the given labels."""
+def aq_pack_weights(W, labels: np.ndarray, bN: int = 64, bK: int = 128, stream=None,
+                    mse: bool = False) -> PackedWeights:
+    """Quantize and pack W (device FP32 [N, K]) under the given labels; with
+    mse=True the weight scales are eq. 7's fitted scales (aq_pack_weights_mse)."""
     N, K = W.shape
     lab = np.ascontiguousarray(labels, dtype=np.uint8)
     plan = aq_plan_pack(N, K, bN, bK, lab)
     pw = aq_alloc_packed(plan, lab, W.device)
-    _check(lib().aq_pack_weights(ctypes.c_void_p(W.data_ptr()), lab.ctypes.data,
-                                 ctypes.byref(pw.desc), _stream(stream)), "aq_pack_weights")
+    fn = lib().aq_pack_weights_mse if mse else lib().aq_pack_weights
+    _check(fn(ctypes.c_void_p(W.data_ptr()), lab.ctypes.data, ctypes.byref(pw.desc), _stream(stream)),
+           "aq_pack_weights_mse" if mse else "aq_pack_weights")
     return pw
 
 

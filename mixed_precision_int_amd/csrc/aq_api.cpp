@@ -136,8 +136,26 @@ aq_status aq_plan_pack(int N, int K, int bN, int bK, const uint8_t *labels, aq_p
   return AQ_OK;
 }
 
+namespace {
+aq_status pack_impl(const float *W, const uint8_t *labels_host, aq_packed *out, void *stream,
+                    bool mse);
+}  // namespace
+
 aq_status aq_pack_weights(const float *W, const uint8_t *labels_host, aq_packed *out,
                           void *stream) {
+  return pack_impl(W, labels_host, out, stream, false);
+}
+
+aq_status aq_pack_weights_mse(const float *W, const uint8_t *labels_host, aq_packed *out,
+                              void *stream) {
+  return pack_impl(W, labels_host, out, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+aq_status pack_impl(const float *W, const uint8_t *labels_host, aq_packed *out, void *stream,
+                    bool mse) {
   if (!W || !labels_host || !out) return AQ_ERR_NULL;
   aq_status st = check_packed(out);
   if (st != AQ_OK) return st;
@@ -188,8 +206,11 @@ aq_status aq_pack_weights(const float *W, const uint8_t *labels_host, aq_packed 
       hipMemcpyAsync(out->row_off8, o8, plan.offs_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)  // host buffers are released on return
     return AQ_ERR_HIP;
-  return aq::launch_pack(W, *out, s) == hipSuccess ? AQ_OK : AQ_ERR_HIP;
+  return aq::launch_pack(W, *out, s, mse) == hipSuccess ? AQ_OK : AQ_ERR_HIP;
 }
+}  // namespace
+
+extern "C" {
 
 aq_status aq_quant_act(const float *X, int M, int K, int8_t *qx, float *sx, void *stream) {
   if (M < 0 || K <= 0 || K % 64) return AQ_ERR_SHAPE;

@@ -37,7 +37,8 @@ inline PackedView view_of(const aq_packed &p) {
 
 // Launchers.  Arguments are already validated; each returns the launch
 // status reported by hipGetLastError().
-hipError_t launch_pack(const float *W, const aq_packed &out, hipStream_t stream);
+// mse: the fitted scale of App. B.2 eq. 7 instead of the absmax scale
+hipError_t launch_pack(const float *W, const aq_packed &out, hipStream_t stream, bool mse = false);
 hipError_t launch_quant_act(const float *X, int M, int K, int8_t *qx, float *sx,
                             hipStream_t stream);
 // Decode: one launch; the input-column splits of each output row group are

@@ -13,7 +13,25 @@
 namespace aq {
 namespace {
 
+constexpr int kGrid = 129;  // App. B.2 eq. 7: candidates i = 0 .. 128
+
+// Eq. 7 squared error of one row segment at scale sc: sum over the columns
+// in index order of (a - sc * Q(a; sc))^2, every product and sum rounded on
+// its own (no fused multiply-add).
 template <int BK>
+__device__ double grid_error(const float *row, double sc, double qmin, double qmax) {
+#pragma clang fp contract(off)
+  double err = 0.0;
+  for (int k = 0; k < BK; ++k) {
+    const double a = (double)row[k];
+    const double qv = fmin(fmax(rint(a / sc), qmin), qmax);
+    const double d = a - sc * qv;
+    err = err + d * d;
+  }
+  return err;
+}
+
+template <int BK, bool MSE>
 __global__ __launch_bounds__(64 * (BK / 32)) void pack_kernel(
     const float *__restrict__ W, int K, int C, int label_words,
     const uint8_t *__restrict__ labels, const int32_t *__restrict__ off4,
@@ -48,7 +66,49 @@ __global__ __launch_bounds__(64 * (BK / 32)) void pack_kernel(
 
   const double qmax = is4 ? 7.0 : 127.0;
   const double qmin = is4 ? -8.0 : -128.0;
-  const double s = fmax((double)amax / qmax, 1e-12);
+  double s = fmax((double)amax / qmax, 1e-12);
+  if constexpr (MSE) {
+    // App. B.2 eq. 7: the row's scale is the first of s_i = max((1/4 + i/128)
+    // s0, 1e-12), i = 0 .. 128, with the least squared error, s0 the endpoint
+    // scale of eq. 6.  The tile is staged in LDS; one thread per (row, i).
+    __shared__ float tv[kTileRows * BK];
+    __shared__ double errs[kTileRows * kGrid];
+    __shared__ double s0v[kTileRows], sst[kTileRows];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) tv[i * BK + q * 32 + e] = v[e];
+    float mx = 0.0f, mn = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      mx = fmaxf(mx, v[e]);
+      mn = fminf(mn, v[e]);
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+      mn = fminf(mn, __shfl_xor(mn, o));
+    }
+    if (q == 0) s0v[i] = fmax(fmax((double)mx / qmax, -(double)mn / -qmin), 1e-12);
+    __syncthreads();
+    for (int p = threadIdx.x; p < kTileRows * kGrid; p += blockDim.x) {
+      const int row = p / kGrid, c = p - row * kGrid;
+      const double sc = fmax((0.25 + c / 128.0) * s0v[row], 1e-12);
+      errs[p] = grid_error<BK>(tv + row * BK, sc, qmin, qmax);
+    }
+    __syncthreads();
+    if (threadIdx.x < kTileRows) {
+      const int row = threadIdx.x;
+      double best = errs[row * kGrid];
+      int bc = 0;
+      for (int c = 1; c < kGrid; ++c)
+        if (errs[row * kGrid + c] < best) {
+          best = errs[row * kGrid + c];
+          bc = c;
+        }
+      sst[row] = fmax((0.25 + bc / 128.0) * s0v[row], 1e-12);
+    }
+    __syncthreads();
+    s = sst[i];
+  }
   int code[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
@@ -92,20 +152,26 @@ __global__ __launch_bounds__(64 * (BK / 32)) void pack_kernel(
   }
 }
 
-}  // namespace
-
-hipError_t launch_pack(const float *W, const aq_packed &out, hipStream_t stream) {
+template <bool MSE>
+void launch_pack_t(const float *W, const aq_packed &out, hipStream_t stream) {
   const int R = out.N / kTileRows, C = out.K / out.bK;
   const int T = R * C;
   const int label_words = (T + 31) / 32;
   if (out.bK == 128)
-    hipLaunchKernelGGL(pack_kernel<128>, dim3(T), dim3(256), 0, stream, W, out.K, C, label_words,
+    hipLaunchKernelGGL((pack_kernel<128, MSE>), dim3(T), dim3(256), 0, stream, W, out.K, C, label_words,
                        out.labels, out.row_off4, out.row_off8, out.w4, out.w8, out.s4, out.s8,
                        out.T4, out.T8);
   else
-    hipLaunchKernelGGL(pack_kernel<64>, dim3(T), dim3(128), 0, stream, W, out.K, C, label_words,
+    hipLaunchKernelGGL((pack_kernel<64, MSE>), dim3(T), dim3(128), 0, stream, W, out.K, C, label_words,
                        out.labels, out.row_off4, out.row_off8, out.w4, out.w8, out.s4, out.s8,
                        out.T4, out.T8);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const float *W, const aq_packed &out, hipStream_t stream, bool mse) {
+  if (mse) launch_pack_t<true>(W, out, stream);
+  else launch_pack_t<false>(W, out, stream);
   return hipGetLastError();
 }
 
