@@ -228,6 +228,105 @@ def quant_act(X: np.ndarray):
 
 
 # --------------------------------------------------------------------------
+# Tile-aligned orthogonal transforms (App. B.1, eq. 4)
+# --------------------------------------------------------------------------
+#
+# Phi_-1 = I, Phi_0 = H_64 (the normalized 64-point Hadamard matrix, entries
+# +-1/8), Phi_s = D_L,s P_s H_64 D_R,s for s = 1 .. 6, with P_s a permutation
+# and D_L,s, D_R,s diagonal sign matrices.  The pages do not say how P_s and
+# the signs follow from s; here they are inputs, `tables` = (perm, dl, dr)
+# with perm[s-1] a permutation of 0..63 ((P v)_i = v[perm[i]]) and dl[s-1],
+# dr[s-1] vectors of +-1.  V = diag(Phi_{v_c}) over 64-feature blocks and
+# U = diag(Phi_{u_r}^T) over 64-row output tile rows.
+
+TB = 64  # transform block (the pages' 64 x 64 configuration)
+
+
+def hadamard64() -> np.ndarray:
+    """H_64 in Sylvester (natural) order, normalized: entries +-1/8, FP64."""
+    H = np.array([[1.0]])
+    while H.shape[0] < TB:
+        H = np.block([[H, H], [H, -H]])
+    return H / 8.0
+
+
+def phi(s: int, tables) -> np.ndarray:
+    """The seeded 64 x 64 transform Phi_s of App. B.1, FP64."""
+    if s == -1:
+        return np.eye(TB)
+    if s == 0:
+        return hadamard64()
+    perm, dl, dr = tables
+    P = np.eye(TB)[np.asarray(perm[s - 1])]
+    return np.diag(np.asarray(dl[s - 1], np.float64)) @ P @ hadamard64() @ np.diag(np.asarray(dr[s - 1], np.float64))
+
+
+def fwht64_f32(v: np.ndarray) -> np.ndarray:
+    """H_64 v in FP32, by the in-place butterflies in order h = 1, 2, 4, ...,
+    32 ((a_i, a_i+h) -> (a_i + a_i+h, a_i - a_i+h) for i with bit h clear),
+    then the exact scaling by 1/8: the evaluation order both sides use so
+    that transformed values are identical to the last bit.  Acts on the
+    last axis."""
+    a = np.array(v, dtype=np.float32, copy=True)
+    h = 1
+    while h < TB:
+        idx = np.arange(TB)
+        lo = idx[(idx & h) == 0]
+        x, y = a[..., lo].copy(), a[..., lo + h].copy()
+        a[..., lo] = x + y
+        a[..., lo + h] = x - y
+        h *= 2
+    return a * np.float32(0.125)
+
+
+def phi_t_f32(v: np.ndarray, s: int, tables) -> np.ndarray:
+    """Phi_s^T v in FP32 along the last axis: D_R H (P^T (D_L v)); the sign
+    flips, the permutation and the 1/8 are exact, only the butterflies
+    round."""
+    v = np.asarray(v, dtype=np.float32)
+    if s == -1:
+        return v.copy()
+    if s == 0:
+        return fwht64_f32(v)
+    perm, dl, dr = tables
+    u = v * np.asarray(dl[s - 1], np.float32)
+    w = np.empty_like(u)
+    w[..., np.asarray(perm[s - 1])] = u            # P^T: w[perm[i]] = u[i]
+    return fwht64_f32(w) * np.asarray(dr[s - 1], np.float32)
+
+
+def transform_rows(X: np.ndarray, seeds, tables) -> np.ndarray:
+    """X~ = X V (App. B.1): every 64-feature block c of every row becomes
+    Phi_{v_c}^T x (x as a column), FP32."""
+    X = np.asarray(X, dtype=np.float32)
+    out = np.empty_like(X)
+    for c, sd in enumerate(seeds):
+        out[..., TB * c:TB * (c + 1)] = phi_t_f32(X[..., TB * c:TB * (c + 1)], int(sd), tables)
+    return out
+
+
+def transform_weights(W: np.ndarray, useeds, vseeds, tables) -> np.ndarray:
+    """W~ = U W V (App. B.1), FP32: first each row's 64-feature blocks
+    (W V), then each 64-row tile row's columns by U_r = Phi_{u_r}^T."""
+    Wv = transform_rows(W, vseeds, tables)
+    out = np.empty_like(Wv)
+    for r, sd in enumerate(useeds):
+        blk = Wv[TB * r:TB * (r + 1), :]                       # [64, K]
+        out[TB * r:TB * (r + 1), :] = phi_t_f32(blk.T, int(sd), tables).T
+    return out
+
+
+def transform_out(Yt: np.ndarray, useeds, tables) -> np.ndarray:
+    """Y = Y~ U (App. B.1 eq. 4), FP64: every 64-feature output block r of
+    every row becomes Phi_{u_r} y~ (U_r = Phi_{u_r}^T acting on row vectors)."""
+    Yt = np.asarray(Yt, dtype=np.float64)
+    out = np.empty_like(Yt)
+    for r, sd in enumerate(useeds):
+        out[:, TB * r:TB * (r + 1)] = Yt[:, TB * r:TB * (r + 1)] @ phi(int(sd), tables).T
+    return out
+
+
+# --------------------------------------------------------------------------
 # The pages' activation quantizer (App. B.3 with App. B.2 eq. 5-6)
 # --------------------------------------------------------------------------
 

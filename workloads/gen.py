@@ -136,6 +136,22 @@ def acts_heavy_tail(rng: np.random.Generator, M: int, K: int, frac: float = 0.05
 
 # ---------------------------------------------------------------- workloads
 
+def transform_tables(seed: int = 6000):
+    """The six signed permutations of the seeded block transforms: perm
+    uint8 [6, 64] (each row a permutation of 0..63), dl and dr int8 [6, 64]
+    of +-1.  Random draws only; what they mean is defined by the consumers."""
+    rng = np.random.default_rng(seed)
+    perm = np.stack([rng.permutation(64) for _ in range(6)]).astype(np.uint8)
+    dl = rng.choice(np.array([-1, 1], dtype=np.int8), size=(6, 64))
+    dr = rng.choice(np.array([-1, 1], dtype=np.int8), size=(6, 64))
+    return perm, dl, dr
+
+
+def transform_seeds(rng: np.random.Generator, n: int) -> np.ndarray:
+    """n block seeds drawn uniformly from -1 .. 6 (int8)."""
+    return rng.integers(-1, 7, size=n).astype(np.int8)
+
+
 def small(seed: int = 1000) -> dict:
     """One 256x512 linear, 16 tiles of 64x128, 8 INT8 / 8 INT4, M = 4."""
     rng = np.random.default_rng(seed)
