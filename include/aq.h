@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AQ_ABI_VERSION 4
+#define AQ_ABI_VERSION 5
 
 typedef enum aq_status {
   AQ_OK = 0,
@@ -284,6 +284,61 @@ aq_status aq_linear_prefill_grouped(const aq_packed *W, const int8_t *qx, const 
  * as INT32 [M][N][K/64] row-major by the grouped decode kernels. */
 aq_status aq_linear_tile_partials_grouped(const aq_packed *W, const int8_t *qx, int M, int32_t *P,
                                           void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Tile-aligned orthogonal transforms (App. B.1, eq. 4).
+ *
+ * Each 64-block transform is Phi_s, s in -1 .. 6: Phi_-1 = I, Phi_0 = H_64
+ * (Sylvester order, entries +-1/8), and for s >= 1 the signed permutation
+ * Phi_s = D_L,s P_s H_64 D_R,s with (P_s v)_i = v[perm[s-1][i]] and the
+ * diagonals dl[s-1], dr[s-1] of +-1.  The pages fix the form, not P_s and
+ * the signs, so the caller supplies them.  The activation transform
+ * V = diag(Phi_{v_c}) acts on 64-feature blocks c; the output transform
+ * U = diag(Phi_{u_r}^T) on 64-row output tile rows r.  The transformed layer
+ * is W~ = U W V, X~ = X V, and Y = Y~ U recovers the output.
+ *
+ * FP32 evaluation order (X~ and W~ feed quantizers, so it is fixed): signs
+ * and the permutation are exact; H_64 is six in-place butterfly stages,
+ * h = 1, 2, 4, .., 32, (a_i, a_i+h) -> (a_i + a_i+h, a_i - a_i+h) for each
+ * i with bit h clear, then the exact factor 1/8.
+ *
+ * Seeds are device INT8 arrays; a seed outside -1 .. 6 turns the block(s) it
+ * governs into NaN.  The tables are read on the host at the call and
+ * checked: every perm row a permutation of 0 .. 63, every sign +-1, else
+ * AQ_ERR_ARG (NULL tables: AQ_ERR_NULL).  They are copied into the launch,
+ * so the host memory may be reused as soon as the call returns.
+ * ------------------------------------------------------------------------- */
+#define AQ_TRANSFORM_SEEDS 6
+typedef struct aq_transform_tables {
+  uint8_t perm[AQ_TRANSFORM_SEEDS][64];
+  int8_t dl[AQ_TRANSFORM_SEEDS][64];
+  int8_t dr[AQ_TRANSFORM_SEEDS][64];
+} aq_transform_tables;
+
+/* X~ = X V: every 64-feature block c of every row x becomes Phi_{v_c}^T x.
+ *   X, Xt    device FP32 [M][K], K a multiple of 64; Xt == X is allowed
+ *   vseeds   device INT8 [K/64]
+ * M == 0 is a no-op. */
+aq_status aq_transform_rows(const float *X, int M, int K, const int8_t *vseeds,
+                            const aq_transform_tables *tables_host, float *Xt, void *stream);
+
+/* Y = Y~ U: every 64-feature block r of every output row y~ becomes
+ * Phi_{u_r} y~ (eq. 4).
+ *   Yt, Y    device FP32 [M][N], N a multiple of 64; Y == Yt is allowed
+ *   useeds   device INT8 [N/64]
+ * M == 0 is a no-op. */
+aq_status aq_transform_out(const float *Yt, int M, int N, const int8_t *useeds,
+                           const aq_transform_tables *tables_host, float *Y, void *stream);
+
+/* W~ = U W V: first each row's 64-feature blocks by Phi_{v_c}^T (as
+ * aq_transform_rows), then the 64 rows of each output tile row r, column by
+ * column, by U_r = Phi_{u_r}^T.
+ *   W, Wt    device FP32 [N][K], N and K multiples of 64; Wt must not
+ *            overlap W
+ *   useeds   device INT8 [N/64];  vseeds device INT8 [K/64] */
+aq_status aq_transform_weights(const float *W, int N, int K, const int8_t *useeds,
+                               const int8_t *vseeds, const aq_transform_tables *tables_host,
+                               float *Wt, void *stream);
 
 #ifdef __cplusplus
 }

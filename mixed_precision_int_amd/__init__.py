@@ -28,6 +28,11 @@ from .binding import (  # noqa: F401
     aq_pack_weights,
     aq_plan_pack,
     aq_quant_act,
+    aq_transform_out,
+    aq_transform_rows,
+    aq_transform_weights,
     aq_workspace_bytes,
+    AqTransformTables,
     lib,
+    transform_tables,
 )

@@ -28,7 +28,8 @@ EXPORTS = ["aq_abi_version", "aq_status_string", "aq_labels_from_map", "aq_plan_
            "aq_pack_weights", "aq_quant_act", "aq_workspace_bytes", "aq_decode_split",
            "aq_linear_decode", "aq_linear_prefill", "aq_linear_tile_partials",
            "aq_quant_act_grouped", "aq_linear_decode_grouped", "aq_linear_prefill_grouped",
-           "aq_linear_tile_partials_grouped", "aq_pack_weights_mse"]
+           "aq_linear_tile_partials_grouped", "aq_pack_weights_mse",
+           "aq_transform_rows", "aq_transform_out", "aq_transform_weights"]
 
 
 class AqError(RuntimeError):
@@ -54,6 +55,11 @@ class AqPacked(ctypes.Structure):
                 ("labels", ctypes.c_void_p), ("row_off4", ctypes.c_void_p),
                 ("row_off8", ctypes.c_void_p), ("w4", ctypes.c_void_p), ("w8", ctypes.c_void_p),
                 ("s4", ctypes.c_void_p), ("s8", ctypes.c_void_p), ("meta_host", ctypes.c_void_p)]
+
+
+class AqTransformTables(ctypes.Structure):
+    _fields_ = [("perm", (ctypes.c_uint8 * 64) * 6), ("dl", (ctypes.c_int8 * 64) * 6),
+                ("dr", (ctypes.c_int8 * 64) * 6)]
 
 
 _LIB = None
@@ -90,6 +96,9 @@ def lib() -> ctypes.CDLL:
         "aq_linear_decode_grouped": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp, sz, vp]),
         "aq_linear_prefill_grouped": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
         "aq_linear_tile_partials_grouped": (i32, [ctypes.POINTER(AqPacked), vp, i32, vp, vp]),
+        "aq_transform_rows": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
+        "aq_transform_out": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
+        "aq_transform_weights": (i32, [vp, i32, i32, vp, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -366,4 +375,92 @@ def aq_linear_tile_partials_grouped(pw: PackedWeights, qx, out=None, stream=None
         out = torch.empty((M, pw.N, pw.K // 64), dtype=torch.int32, device=qx.device)
     _check(lib().aq_linear_tile_partials_grouped(ctypes.byref(pw.desc), _ptr(qx), M, _ptr(out),
                                                  _stream(stream)), "aq_linear_tile_partials_grouped")
+    return out
+
+
+# ------------------------------------------------ block transforms (App. B.1)
+
+def transform_tables(perm, dl, dr) -> AqTransformTables:
+    """The six signed permutations (perm uint8 [6, 64], dl / dr int8 [6, 64]
+    of +-1) as the C struct the transform calls read."""
+    t = AqTransformTables()
+    perm = np.ascontiguousarray(perm, dtype=np.uint8).reshape(6, 64)
+    dl = np.ascontiguousarray(dl, dtype=np.int8).reshape(6, 64)
+    dr = np.ascontiguousarray(dr, dtype=np.int8).reshape(6, 64)
+    ctypes.memmove(ctypes.addressof(t.perm), perm.ctypes.data, perm.nbytes)
+    ctypes.memmove(ctypes.addressof(t.dl), dl.ctypes.data, dl.nbytes)
+    ctypes.memmove(ctypes.addressof(t.dr), dr.ctypes.data, dr.nbytes)
+    return t
+
+
+def _seeds_dev(seeds, n: int, device):
+    """The n block seeds as a device INT8 tensor (the C calls read n)."""
+    import torch
+    if isinstance(seeds, torch.Tensor):
+        if not (seeds.dtype == torch.int8 and seeds.is_contiguous() and seeds.device.type == "cuda"):
+            raise ValueError("seeds must be a contiguous int8 device tensor")
+    else:
+        seeds = torch.as_tensor(np.asarray(seeds, dtype=np.int8)).to(device)
+    if seeds.numel() != n:
+        raise ValueError(f"expected {n} block seeds, got {seeds.numel()}")
+    return seeds
+
+
+def _check_f32(t, shape, what):
+    import torch
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must be a contiguous float32 tensor of shape {tuple(shape)}")
+
+
+def _tables(tables) -> AqTransformTables:
+    return tables if isinstance(tables, AqTransformTables) else transform_tables(*tables)
+
+
+def aq_transform_rows(X, vseeds, tables, out=None, stream=None):
+    """X~ = X V (FP32 [M, K] on the device); vseeds: K/64 seeds in -1..6."""
+    import torch
+    M, K = X.shape
+    if out is None:
+        out = torch.empty_like(X)
+    _check_f32(X, (M, K), "X")
+    _check_f32(out, (M, K), "out")
+    sd = _seeds_dev(vseeds, K // 64, X.device)
+    t = _tables(tables)
+    _check(lib().aq_transform_rows(ctypes.c_void_p(X.data_ptr()), M, K, ctypes.c_void_p(sd.data_ptr()),
+                                   ctypes.byref(t), ctypes.c_void_p(out.data_ptr()), _stream(stream)),
+           "aq_transform_rows")
+    return out
+
+
+def aq_transform_out(Yt, useeds, tables, out=None, stream=None):
+    """Y = Y~ U (FP32 [M, N] on the device; out=Yt transforms in place)."""
+    import torch
+    M, N = Yt.shape
+    if out is None:
+        out = torch.empty_like(Yt)
+    _check_f32(Yt, (M, N), "Yt")
+    _check_f32(out, (M, N), "out")
+    sd = _seeds_dev(useeds, N // 64, Yt.device)
+    t = _tables(tables)
+    _check(lib().aq_transform_out(ctypes.c_void_p(Yt.data_ptr()), M, N, ctypes.c_void_p(sd.data_ptr()),
+                                  ctypes.byref(t), ctypes.c_void_p(out.data_ptr()), _stream(stream)),
+           "aq_transform_out")
+    return out
+
+
+def aq_transform_weights(W, useeds, vseeds, tables, out=None, stream=None):
+    """W~ = U W V (FP32 [N, K] on the device)."""
+    import torch
+    N, K = W.shape
+    if out is None:
+        out = torch.empty_like(W)
+    _check_f32(W, (N, K), "W")
+    _check_f32(out, (N, K), "out")
+    su = _seeds_dev(useeds, N // 64, W.device)
+    sv = _seeds_dev(vseeds, K // 64, W.device)
+    t = _tables(tables)
+    _check(lib().aq_transform_weights(ctypes.c_void_p(W.data_ptr()), N, K, ctypes.c_void_p(su.data_ptr()),
+                                      ctypes.c_void_p(sv.data_ptr()), ctypes.byref(t),
+                                      ctypes.c_void_p(out.data_ptr()), _stream(stream)),
+           "aq_transform_weights")
     return out

@@ -349,3 +349,71 @@ aq_status aq_linear_tile_partials(const aq_packed *W, const int8_t *qx, int M, i
 }
 
 }  // extern "C"
+
+namespace {
+
+// Tables of App. B.1's signed permutations: rows of perm are permutations
+// of 0..63, signs are +-1.
+aq_status check_tables(const aq_transform_tables *t) {
+  if (!t) return AQ_ERR_NULL;
+  for (int s = 0; s < AQ_TRANSFORM_SEEDS; ++s) {
+    uint64_t seen = 0;
+    for (int l = 0; l < 64; ++l) {
+      if (t->perm[s][l] >= 64) return AQ_ERR_ARG;
+      seen |= 1ull << t->perm[s][l];
+      if ((t->dl[s][l] != 1 && t->dl[s][l] != -1) || (t->dr[s][l] != 1 && t->dr[s][l] != -1))
+        return AQ_ERR_ARG;
+    }
+    if (seen != ~0ull) return AQ_ERR_ARG;
+  }
+  return AQ_OK;
+}
+
+aq_status run_row_transform(int kind, const float *src, int M, int K, const int8_t *seeds,
+                            const aq_transform_tables *t, float *dst, void *stream) {
+  if (M < 0 || K <= 0 || K % 64) return AQ_ERR_SHAPE;
+  if (M == 0) return AQ_OK;
+  if (!src || !dst || !seeds) return AQ_ERR_NULL;
+  aq_status st = check_tables(t);
+  if (st != AQ_OK) return st;
+  if (!aligned16(src) || !aligned16(dst)) return AQ_ERR_ALIGN;
+  if ((long long)M * K > (1LL << 40)) return AQ_ERR_SHAPE;
+  return aq::launch_transform(kind, src, dst, M, K, seeds, nullptr, *t,
+                              static_cast<hipStream_t>(stream)) == hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+aq_status aq_transform_rows(const float *X, int M, int K, const int8_t *vseeds,
+                            const aq_transform_tables *tables_host, float *Xt, void *stream) {
+  return run_row_transform(aq::kTransformRows, X, M, K, vseeds, tables_host, Xt, stream);
+}
+
+aq_status aq_transform_out(const float *Yt, int M, int N, const int8_t *useeds,
+                           const aq_transform_tables *tables_host, float *Y, void *stream) {
+  return run_row_transform(aq::kTransformOut, Yt, M, N, useeds, tables_host, Y, stream);
+}
+
+aq_status aq_transform_weights(const float *W, int N, int K, const int8_t *useeds,
+                               const int8_t *vseeds, const aq_transform_tables *tables_host,
+                               float *Wt, void *stream) {
+  if (N <= 0 || K <= 0 || N % 64 || K % 64) return AQ_ERR_SHAPE;
+  if (!W || !Wt || !useeds || !vseeds) return AQ_ERR_NULL;
+  aq_status st = check_tables(tables_host);
+  if (st != AQ_OK) return st;
+  if (!aligned16(W) || !aligned16(Wt)) return AQ_ERR_ALIGN;
+  if ((long long)N * K > (1LL << 40) || N / 64 > 65535) return AQ_ERR_SHAPE;
+  const uintptr_t w0 = reinterpret_cast<uintptr_t>(W), t0 = reinterpret_cast<uintptr_t>(Wt);
+  const uintptr_t bytes = (uintptr_t)N * K * sizeof(float);
+  if (w0 < t0 + bytes && t0 < w0 + bytes) return AQ_ERR_ARG;
+  return aq::launch_transform(aq::kTransformWeights, W, Wt, N, K, vseeds, useeds, *tables_host,
+                              static_cast<hipStream_t>(stream)) == hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -114,4 +114,13 @@ int decode_split(const PackedView &w, int M);
 bool decode_split_supported(const PackedView &w, int M, int S);
 size_t decode_workspace_bytes(const PackedView &w, int M, int split);
 
+// Block transforms of App. B.1 (kind: rows = X V, out = Y~ U, weights =
+// U W V); seeds2 is the per-tile-row seed array of the weight transform.
+using TransformTables = aq_transform_tables;
+constexpr int kTransformSeeds = AQ_TRANSFORM_SEEDS;
+enum { kTransformRows = 0, kTransformOut = 1, kTransformWeights = 2 };
+hipError_t launch_transform(int kind, const float *src, float *dst, int rows, int cols,
+                            const int8_t *seeds, const int8_t *seeds2, const TransformTables &t,
+                            hipStream_t stream);
+
 }  // namespace aq

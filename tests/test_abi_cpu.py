@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(aqlib):
 
 
 def test_abi_version_and_status_strings(aqlib):
-    assert B.aq_abi_version() == 4
+    assert B.aq_abi_version() == 5
     for code in list(B.STATUS) + [-99]:
         assert aqlib.aq_status_string(code)
 
@@ -201,3 +201,34 @@ def test_adaptive_split_bounds(aqlib):
         d = fake_packed(N=N, K=K, T4=R * C, T8=0)
         S = B.lib().aq_decode_split(ctypes.byref(d), 1)
         assert S in (4, 8, 16)
+
+
+def test_transform_entry_points_rejected(aqlib):
+    """App. B.1 transforms: shapes, pointers, alignment and the signed
+    permutation tables are checked on the host before any launch."""
+    from workloads import gen
+    L = B.lib()
+    perm, dl, dr = gen.transform_tables()
+    t = B.transform_tables(perm, dl, dr)
+    T = ctypes.byref(t)
+    assert L.aq_transform_rows(FAKE, 4, 100, FAKE, T, FAKE, None) == -2          # K % 64
+    assert L.aq_transform_rows(FAKE, 0, 128, FAKE, T, FAKE, None) == 0
+    assert L.aq_transform_rows(FAKE, 4, 128, None, T, FAKE, None) == -1
+    assert L.aq_transform_rows(FAKE, 4, 128, FAKE, None, FAKE, None) == -1
+    assert L.aq_transform_rows(FAKE + 4, 4, 128, FAKE, T, FAKE, None) == -5
+    assert L.aq_transform_out(FAKE, -1, 128, FAKE, T, FAKE, None) == -2
+    assert L.aq_transform_weights(FAKE, 100, 128, FAKE, FAKE, T, FAKE + (1 << 20), None) == -2
+    assert L.aq_transform_weights(FAKE, 64, 128, FAKE, FAKE, T, FAKE + 64 * 128, None) == -8  # overlap
+    assert L.aq_transform_weights(FAKE, 64, 128, None, FAKE, T, FAKE + (1 << 20), None) == -1
+    bad = perm.copy()
+    bad[3, 5] = bad[3, 6]                      # not a permutation
+    assert L.aq_transform_rows(FAKE, 4, 128, FAKE, ctypes.byref(B.transform_tables(bad, dl, dr)),
+                               FAKE, None) == -8
+    bad = perm.copy()
+    bad[0, 0] = 64
+    assert L.aq_transform_rows(FAKE, 4, 128, FAKE, ctypes.byref(B.transform_tables(bad, dl, dr)),
+                               FAKE, None) == -8
+    bads = dr.copy()
+    bads[5, 63] = 0                            # a sign must be +-1
+    assert L.aq_transform_out(FAKE, 4, 128, FAKE, ctypes.byref(B.transform_tables(perm, dl, bads)),
+                              FAKE, None) == -8

@@ -1,0 +1,165 @@
+"""GPU parity of the tile-aligned block transforms (App. B.1, eq. 4) through
+the C ABI, against the oracle.  X~ = X V and W~ = U W V feed quantizers, so
+both follow one fixed FP32 evaluation order and must match the oracle to
+the last bit; Y = Y~ U is compared with the oracle's FP64 product within the
+FP32 error of six butterfly stages: per 64-block, |error|_2 <= 3e-6 |y~|_2
+(6 roundings of relative size 2^-24 on values whose 2-norm the orthonormal
+stages preserve, with margin).  The transformed linear runs the untouched
+decode / prefill kernels on transformed operands; its codes, scales and
+outputs meet the bar of the untransformed path."""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_int_amd as aq
+from oracle import aq_oracle as O
+from tests.parity import assert_output_close, say, to_dev
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+TABLES = gen.transform_tables()
+
+
+def bits(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def assert_bits_equal(got, ref, name):
+    bad = np.argwhere(bits(got) != bits(ref))
+    assert bad.size == 0, f"{name}: {len(bad)} values differ, first {bad[:4].tolist()}"
+
+
+def assert_blocks_close(got, ref, name, rel=3e-6):
+    M, N = ref.shape
+    g = np.asarray(got, np.float64).reshape(M, N // 64, 64)
+    r = np.asarray(ref, np.float64).reshape(M, N // 64, 64)
+    err = np.linalg.norm(g - r, axis=-1)
+    bound = rel * np.linalg.norm(r, axis=-1) + 1e-30
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, f"{name}: {len(bad)} blocks off, first {bad[:4].tolist()}"
+
+
+def every_seed(rng, n):
+    """n seeds covering all of -1 .. 6 when n >= 8, the rest drawn."""
+    s = gen.transform_seeds(rng, n)
+    s[:min(n, 8)] = np.arange(-1, 7)[:min(n, 8)]
+    return s
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (5, 512), (33, 1088), (64, 4096), (3, 14336)])
+def test_transform_rows_bit_exact(M, K):
+    """X~ = X V over every seed, ragged workgroup tails (1088 = 17 blocks)."""
+    rng = np.random.default_rng(7 * M + K)
+    X = gen.acts_outliers(rng, M, K, max(1, K // 200), 25.0)
+    vs = every_seed(rng, K // 64)
+    say(f"  transform_rows M={M} K={K}")
+    Xt = aq.aq_transform_rows(to_dev(X), vs, TABLES)
+    torch.cuda.synchronize()
+    assert_bits_equal(Xt.cpu().numpy(), O.transform_rows(X, vs, TABLES), f"rows M{M} K{K}")
+    # in place gives the same bits
+    Xd = to_dev(X)
+    aq.aq_transform_rows(Xd, vs, TABLES, out=Xd)
+    torch.cuda.synchronize()
+    assert_bits_equal(Xd.cpu().numpy(), Xt.cpu().numpy(), f"rows in place M{M} K{K}")
+
+
+@pytest.mark.parametrize("N,K", [(64, 64), (192, 320), (512, 1024), (4096, 4096)])
+def test_transform_weights_bit_exact(N, K):
+    """W~ = U W V: row blocks, then the columns of every output tile row."""
+    rng = np.random.default_rng(N + 3 * K)
+    W = gen.weights(rng, N, K)
+    us, vs = every_seed(rng, N // 64), every_seed(rng, K // 64)
+    say(f"  transform_weights N={N} K={K}")
+    Wt = aq.aq_transform_weights(to_dev(W), us, vs, TABLES)
+    torch.cuda.synchronize()
+    assert_bits_equal(Wt.cpu().numpy(), O.transform_weights(W, us, vs, TABLES), f"weights N{N} K{K}")
+
+
+@pytest.mark.parametrize("M,N", [(1, 64), (4, 576), (37, 4096), (1024, 1024)])
+def test_transform_out_close(M, N):
+    """Y = Y~ U against the FP64 product, in place and out of place."""
+    rng = np.random.default_rng(11 * M + N)
+    Yt = (rng.standard_normal((M, N)) * rng.uniform(0.1, 30.0, size=(M, 1))).astype(np.float32)
+    us = every_seed(rng, N // 64)
+    ref = O.transform_out(Yt, us, TABLES)
+    say(f"  transform_out M={M} N={N}")
+    Y = aq.aq_transform_out(to_dev(Yt), us, TABLES)
+    Yd = to_dev(Yt)
+    aq.aq_transform_out(Yd, us, TABLES, out=Yd)
+    torch.cuda.synchronize()
+    assert_blocks_close(Y.cpu().numpy(), ref, f"out M{M} N{N}")
+    assert_bits_equal(Yd.cpu().numpy(), Y.cpu().numpy(), f"out in place M{M} N{N}")
+
+
+def test_transform_round_trip():
+    """Phi_s applied after Phi_s^T returns the input up to FP32 rounding (the
+    transforms are orthogonal)."""
+    rng = np.random.default_rng(5)
+    X = gen.acts_outliers(rng, 8, 1024, 10, 20.0)
+    s = every_seed(rng, 16)
+    back = aq.aq_transform_out(aq.aq_transform_rows(to_dev(X), s, TABLES), s, TABLES)
+    torch.cuda.synchronize()
+    assert_blocks_close(back.cpu().numpy(), X.astype(np.float64), "round trip", rel=6e-6)
+
+
+def test_transform_bad_seed_gives_nan():
+    """A seed outside -1 .. 6 is not a transform: its block comes out NaN and
+    the others are untouched."""
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((3, 256)).astype(np.float32)
+    s = np.array([0, 7, -1, -2], np.int8)
+    Xt = aq.aq_transform_rows(to_dev(X), s, TABLES).cpu().numpy()
+    assert np.isnan(Xt[:, 64:128]).all() and np.isnan(Xt[:, 192:]).all()
+    ok = np.array([0, -1, -1, -1], np.int8)
+    ref = O.transform_rows(X, ok, TABLES)
+    assert_bits_equal(Xt[:, :64], ref[:, :64], "seed 0 block")
+    assert_bits_equal(Xt[:, 128:192], ref[:, 128:192], "identity block")
+    W = gen.weights(rng, 128, 128)
+    Wt = aq.aq_transform_weights(to_dev(W), np.array([1, 9], np.int8), np.array([2, 3], np.int8),
+                                 TABLES).cpu().numpy()
+    assert not np.isnan(Wt[:64]).any() and np.isnan(Wt[64:]).all()
+
+
+@pytest.mark.parametrize("N,K,bK,M", [(256, 1024, 128, 1), (192, 768, 128, 16), (256, 512, 64, 37),
+                                      (320, 2560, 128, 1030)])
+def test_transformed_linear(N, K, bK, M):
+    """The transformed layer end to end (App. B.1): W~ = U W V packed with the
+    App. E map, X~ = X V quantized per token, the decode (or long prefill)
+    kernels give Y~, and Y = Y~ U.  Every integer stage bit-exact with the
+    oracle on the oracle's own transformed operands; Y~ within the linear's
+    bar; Y within the transform's bound of the oracle's Y~ U of the GPU Y~;
+    and Y close to X W^T where quantization error allows (orthogonality)."""
+    rng = np.random.default_rng(N + K + M)
+    W = gen.weights(rng, N, K)
+    X = gen.acts_outliers(rng, M, K, max(1, K // 100), 25.0)
+    R, C = N // 64, K // bK
+    z = gen.map_uniform(rng, R, C, 0.35)
+    us, vs = every_seed(rng, R), every_seed(rng, K // 64)
+    name = f"transformed{N}x{K}/bK{bK}/M{M}"
+    say(f"[{name}]")
+    # oracle
+    Wt_r = O.transform_weights(W, us, vs, TABLES)
+    Xt_r = O.transform_rows(X, vs, TABLES)
+    codes, sW = O.quant_weights(Wt_r, z, 64, bK)
+    qx_r, sx_r = O.quant_act(Xt_r)
+    P_r = O.tile_partials(qx_r, codes, bK)
+    yt_r = O.linear_from_partials(P_r, sx_r, sW)
+    # HIP path
+    Wt = aq.aq_transform_weights(to_dev(W), us, vs, TABLES)
+    pw = aq.aq_pack_weights(Wt, aq.aq_labels_from_map(z.astype(np.uint8)), 64, bK)
+    Xt = aq.aq_transform_rows(to_dev(X), vs, TABLES)
+    qx, sx = aq.aq_quant_act(Xt)
+    Yt = aq.aq_linear_decode(pw, qx, sx) if M < 1024 else aq.aq_linear_prefill(pw, qx, sx)
+    Y = aq.aq_transform_out(Yt, us, TABLES)
+    torch.cuda.synchronize()
+    assert_bits_equal(Wt.cpu().numpy(), Wt_r, f"{name}: W~")
+    assert np.array_equal(qx.cpu().numpy().astype(np.int64), qx_r), f"{name}: codes differ"
+    assert_bits_equal(sx.cpu().numpy(), sx_r, f"{name}: activation scales")
+    Yt_h = Yt.cpu().numpy()
+    assert_output_close(Yt_h, yt_r, O.abs_contrib(P_r, sx_r, sW), f"{name}: Y~")
+    assert_blocks_close(Y.cpu().numpy(), O.transform_out(Yt_h, us, TABLES), f"{name}: Y")
+    # U and V orthogonal: Y~ U approximates X W^T up to the quantization error
+    y_fp = X.astype(np.float64) @ W.astype(np.float64).T
+    rel = np.linalg.norm(Y.cpu().numpy() - y_fp) / np.linalg.norm(y_fp)
+    assert rel < 0.1, f"{name}: transformed layer far from X W^T ({rel:.3g})"
