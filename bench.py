@@ -83,6 +83,10 @@ def parse():
                     help="only time packing with absmax vs fitted (eq. 7) scales, and decode of "
                          "input-sharing projections called separately vs packed as one group (App. E.4), "
                          "on 8B-class shapes, and print a markdown table")
+    ap.add_argument("--transformed", action="store_true",
+                    help="only time the App. B.1 block transforms around the linear (X V before "
+                         "quantization, Y~ U after it) on the Llama-3.2-3B decode and Qwen3-4B prefill "
+                         "shapes, and print a markdown table")
     ap.add_argument("--traffic-summary", nargs=4, metavar="CSV",
                     help="print the per-launch HBM traffic summary from four rocprofv3 counter "
                          "CSVs: bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE")
@@ -385,6 +389,56 @@ def grouped_comparison(aq, torch, dec, ws, pre, reps: int = 48):
     print("\n".join(rows))
 
 
+def transformed_comparison(aq, gen, torch, dec, ws, pre, reps: int = 48):
+    """Cost of the online App. B.1 transforms: per call the transform of the
+    activations (X V), quantization, both in one pass, the linear and the
+    output transform (Y~ U), each timed alone; "added" is (one pass + Y~ U -
+    quantization) over the untransformed quantization + linear.
+    Decode runs on the 24 weight copies (HBM-resident weights); the linear's
+    time does not depend on the weight values, so the untransformed packed
+    copies stand in for packed W~."""
+    tables = aq.transform_tables(*gen.transform_tables())
+
+    def timed(calls):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(30_000_000)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for f in calls:
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / len(calls)
+
+    rows = ["| call | M | X V µs | quant µs | X V + quant in one pass µs | linear µs | Y~ U µs "
+            "| added by the transforms | X V rate | one-pass rate | Y~ U rate |",
+            "|---|---|---|---|---|---|---|---|---|---|---|"]
+    rng = np.random.default_rng(77)
+    todo = [(f"decode {proj}", copies, xs[M], bufs[M], M,
+             lambda c, q, s, Y, copies=copies: aq.aq_linear_decode(copies[c % N_COPIES], q, s, None, 0, Y, ws), reps)
+            for proj, copies, xs, bufs in dec for M in DECODE_M]
+    for proj, pw, x, bufs in pre:
+        pws = torch.empty(max(16, aq.aq_workspace_bytes(pw, PREFILL_M, aq.AQ_PHASE_PREFILL)), dtype=torch.uint8,
+                          device=x.device)
+        todo.append((f"prefill {proj}", [pw], x, bufs, PREFILL_M,
+                     lambda c, q, s, Y, pw=pw, pws=pws: aq.aq_linear_prefill(pw, q, s, None, Y, pws), 4))
+    for name, copies, X, (qx, sx, Y), M, lin, n in todo:
+        N, K = copies[0].plan.N, copies[0].plan.K
+        vs = torch.from_numpy(gen.transform_seeds(rng, K // 64)).to(X.device)
+        us = torch.from_numpy(gen.transform_seeds(rng, N // 64)).to(X.device)
+        Xt = torch.empty_like(X)
+        t = [timed([(lambda: aq.aq_transform_rows(X, vs, tables, out=Xt))] * n),
+             timed([(lambda: aq.aq_quant_act(Xt, qx, sx))] * n),
+             timed([(lambda: aq.aq_quant_act_transformed(X, vs, tables, qx, sx))] * n),
+             timed([(lambda c=c: lin(c, qx, sx, Y)) for c in range(n)]),
+             timed([(lambda: aq.aq_transform_out(Y, us, tables, out=Y))] * n)]
+        added = (t[2] + t[4] - t[1]) / (t[1] + t[3])
+        rows.append(f"| {name} {N}x{K} | {M} | " + " | ".join(f"{v:.2f}" for v in t)
+                    + f" | {100 * added:.1f} % | {8 * M * K / t[0] / 1e3:.0f} GB/s | {5 * M * K / t[2] / 1e3:.0f} GB/s"
+                    f" | {8 * M * N / t[4] / 1e3:.0f} GB/s |")
+    print("\n".join(rows))
+
+
 def pack_and_group(aq, gen, torch, reps: int = 24):
     """Pack time with absmax and with eq. 7 fitted scales; decode of the 8B
     attention inputs (q 4096, k 1024, v 1024 rows) and MLP inputs (gate, up
@@ -480,6 +534,9 @@ def main():
         return
     if args.grouped:
         grouped_comparison(aq, torch, dec, ws, pre)
+        return
+    if args.transformed:
+        transformed_comparison(aq, gen, torch, dec, ws, pre)
         return
 
     t_host = 0.0

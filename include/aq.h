@@ -322,13 +322,30 @@ typedef struct aq_transform_tables {
 aq_status aq_transform_rows(const float *X, int M, int K, const int8_t *vseeds,
                             const aq_transform_tables *tables_host, float *Xt, void *stream);
 
-/* Y = Y~ U: every 64-feature block r of every output row y~ becomes
- * Phi_{u_r} y~ (eq. 4).
+/* Y = Y~ U (+ bias): every 64-feature block r of every output row y~
+ * becomes Phi_{u_r} y~ (eq. 4), then bias[n] is added.  The bias belongs to
+ * the untransformed output, so a transformed layer passes it here and not
+ * to the linear call.
  *   Yt, Y    device FP32 [M][N], N a multiple of 64; Y == Yt is allowed
  *   useeds   device INT8 [N/64]
+ *   bias     device FP32 [N] or NULL
  * M == 0 is a no-op. */
 aq_status aq_transform_out(const float *Yt, int M, int N, const int8_t *useeds,
-                           const aq_transform_tables *tables_host, float *Y, void *stream);
+                           const aq_transform_tables *tables_host, const float *bias, float *Y,
+                           void *stream);
+
+/* aq_quant_act of X~ = X V in one pass: the same codes and scales as
+ * aq_transform_rows followed by aq_quant_act, bit for bit, with the
+ * transformed rows kept on chip (read X once, write the codes once).
+ *   X        device FP32 [M][K], K a multiple of 64 and at most 40768 (one
+ *            transformed row is staged in 160 KiB of LDS; longer rows take
+ *            the two calls)
+ *   vseeds   device INT8 [K/64]
+ *   qx, sx   as aq_quant_act
+ * A seed outside -1 .. 6 makes that row's scale NaN.  M == 0 is a no-op. */
+aq_status aq_quant_act_transformed(const float *X, int M, int K, const int8_t *vseeds,
+                                   const aq_transform_tables *tables_host, int8_t *qx, float *sx,
+                                   void *stream);
 
 /* W~ = U W V: first each row's 64-feature blocks by Phi_{v_c}^T (as
  * aq_transform_rows), then the 64 rows of each output tile row r, column by

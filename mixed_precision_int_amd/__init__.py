@@ -28,6 +28,7 @@ from .binding import (  # noqa: F401
     aq_pack_weights,
     aq_plan_pack,
     aq_quant_act,
+    aq_quant_act_transformed,
     aq_transform_out,
     aq_transform_rows,
     aq_transform_weights,

@@ -29,7 +29,7 @@ EXPORTS = ["aq_abi_version", "aq_status_string", "aq_labels_from_map", "aq_plan_
            "aq_linear_decode", "aq_linear_prefill", "aq_linear_tile_partials",
            "aq_quant_act_grouped", "aq_linear_decode_grouped", "aq_linear_prefill_grouped",
            "aq_linear_tile_partials_grouped", "aq_pack_weights_mse",
-           "aq_transform_rows", "aq_transform_out", "aq_transform_weights"]
+           "aq_transform_rows", "aq_transform_out", "aq_transform_weights", "aq_quant_act_transformed"]
 
 
 class AqError(RuntimeError):
@@ -97,7 +97,8 @@ def lib() -> ctypes.CDLL:
         "aq_linear_prefill_grouped": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
         "aq_linear_tile_partials_grouped": (i32, [ctypes.POINTER(AqPacked), vp, i32, vp, vp]),
         "aq_transform_rows": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
-        "aq_transform_out": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
+        "aq_transform_out": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp, vp]),
+        "aq_quant_act_transformed": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp, vp]),
         "aq_transform_weights": (i32, [vp, i32, i32, vp, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -432,20 +433,42 @@ def aq_transform_rows(X, vseeds, tables, out=None, stream=None):
     return out
 
 
-def aq_transform_out(Yt, useeds, tables, out=None, stream=None):
-    """Y = Y~ U (FP32 [M, N] on the device; out=Yt transforms in place)."""
+def aq_transform_out(Yt, useeds, tables, bias=None, out=None, stream=None):
+    """Y = Y~ U + bias (FP32 [M, N] on the device; out=Yt transforms in place)."""
     import torch
     M, N = Yt.shape
     if out is None:
         out = torch.empty_like(Yt)
     _check_f32(Yt, (M, N), "Yt")
     _check_f32(out, (M, N), "out")
+    if bias is not None:
+        _check_f32(bias, (N,), "bias")
     sd = _seeds_dev(useeds, N // 64, Yt.device)
     t = _tables(tables)
     _check(lib().aq_transform_out(ctypes.c_void_p(Yt.data_ptr()), M, N, ctypes.c_void_p(sd.data_ptr()),
-                                  ctypes.byref(t), ctypes.c_void_p(out.data_ptr()), _stream(stream)),
+                                  ctypes.byref(t), _ptr(bias), ctypes.c_void_p(out.data_ptr()),
+                                  _stream(stream)),
            "aq_transform_out")
     return out
+
+
+def aq_quant_act_transformed(X, vseeds, tables, qx=None, sx=None, stream=None):
+    """INT8 codes [M, K] and FP32 per-token scales [M] of X~ = X V, computed
+    in one pass (X FP32 [M, K] on the device, K <= 40768)."""
+    import torch
+    M, K = X.shape
+    _check_f32(X, (M, K), "X")
+    if qx is None:
+        qx = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float32, device=X.device)
+    sd = _seeds_dev(vseeds, K // 64, X.device)
+    t = _tables(tables)
+    _check(lib().aq_quant_act_transformed(ctypes.c_void_p(X.data_ptr()), M, K, ctypes.c_void_p(sd.data_ptr()),
+                                          ctypes.byref(t), ctypes.c_void_p(qx.data_ptr()),
+                                          ctypes.c_void_p(sx.data_ptr()), _stream(stream)),
+           "aq_quant_act_transformed")
+    return qx, sx
 
 
 def aq_transform_weights(W, useeds, vseeds, tables, out=None, stream=None):

@@ -370,15 +370,16 @@ aq_status check_tables(const aq_transform_tables *t) {
 }
 
 aq_status run_row_transform(int kind, const float *src, int M, int K, const int8_t *seeds,
-                            const aq_transform_tables *t, float *dst, void *stream) {
+                            const aq_transform_tables *t, const float *bias, float *dst,
+                            void *stream) {
   if (M < 0 || K <= 0 || K % 64) return AQ_ERR_SHAPE;
   if (M == 0) return AQ_OK;
   if (!src || !dst || !seeds) return AQ_ERR_NULL;
   aq_status st = check_tables(t);
   if (st != AQ_OK) return st;
-  if (!aligned16(src) || !aligned16(dst)) return AQ_ERR_ALIGN;
-  if ((long long)M * K > (1LL << 40)) return AQ_ERR_SHAPE;
-  return aq::launch_transform(kind, src, dst, M, K, seeds, nullptr, *t,
+  if (!aligned16(src) || !aligned16(dst) || (bias && !aligned16(bias))) return AQ_ERR_ALIGN;
+  if ((long long)M * K > (1LL << 40) || (K / 64 + 15) / 16 > 65535) return AQ_ERR_SHAPE;
+  return aq::launch_transform(kind, src, dst, M, K, seeds, nullptr, bias, *t,
                               static_cast<hipStream_t>(stream)) == hipSuccess
              ? AQ_OK
              : AQ_ERR_HIP;
@@ -390,12 +391,28 @@ extern "C" {
 
 aq_status aq_transform_rows(const float *X, int M, int K, const int8_t *vseeds,
                             const aq_transform_tables *tables_host, float *Xt, void *stream) {
-  return run_row_transform(aq::kTransformRows, X, M, K, vseeds, tables_host, Xt, stream);
+  return run_row_transform(aq::kTransformRows, X, M, K, vseeds, tables_host, nullptr, Xt, stream);
 }
 
 aq_status aq_transform_out(const float *Yt, int M, int N, const int8_t *useeds,
-                           const aq_transform_tables *tables_host, float *Y, void *stream) {
-  return run_row_transform(aq::kTransformOut, Yt, M, N, useeds, tables_host, Y, stream);
+                           const aq_transform_tables *tables_host, const float *bias, float *Y,
+                           void *stream) {
+  return run_row_transform(aq::kTransformOut, Yt, M, N, useeds, tables_host, bias, Y, stream);
+}
+
+aq_status aq_quant_act_transformed(const float *X, int M, int K, const int8_t *vseeds,
+                                   const aq_transform_tables *tables_host, int8_t *qx, float *sx,
+                                   void *stream) {
+  if (M < 0 || K <= 0 || K % 64 || K > aq::kQuantTransformMaxK) return AQ_ERR_SHAPE;
+  if (M == 0) return AQ_OK;
+  if (!X || !qx || !sx || !vseeds) return AQ_ERR_NULL;
+  aq_status st = check_tables(tables_host);
+  if (st != AQ_OK) return st;
+  if (!aligned16(X) || !aligned16(qx) || !aligned4(sx)) return AQ_ERR_ALIGN;
+  return aq::launch_quant_act_transformed(X, M, K, vseeds, *tables_host, qx, sx,
+                                          static_cast<hipStream_t>(stream)) == hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
 }
 
 aq_status aq_transform_weights(const float *W, int N, int K, const int8_t *useeds,
@@ -410,7 +427,7 @@ aq_status aq_transform_weights(const float *W, int N, int K, const int8_t *useed
   const uintptr_t w0 = reinterpret_cast<uintptr_t>(W), t0 = reinterpret_cast<uintptr_t>(Wt);
   const uintptr_t bytes = (uintptr_t)N * K * sizeof(float);
   if (w0 < t0 + bytes && t0 < w0 + bytes) return AQ_ERR_ARG;
-  return aq::launch_transform(aq::kTransformWeights, W, Wt, N, K, vseeds, useeds, *tables_host,
+  return aq::launch_transform(aq::kTransformWeights, W, Wt, N, K, vseeds, useeds, nullptr, *tables_host,
                               static_cast<hipStream_t>(stream)) == hipSuccess
              ? AQ_OK
              : AQ_ERR_HIP;

@@ -120,7 +120,14 @@ using TransformTables = aq_transform_tables;
 constexpr int kTransformSeeds = AQ_TRANSFORM_SEEDS;
 enum { kTransformRows = 0, kTransformOut = 1, kTransformWeights = 2 };
 hipError_t launch_transform(int kind, const float *src, float *dst, int rows, int cols,
-                            const int8_t *seeds, const int8_t *seeds2, const TransformTables &t,
-                            hipStream_t stream);
+                            const int8_t *seeds, const int8_t *seeds2, const float *bias,
+                            const TransformTables &t, hipStream_t stream);
+// X V and the per-token quantizer in one pass; the transformed row is staged
+// in LDS (160 KiB less the tables and the reduction slots), so K is bounded
+// by kQuantTransformMaxK.
+constexpr int kQuantTransformMaxK = 40768;
+hipError_t launch_quant_act_transformed(const float *X, int M, int K, const int8_t *seeds,
+                                        const TransformTables &t, int8_t *qx, float *sx,
+                                        hipStream_t stream);
 
 }  // namespace aq

@@ -216,7 +216,12 @@ def test_transform_entry_points_rejected(aqlib):
     assert L.aq_transform_rows(FAKE, 4, 128, None, T, FAKE, None) == -1
     assert L.aq_transform_rows(FAKE, 4, 128, FAKE, None, FAKE, None) == -1
     assert L.aq_transform_rows(FAKE + 4, 4, 128, FAKE, T, FAKE, None) == -5
-    assert L.aq_transform_out(FAKE, -1, 128, FAKE, T, FAKE, None) == -2
+    assert L.aq_transform_out(FAKE, -1, 128, FAKE, T, None, FAKE, None) == -2
+    assert L.aq_transform_out(FAKE, 4, 128, FAKE, T, FAKE + 4, FAKE, None) == -5   # bias alignment
+    q = lambda **k: L.aq_quant_act_transformed(k.get("X", FAKE), k.get("M", 4), k.get("K", 128), k.get("s", FAKE),
+                                               k.get("T", T), FAKE, FAKE, None)
+    assert q(K=40768 + 64) == -2 and q(K=96) == -2 and q(M=0) == 0
+    assert q(s=None) == -1 and q(T=None) == -1 and q(X=FAKE + 4) == -5
     assert L.aq_transform_weights(FAKE, 100, 128, FAKE, FAKE, T, FAKE + (1 << 20), None) == -2
     assert L.aq_transform_weights(FAKE, 64, 128, FAKE, FAKE, T, FAKE + 64 * 128, None) == -8  # overlap
     assert L.aq_transform_weights(FAKE, 64, 128, None, FAKE, T, FAKE + (1 << 20), None) == -1
@@ -231,4 +236,4 @@ def test_transform_entry_points_rejected(aqlib):
     bads = dr.copy()
     bads[5, 63] = 0                            # a sign must be +-1
     assert L.aq_transform_out(FAKE, 4, 128, FAKE, ctypes.byref(B.transform_tables(perm, dl, bads)),
-                              FAKE, None) == -8
+                              None, FAKE, None) == -8

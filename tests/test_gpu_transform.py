@@ -30,12 +30,16 @@ def assert_bits_equal(got, ref, name):
     assert bad.size == 0, f"{name}: {len(bad)} values differ, first {bad[:4].tolist()}"
 
 
-def assert_blocks_close(got, ref, name, rel=3e-6):
+def assert_blocks_close(got, ref, name, rel=3e-6, src=None):
+    """Per 64-block, |got - ref|_2 <= rel |src|_2 + 2^-23 |ref|_2 (src: the
+    block before the transform, default ref; the second term covers one
+    final FP32 rounding, such as a bias add)."""
     M, N = ref.shape
     g = np.asarray(got, np.float64).reshape(M, N // 64, 64)
     r = np.asarray(ref, np.float64).reshape(M, N // 64, 64)
+    s0 = r if src is None else np.asarray(src, np.float64).reshape(M, N // 64, 64)
     err = np.linalg.norm(g - r, axis=-1)
-    bound = rel * np.linalg.norm(r, axis=-1) + 1e-30
+    bound = rel * np.linalg.norm(s0, axis=-1) + 2.0 ** -23 * np.linalg.norm(r, axis=-1) + 1e-30
     bad = np.argwhere(err > bound)
     assert bad.size == 0, f"{name}: {len(bad)} blocks off, first {bad[:4].tolist()}"
 
@@ -76,20 +80,47 @@ def test_transform_weights_bit_exact(N, K):
     assert_bits_equal(Wt.cpu().numpy(), O.transform_weights(W, us, vs, TABLES), f"weights N{N} K{K}")
 
 
-@pytest.mark.parametrize("M,N", [(1, 64), (4, 576), (37, 4096), (1024, 1024)])
-def test_transform_out_close(M, N):
-    """Y = Y~ U against the FP64 product, in place and out of place."""
+@pytest.mark.parametrize("M,N,bias", [(1, 64, False), (4, 576, True), (37, 4096, True), (1024, 1024, False)])
+def test_transform_out_close(M, N, bias):
+    """Y = Y~ U (+ bias) against the FP64 product, in place and out of place."""
     rng = np.random.default_rng(11 * M + N)
     Yt = (rng.standard_normal((M, N)) * rng.uniform(0.1, 30.0, size=(M, 1))).astype(np.float32)
     us = every_seed(rng, N // 64)
-    ref = O.transform_out(Yt, us, TABLES)
-    say(f"  transform_out M={M} N={N}")
-    Y = aq.aq_transform_out(to_dev(Yt), us, TABLES)
+    b = rng.standard_normal(N).astype(np.float32) if bias else None
+    ref = O.transform_out(Yt, us, TABLES) + (0.0 if b is None else b.astype(np.float64)[None, :])
+    say(f"  transform_out M={M} N={N} bias={bias}")
+    bd = None if b is None else to_dev(b)
+    Y = aq.aq_transform_out(to_dev(Yt), us, TABLES, bias=bd)
     Yd = to_dev(Yt)
-    aq.aq_transform_out(Yd, us, TABLES, out=Yd)
+    aq.aq_transform_out(Yd, us, TABLES, bias=bd, out=Yd)
     torch.cuda.synchronize()
-    assert_blocks_close(Y.cpu().numpy(), ref, f"out M{M} N{N}")
+    assert_blocks_close(Y.cpu().numpy(), ref, f"out M{M} N{N}", src=Yt)
     assert_bits_equal(Yd.cpu().numpy(), Y.cpu().numpy(), f"out in place M{M} N{N}")
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (5, 3072), (33, 1088), (300, 9728), (2, 40768), (256, 2560)])
+def test_quant_act_transformed_bit_exact(M, K):
+    """X V and the per-token quantizer in one pass: codes and scales equal the
+    oracle's quantizer applied to the oracle's X V, on both workgroup widths
+    (fewer than 256 rows: 1024 threads; else 256) and the longest row the
+    on-chip staging takes; a zero row keeps the 1e-12 floor."""
+    rng = np.random.default_rng(13 * M + K)
+    X = gen.acts_outliers(rng, M, K, max(1, K // 100), 30.0)
+    X[0, :] = 0.0
+    vs = every_seed(rng, K // 64)
+    qx_r, sx_r = O.quant_act(O.transform_rows(X, vs, TABLES))
+    say(f"  quant_act_transformed M={M} K={K}")
+    qx, sx = aq.aq_quant_act_transformed(to_dev(X), vs, TABLES)
+    torch.cuda.synchronize()
+    assert np.array_equal(qx.cpu().numpy().astype(np.int64), qx_r), f"M{M} K{K}: codes differ"
+    assert_bits_equal(sx.cpu().numpy(), sx_r, f"M{M} K{K}: scales")
+
+
+def test_quant_act_transformed_bad_seed():
+    """A seed outside -1 .. 6 gives every row a NaN scale."""
+    X = np.ones((3, 128), np.float32)
+    _, sx = aq.aq_quant_act_transformed(to_dev(X), np.array([0, 8], np.int8), TABLES)
+    assert np.isnan(sx.cpu().numpy()).all()
 
 
 def test_transform_round_trip():
@@ -129,13 +160,15 @@ def test_transformed_linear(N, K, bK, M):
     kernels give Y~, and Y = Y~ U.  Every integer stage bit-exact with the
     oracle on the oracle's own transformed operands; Y~ within the linear's
     bar; Y within the transform's bound of the oracle's Y~ U of the GPU Y~;
-    and Y close to X W^T where quantization error allows (orthogonality)."""
+    and Y close to X W^T + bias where quantization error allows
+    (orthogonality)."""
     rng = np.random.default_rng(N + K + M)
     W = gen.weights(rng, N, K)
     X = gen.acts_outliers(rng, M, K, max(1, K // 100), 25.0)
     R, C = N // 64, K // bK
     z = gen.map_uniform(rng, R, C, 0.35)
     us, vs = every_seed(rng, R), every_seed(rng, K // 64)
+    b = rng.standard_normal(N).astype(np.float32)
     name = f"transformed{N}x{K}/bK{bK}/M{M}"
     say(f"[{name}]")
     # oracle
@@ -148,18 +181,17 @@ def test_transformed_linear(N, K, bK, M):
     # HIP path
     Wt = aq.aq_transform_weights(to_dev(W), us, vs, TABLES)
     pw = aq.aq_pack_weights(Wt, aq.aq_labels_from_map(z.astype(np.uint8)), 64, bK)
-    Xt = aq.aq_transform_rows(to_dev(X), vs, TABLES)
-    qx, sx = aq.aq_quant_act(Xt)
+    qx, sx = aq.aq_quant_act_transformed(to_dev(X), vs, TABLES)
     Yt = aq.aq_linear_decode(pw, qx, sx) if M < 1024 else aq.aq_linear_prefill(pw, qx, sx)
-    Y = aq.aq_transform_out(Yt, us, TABLES)
+    Y = aq.aq_transform_out(Yt, us, TABLES, bias=to_dev(b))
     torch.cuda.synchronize()
     assert_bits_equal(Wt.cpu().numpy(), Wt_r, f"{name}: W~")
     assert np.array_equal(qx.cpu().numpy().astype(np.int64), qx_r), f"{name}: codes differ"
     assert_bits_equal(sx.cpu().numpy(), sx_r, f"{name}: activation scales")
     Yt_h = Yt.cpu().numpy()
     assert_output_close(Yt_h, yt_r, O.abs_contrib(P_r, sx_r, sW), f"{name}: Y~")
-    assert_blocks_close(Y.cpu().numpy(), O.transform_out(Yt_h, us, TABLES), f"{name}: Y")
+    assert_blocks_close(Y.cpu().numpy(), O.transform_out(Yt_h, us, TABLES) + b[None, :], f"{name}: Y", src=Yt_h)
     # U and V orthogonal: Y~ U approximates X W^T up to the quantization error
-    y_fp = X.astype(np.float64) @ W.astype(np.float64).T
+    y_fp = X.astype(np.float64) @ W.astype(np.float64).T + b[None, :]
     rel = np.linalg.norm(Y.cpu().numpy() - y_fp) / np.linalg.norm(y_fp)
     assert rel < 0.1, f"{name}: transformed layer far from X W^T ({rel:.3g})"
