@@ -87,6 +87,11 @@ def parse():
                     help="only time the App. B.1 block transforms around the linear (X V before "
                          "quantization, Y~ U after it) on the Llama-3.2-3B decode and Qwen3-4B prefill "
                          "shapes, and print a markdown table")
+    ap.add_argument("--model-step", action="store_true",
+                    help="only time whole decode steps of the 8B-class model (36 layers x 4 packed "
+                         "projections resident in HBM; quantization + linear per projection) at "
+                         "M = 1, 8, 32, 64: enqueued ahead, captured in a HIP graph, and host-paced "
+                         "wall-clock; print a markdown table")
     ap.add_argument("--traffic-summary", nargs=4, metavar="CSV",
                     help="print the per-launch HBM traffic summary from four rocprofv3 counter "
                          "CSVs: bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE")
@@ -439,6 +444,94 @@ def transformed_comparison(aq, gen, torch, dec, ws, pre, reps: int = 48):
     print("\n".join(rows))
 
 
+def model_step(aq, gen, torch, reps: int = 10):
+    """Whole decode steps of the 8B-class model: all 144 projections (36
+    layers x qkv 6144x4096, o 4096x4096, gate_up 28672x4096, down 4096x14336;
+    per-layer INT8 fraction ~ U(0.15, 0.45)), packed and resident (about
+    5.4 GB, far beyond the last-level cache). A step quantizes each
+    projection's activations and runs its decode linear. Three timings:
+    launches enqueued behind a GPU hold (device back to back), the step
+    captured once as a HIP graph and replayed, and host-paced wall-clock
+    (each step enqueued and synchronized). The graph's outputs are checked
+    against the eager step's, bit for bit."""
+    from mixed_precision_int_amd.model import pack_model
+    dev = torch.device("cuda", 0)
+    maps = gen.dense8b_maps()
+    model = pack_model(gen.DENSE8B, maps, lambda l, name, N, K: gen.device_weights(N, K, gen.seed_for(4, l, name)))
+    torch.cuda.synchronize()
+    per_us = sleep_cycles_per_us(torch)
+    rows = [f"Packed model: {model.nbytes() / 1e9:.3f} GB resident.", "",
+            "| M | algorithmic GB / step | enqueued ahead ms | GB/s | HIP graph ms | GB/s | host-paced ms "
+            "| graph = eager |", "|---|---|---|---|---|---|---|---|"]
+    for M in (1, 8, 32, 64):
+        xs = {name: gen.device_acts_outliers(M, K, gen.act_seed(4, 0, name, M)) for name, N, K in gen.DENSE8B}
+        bufs = {name: (torch.empty((M, K), dtype=torch.int8, device=dev), torch.empty((M,), dtype=torch.float32, device=dev),
+                       torch.empty((M, N), dtype=torch.float32, device=dev)) for name, N, K in gen.DENSE8B}
+        need = max(aq.aq_workspace_bytes(pw, M, aq.AQ_PHASE_DECODE) for _, _, pw in model)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+        nbytes = sum(linear_bytes(pw.plan, M) for _, _, pw in model)
+
+        def step():
+            for l, name, pw in model:
+                qx, sx, Y = bufs[name]
+                aq.aq_quant_act(xs[name], qx, sx)
+                aq.aq_linear_decode(pw, qx, sx, None, 0, Y, ws)
+
+        step()
+        torch.cuda.synchronize()
+        eager = {name: b[2].clone() for name, b in bufs.items()}
+        t0 = time.perf_counter()
+        step()
+        host_us = (time.perf_counter() - t0) * 1e6
+        torch.cuda.synchronize()
+        E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        # enqueued ahead behind a hold
+        a, b = E(), E()
+        torch.cuda._sleep(int(per_us * (host_us * reps * 1.5 + 2000)))
+        a.record()
+        for _ in range(reps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        t_ahead = a.elapsed_time(b) / reps
+        # HIP graph
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for Y in bufs.values():
+            Y[2].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(bufs[name][2], eager[name]) for name in bufs)
+        a, b = E(), E()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        same = same and all(torch.equal(bufs[name][2], eager[name]) for name in bufs)
+        t_graph = a.elapsed_time(b) / reps
+        # host-paced wall-clock
+        walls = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            step()
+            torch.cuda.synchronize()
+            walls.append((time.perf_counter() - t0) * 1e3)
+        t_wall = float(np.median(walls))
+        rows.append(f"| {M} | {nbytes / 1e9:.3f} | {t_ahead:.3f} | {nbytes / t_ahead / 1e6:.0f} | {t_graph:.3f} | "
+                    f"{nbytes / t_graph / 1e6:.0f} | {t_wall:.3f} | {same} |")
+        print(rows[-1], flush=True)
+        del g, xs, bufs, eager, ws
+    print("\n".join(rows))
+
+
 def pack_and_group(aq, gen, torch, reps: int = 24):
     """Pack time with absmax and with eq. 7 fitted scales; decode of the 8B
     attention inputs (q 4096, k 1024, v 1024 rows) and MLP inputs (gate, up
@@ -525,6 +618,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n}))
         return
     aq.lib()
+    if args.model_step:
+        model_step(aq, gen, torch)
+        return
     if args.pack_and_group:
         pack_and_group(aq, gen, torch)
         return
