@@ -195,3 +195,30 @@ def test_transformed_linear(N, K, bK, M):
     y_fp = X.astype(np.float64) @ W.astype(np.float64).T + b[None, :]
     rel = np.linalg.norm(Y.cpu().numpy() - y_fp) / np.linalg.norm(y_fp)
     assert rel < 0.1, f"{name}: transformed layer far from X W^T ({rel:.3g})"
+
+
+@pytest.mark.parametrize("proj", ["qkv", "down"])
+def test_transforms_full_prefill_size_sampled(proj):
+    """Full Qwen3-4B-shaped prefill size (M = 2048), in the launch shapes the
+    transform benchmark times: the one-pass quantizer's codes and scales on
+    sampled token rows, bit-exact with the oracle's quantizer of the
+    oracle's X V, and Y~ U (+ bias) of the full [2048, N] output on the same
+    rows within the transform bound."""
+    d = gen.qwen4b_prefill(proj, 2048)
+    X = d["X"]
+    M, K = X.shape
+    N = d["W"].shape[0]
+    rng = np.random.default_rng(K + N)
+    vs, us = every_seed(rng, K // 64), every_seed(rng, N // 64)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, M - 1], rng.choice(M, 11, replace=False)]))
+    say(f"  full-size transforms {proj} M={M} K={K} N={N}, rows {rows.tolist()}")
+    qx, sx = aq.aq_quant_act_transformed(to_dev(X), vs, TABLES)
+    Yt = (rng.standard_normal((M, N)) * 4.0).astype(np.float32)
+    b = rng.standard_normal(N).astype(np.float32)
+    Y = aq.aq_transform_out(to_dev(Yt), us, TABLES, bias=to_dev(b))
+    torch.cuda.synchronize()
+    qx_r, sx_r = O.quant_act(O.transform_rows(X[rows], vs, TABLES))
+    assert np.array_equal(qx.cpu().numpy()[rows].astype(np.int64), qx_r), f"{proj}: codes differ"
+    assert_bits_equal(sx.cpu().numpy()[rows], sx_r, f"{proj}: scales")
+    ref = O.transform_out(Yt[rows], us, TABLES) + b.astype(np.float64)[None, :]
+    assert_blocks_close(Y.cpu().numpy()[rows], ref, f"{proj}: Y", src=Yt[rows])
