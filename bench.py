@@ -92,6 +92,11 @@ def parse():
                          "projections resident in HBM; quantization + linear per projection) at "
                          "M = 1, 8, 32, 64: enqueued ahead, captured in a HIP graph, and host-paced "
                          "wall-clock; print a markdown table")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure reference ceilings with library kernels on this GPU: streaming "
+                         "read and copy bandwidth by size, back-to-back launch floor, and hipBLASLt INT8 "
+                         "GEMM rate (torch._int_mm) on the prefill shapes and a large square; print a "
+                         "markdown table")
     ap.add_argument("--traffic-summary", nargs=4, metavar="CSV",
                     help="print the per-launch HBM traffic summary from four rocprofv3 counter "
                          "CSVs: bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE")
@@ -532,6 +537,58 @@ def model_step(aq, gen, torch, reps: int = 10):
     print("\n".join(rows))
 
 
+def ceilings(torch):
+    """Reference ceilings measured with library kernels (not this library's):
+    HBM streaming read (a sum over int64 words) and copy, cycling over
+    distinct buffers of at least 1 GiB in total so the 256 MB last-level
+    cache does not serve them; the back-to-back floor of a tiny kernel; and
+    hipBLASLt INT8 GEMM (torch._int_mm, INT32 out, no rescale, no INT4)."""
+    dev = torch.device("cuda", 0)
+
+    def span(fns):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for f in fns:
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / len(fns)
+
+    rows = ["| size MB | read by torch.sum GB/s | copy GB/s (read + write) |", "|---|---|---|"]
+    for mb in (6, 16, 32, 64, 256, 1024):
+        n = max(1, (1024 + mb - 1) // mb + 1)
+        nbytes = mb << 20
+        bufs = [torch.ones(nbytes // 8, dtype=torch.int64, device=dev) for _ in range(n)]
+        outs = [torch.empty_like(b) for b in bufs]
+        reps = max(2 * n, 8)
+        for b in bufs:
+            b.sum()
+        tr = span([(lambda k=k: bufs[k % n].sum()) for k in range(reps)])
+        tc = span([(lambda k=k: outs[k % n].copy_(bufs[k % n])) for k in range(reps)])
+        rows.append(f"| {mb} | {nbytes / tr / 1e3:.0f} | {2 * nbytes / tc / 1e3:.0f} |")
+        del bufs, outs
+        torch.cuda.empty_cache()
+    one = torch.zeros(1, device=dev)
+    for _ in range(3):
+        one.add_(1.0)
+    tl = span([(lambda: one.add_(1.0))] * 200)
+    rows += ["", f"Back-to-back floor of a one-element kernel: {tl:.2f} µs per launch.", "",
+             "| INT8 GEMM (hipBLASLt via torch._int_mm) | µs | TOPS |", "|---|---|---|"]
+    for M, N, K in ((2048, 6144, 2560), (2048, 2560, 4096), (2048, 19456, 2560), (2048, 2560, 9728),
+                    (8192, 34816, 5120), (8192, 8192, 8192)):
+        a = torch.randint(-128, 127, (M, K), dtype=torch.int8, device=dev)
+        b = torch.randint(-128, 127, (N, K), dtype=torch.int8, device=dev).t()
+        torch._int_mm(a, b)
+        n = 6 if M * N * K < 2 ** 38 else 3
+        t = span([(lambda: torch._int_mm(a, b))] * n)
+        rows.append(f"| M {M} x N {N} x K {K} | {t:.1f} | {2 * M * N * K / t / 1e6:.0f} |")
+        del a, b
+        torch.cuda.empty_cache()
+    print("\n".join(rows))
+
+
 def pack_and_group(aq, gen, torch, reps: int = 24):
     """Pack time with absmax and with eq. 7 fitted scales; decode of the 8B
     attention inputs (q 4096, k 1024, v 1024 rows) and MLP inputs (gate, up
@@ -592,6 +649,10 @@ def pack_and_group(aq, gen, torch, reps: int = 24):
     print("\n".join(rows))
 
 
+def _med_min(v):
+    return {"median": round(float(np.median(v)), 4), "min": round(float(np.min(v)), 4)}
+
+
 def main():
     args = parse()
     if args.traffic_summary:
@@ -616,6 +677,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n}))
+        return
+    if args.ceilings:
+        ceilings(torch)
         return
     aq.lib()
     if args.model_step:
@@ -738,6 +802,15 @@ def main():
         },
         "segments_ms_per_step": {"decode": round(dseg / args.steps, 4),
                                  "prefill": round(pseg / args.steps, 4)},
+        # per-step spread (median and minimum over the K timed steps)
+        "step_stats": {
+            "decode_linear_us_per_call": _med_min([d_call[i].elapsed_time(d_seg[i + 1]) * 1e3
+                                                   / (len(DECODE_M) * len(dec)) for i in range(K)]),
+            "prefill_linear_us_per_call": _med_min([p_call[i].elapsed_time(p_seg[i + 1]) * 1e3 / len(pre)
+                                                    for i in range(K)]),
+            "decode_segment_ms": _med_min([d_seg[i].elapsed_time(d_seg[i + 1]) for i in range(K)]),
+            "prefill_segment_ms": _med_min([p_seg[i].elapsed_time(p_seg[i + 1]) for i in range(K)]),
+        },
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
