@@ -170,16 +170,15 @@ __device__ __forceinline__ void fwht_quad(float (&r)[16], int q) {
         r[k] = a + b;
         r[k + h] = a - b;
       }
+  // h = 16 and 32 pair lanes q, q ^ 1 and q, q ^ 2.  The lane with the
+  // bit clear keeps self + partner, its partner partner - self: both are
+  // partner + (self with its sign flipped on the second lane), the same
+  // IEEE sums, one sign-bit XOR and one add (the DPP move folds into it).
+  const uint32_t f16 = (uint32_t)(q & 1) << 31, f32 = (uint32_t)((q >> 1) & 1) << 31;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {  // h = 16: lanes q, q ^ 1
-    const float p = quad_xor<0xB1>(r[k]);
-    r[k] = (q & 1) ? p - r[k] : r[k] + p;
-  }
+  for (int k = 0; k < 16; ++k) r[k] = quad_xor<0xB1>(r[k]) + __uint_as_float(__float_as_uint(r[k]) ^ f16);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {  // h = 32: lanes q, q ^ 2
-    const float p = quad_xor<0x4E>(r[k]);
-    r[k] = (q & 2) ? p - r[k] : r[k] + p;
-  }
+  for (int k = 0; k < 16; ++k) r[k] = quad_xor<0x4E>(r[k]) + __uint_as_float(__float_as_uint(r[k]) ^ f32);
 #pragma unroll
   for (int k = 0; k < 16; ++k) r[k] *= 0.125f;
 }
