@@ -92,6 +92,10 @@ def parse():
                          "projections resident in HBM; quantization + linear per projection) at "
                          "M = 1, 8, 32, 64: enqueued ahead, captured in a HIP graph, and host-paced "
                          "wall-clock; print a markdown table")
+    ap.add_argument("--chunked-prefill", action="store_true",
+                    help="only time a long prompt prefilled in chunks through Qwen3-14B-shaped projections: "
+                         "the temporary INT8 operand prepared with every chunk (aq_linear_prefill) or once "
+                         "(aq_prefill_prepare + aq_linear_prefill_prepared); print a markdown table")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure reference ceilings with library kernels on this GPU: streaming "
                          "read and copy bandwidth by size, back-to-back launch floor, and hipBLASLt INT8 "
@@ -537,6 +541,62 @@ def model_step(aq, gen, torch, reps: int = 10):
     print("\n".join(rows))
 
 
+def chunked_prefill(aq, gen, torch):
+    """A 16K-token prompt prefilled in chunks of 1024 or 8192 tokens through
+    Qwen3-14B-shaped projections (30% INT8 tiles in bands): the long-prompt
+    operand (App. E.3 Prefill) prepared with every chunk, or once for all of
+    them (it depends on the weights only).  Outputs compared bit for bit."""
+    dev = torch.device("cuda", 0)
+
+    def span(fn, n=1):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    total = 16384
+    rows = ["| projection | chunk | chunks | operand prepared per chunk µs | prepared once µs | saved | equal |",
+            "|---|---|---|---|---|---|---|"]
+    for name, N, K in (("gate_up", 34816, 5120), ("down", 5120, 17408), ("o", 5120, 5120)):
+        rng = np.random.default_rng(N + K)
+        z = gen.map_bands(rng, N // 64, K // 128, 0.30)
+        W = gen.device_weights(N, K, seed=N + K, device=dev)
+        pw = aq.aq_pack_weights(W, aq.aq_labels_from_map(z.astype(np.uint8)), 64, 128)
+        del W
+        ws = torch.empty(max(16, aq.aq_workspace_bytes(pw, 1024, aq.AQ_PHASE_PREFILL)), dtype=torch.uint8, device=dev)
+        for chunk in (1024, 8192):
+            n = total // chunk
+            X = gen.device_acts_heavy_tail(chunk, K, seed=5, device=dev)
+            qx, sx = aq.aq_quant_act(X)
+            del X
+            Ya = torch.empty((chunk, N), dtype=torch.float32, device=dev)
+            Yb = torch.empty_like(Ya)
+
+            def per_chunk():
+                for _ in range(n):
+                    aq.aq_linear_prefill(pw, qx, sx, None, Ya, ws)
+
+            def once():
+                aq.aq_prefill_prepare(pw, ws)
+                for _ in range(n):
+                    aq.aq_linear_prefill_prepared(pw, qx, sx, ws, None, Yb)
+
+            per_chunk(); once()
+            ta, tb = span(per_chunk), span(once)
+            same = bool(torch.equal(Ya, Yb))
+            rows.append(f"| {name} {N}x{K} | {chunk} | {n} | {ta:.0f} | {tb:.0f} | {100 * (ta - tb) / ta:.1f} % | {same} |")
+            print(rows[-1], flush=True)
+            del qx, sx, Ya, Yb
+        del pw, ws
+        torch.cuda.empty_cache()
+    print("\n".join(rows))
+
+
 def ceilings(torch):
     """Reference ceilings measured with library kernels (not this library's):
     HBM streaming read (a sum over int64 words) and copy, cycling over
@@ -682,6 +742,9 @@ def main():
         ceilings(torch)
         return
     aq.lib()
+    if args.chunked_prefill:
+        chunked_prefill(aq, gen, torch)
+        return
     if args.model_step:
         model_step(aq, gen, torch)
         return

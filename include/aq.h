@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AQ_ABI_VERSION 5
+#define AQ_ABI_VERSION 6
 
 typedef enum aq_status {
   AQ_OK = 0,
@@ -235,6 +235,27 @@ aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx
  * Other arguments as aq_linear_decode.  Any M >= 1 is accepted. */
 aq_status aq_linear_prefill(const aq_packed *W, const int8_t *qx, const float *sx, int M,
                             const float *bias, float *Y, void *ws, size_t ws_bytes, void *stream);
+
+/* The long-prompt operand preparation of aq_linear_prefill alone (App. E.3
+ * Prefill): writes the temporary INT8 operand of a projection with INT4
+ * tiles to ws.  It depends on the weights only: a chunked long prompt can
+ * prepare it once and run every chunk's GEMM over it, and a caller can
+ * prepare the next projection's operand ahead of its activations.
+ * A no-op (AQ_OK, nothing launched) when aq_workspace_bytes(W, 1024, 1, 0)
+ * is 0: no INT4 tile, or no long route for this geometry.
+ *   ws    device workspace of at least aq_workspace_bytes(W, 1024, 1, 0)
+ *         bytes, 16-byte aligned, else AQ_ERR_WORKSPACE */
+aq_status aq_prefill_prepare(const aq_packed *W, void *ws, size_t ws_bytes, void *stream);
+
+/* aq_linear_prefill over an operand that aq_prefill_prepare has already
+ * written to ws for the same W; the caller orders the two (same stream, or
+ * an event), and keeps ws unchanged until this call's kernels have run.
+ * Prompts that take the short route (M < 1024) do not read ws.  The same
+ * kernels as aq_linear_prefill, so the same Y bit for bit.  Arguments and
+ * errors as aq_linear_prefill. */
+aq_status aq_linear_prefill_prepared(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                                     const float *bias, float *Y, const void *ws, size_t ws_bytes,
+                                     void *stream);
 
 /* Debug: the INT32 tile products P[m, n, j] of eq. 19 (the parenthesized
  * product, before any scaling), written to P as INT32 [M][N][C] row-major,

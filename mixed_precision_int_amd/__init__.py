@@ -24,6 +24,8 @@ from .binding import (  # noqa: F401
     aq_linear_tile_partials_grouped,
     aq_quant_act_grouped,
     aq_linear_prefill,
+    aq_linear_prefill_prepared,
+    aq_prefill_prepare,
     aq_linear_tile_partials,
     aq_pack_weights,
     aq_plan_pack,

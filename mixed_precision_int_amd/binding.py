@@ -29,7 +29,8 @@ EXPORTS = ["aq_abi_version", "aq_status_string", "aq_labels_from_map", "aq_plan_
            "aq_linear_decode", "aq_linear_prefill", "aq_linear_tile_partials",
            "aq_quant_act_grouped", "aq_linear_decode_grouped", "aq_linear_prefill_grouped",
            "aq_linear_tile_partials_grouped", "aq_pack_weights_mse",
-           "aq_transform_rows", "aq_transform_out", "aq_transform_weights", "aq_quant_act_transformed"]
+           "aq_transform_rows", "aq_transform_out", "aq_transform_weights", "aq_quant_act_transformed",
+           "aq_prefill_prepare", "aq_linear_prefill_prepared"]
 
 
 class AqError(RuntimeError):
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
         "aq_linear_tile_partials_grouped": (i32, [ctypes.POINTER(AqPacked), vp, i32, vp, vp]),
         "aq_transform_rows": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
         "aq_transform_out": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp, vp]),
+        "aq_prefill_prepare": (i32, [ctypes.POINTER(AqPacked), vp, sz, vp]),
+        "aq_linear_prefill_prepared": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
         "aq_quant_act_transformed": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp, vp]),
         "aq_transform_weights": (i32, [vp, i32, i32, vp, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
     }
@@ -296,6 +299,30 @@ def aq_linear_prefill(pw: PackedWeights, qx, sx, bias=None, out=None, ws=None, s
     ws, ws_bytes = _workspace(pw, M, AQ_PHASE_PREFILL, ws, qx.device)
     _check(lib().aq_linear_prefill(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias),
                                    _ptr(out), _ptr(ws), ws_bytes, _stream(stream)), "aq_linear_prefill")
+    return out
+
+
+def aq_prefill_prepare(pw: PackedWeights, ws, stream=None):
+    """Write the long-prompt temporary INT8 operand of pw into ws (a device
+    uint8 tensor of at least aq_workspace_bytes(pw, 1024, prefill) bytes);
+    a no-op when the projection needs none."""
+    need = aq_workspace_bytes(pw, 1024, AQ_PHASE_PREFILL)
+    _check(lib().aq_prefill_prepare(ctypes.byref(pw.desc), _ptr(ws) if need else None,
+                                    ws.numel() * ws.element_size() if (need and ws is not None) else 0, _stream(stream)),
+           "aq_prefill_prepare")
+
+
+def aq_linear_prefill_prepared(pw: PackedWeights, qx, sx, ws, bias=None, out=None, stream=None):
+    """aq_linear_prefill over an operand aq_prefill_prepare already wrote to ws."""
+    import torch
+    M = qx.shape[0]
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=qx.device)
+    need = aq_workspace_bytes(pw, M, AQ_PHASE_PREFILL)
+    _check(lib().aq_linear_prefill_prepared(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias), _ptr(out),
+                                            _ptr(ws) if need else None,
+                                            ws.numel() * ws.element_size() if (need and ws is not None) else 0, _stream(stream)),
+           "aq_linear_prefill_prepared")
     return out
 
 

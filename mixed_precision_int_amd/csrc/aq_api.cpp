@@ -64,12 +64,16 @@ aq_status check_workspace(void *ws, size_t ws_bytes, size_t need) {
 }
 
 // Prefill dispatch (Y, or INT32 products into P when P != nullptr).
+// prepared: ws already holds the temporary INT8 operand (aq_prefill_prepare).
 hipError_t run_prefill(const aq::PackedView &v, const int8_t *qx, const float *sx, int M,
-                       const float *bias, float *Y, int32_t *P, void *ws, hipStream_t s) {
+                       const float *bias, float *Y, int32_t *P, void *ws, hipStream_t s,
+                       bool prepared = false) {
   if (!aq::prefill_long(v, M)) return aq::launch_prefill(v, qx, sx, M, bias, Y, P, s);
   const int8_t *E = v.w8;
   const float *Es = v.s8;
-  if (v.T4 > 0) {
+  if (v.T4 > 0 && prepared) {
+    aq::expand_layout(v, ws, &E, &Es);
+  } else if (v.T4 > 0) {
     const hipError_t e = aq::launch_expand(v, ws, s, &E, &Es);
     if (e != hipSuccess) return e;
   }
@@ -319,6 +323,37 @@ aq_status aq_linear_prefill(const aq_packed *W, const int8_t *qx, const float *s
   if (st != AQ_OK) return st;
   return run_prefill(v, qx, sx, M, bias, Y, nullptr, ws, static_cast<hipStream_t>(stream)) ==
                  hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
+aq_status aq_prefill_prepare(const aq_packed *W, void *ws, size_t ws_bytes, void *stream) {
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  const aq::PackedView v = aq::view_of(*W);
+  const size_t need = aq::prefill_workspace_bytes(v, aq::kLongPrefillM);
+  if (need == 0) return AQ_OK;  // no INT4 tile, or no long route: nothing to prepare
+  st = check_workspace(ws, ws_bytes, need);
+  if (st != AQ_OK) return st;
+  const int8_t *E;
+  const float *Es;
+  return aq::launch_expand(v, ws, static_cast<hipStream_t>(stream), &E, &Es) == hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
+aq_status aq_linear_prefill_prepared(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                                     const float *bias, float *Y, const void *ws, size_t ws_bytes,
+                                     void *stream) {
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  st = check_linear_io(W, qx, sx, M, bias, Y);
+  if (st != AQ_OK || M == 0) return st;
+  const aq::PackedView v = aq::view_of(*W);
+  st = check_workspace(const_cast<void *>(ws), ws_bytes, aq::prefill_workspace_bytes(v, M));
+  if (st != AQ_OK) return st;
+  return run_prefill(v, qx, sx, M, bias, Y, nullptr, const_cast<void *>(ws),
+                     static_cast<hipStream_t>(stream), true) == hipSuccess
              ? AQ_OK
              : AQ_ERR_HIP;
 }

@@ -67,6 +67,12 @@ size_t expand_bytes(const PackedView &w) {
   return ((e + 255) & ~(size_t)255) + s;
 }
 
+void expand_layout(const PackedView &w, const void *ws, const int8_t **E, const float **Es) {
+  const int8_t *e = static_cast<const int8_t *>(ws);
+  *E = e;
+  *Es = reinterpret_cast<const float *>(e + (((size_t)w.N * w.K + 255) & ~(size_t)255));
+}
+
 hipError_t launch_expand(const PackedView &w, void *ws, hipStream_t stream, const int8_t **E,
                          const float **Es) {
   int8_t *e = static_cast<int8_t *>(ws);

@@ -79,6 +79,8 @@ hipError_t launch_prefill_big(const int8_t *E, const float *Es, int N, int K, co
 size_t expand_bytes(const PackedView &w);
 hipError_t launch_expand(const PackedView &w, void *ws, hipStream_t stream, const int8_t **E,
                          const float **Es);
+// Where launch_expand puts the two parts inside ws (no launch).
+void expand_layout(const PackedView &w, const void *ws, const int8_t **E, const float **Es);
 
 // Prefill routing: prompts of at least kLongPrefillM rows run the GEMM over
 // INT8 tiles in logical order (the packed W8 buffer itself when the map has

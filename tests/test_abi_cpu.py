@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(aqlib):
 
 
 def test_abi_version_and_status_strings(aqlib):
-    assert B.aq_abi_version() == 5
+    assert B.aq_abi_version() == 6
     for code in list(B.STATUS) + [-99]:
         assert aqlib.aq_status_string(code)
 
@@ -237,3 +237,25 @@ def test_transform_entry_points_rejected(aqlib):
     bads[5, 63] = 0                            # a sign must be +-1
     assert L.aq_transform_out(FAKE, 4, 128, FAKE, ctypes.byref(B.transform_tables(perm, dl, bads)),
                               None, FAKE, None) == -8
+
+
+def test_prepared_prefill_rejected(aqlib):
+    """The split long-prompt route validates on the host: the preparation
+    needs the temporary-operand workspace when the projection has INT4
+    tiles (and is a no-op without them); the prepared GEMM needs it for a
+    long prompt and not for a short one."""
+    L = B.lib()
+    d = fake_packed(N=256, K=512, T4=8, T8=8)
+    need = L.aq_workspace_bytes(ctypes.byref(d), 1024, 1, 0)
+    assert need == 256 * 512 + 4 * 256 * 4
+    assert L.aq_prefill_prepare(ctypes.byref(d), None, 0, None) == -6
+    assert L.aq_prefill_prepare(ctypes.byref(d), FAKE, need - 1, None) == -6
+    assert L.aq_prefill_prepare(ctypes.byref(d), FAKE + 4, need, None) == -5
+    d8 = fake_packed(N=256, K=512, T4=0, T8=16)
+    assert L.aq_prefill_prepare(ctypes.byref(d8), None, 0, None) == 0          # nothing to prepare
+    pp = lambda dd, M, ws=None, n=0: L.aq_linear_prefill_prepared(ctypes.byref(dd), FAKE, FAKE, M, None, FAKE,
+                                                                  ws, n, None)
+    assert pp(d, 1024) == -6 and pp(d, 1024, FAKE, need - 1) == -6 and pp(d, 1024, FAKE + 4, need) == -5
+    assert pp(d, 0) == 0
+    assert L.aq_linear_prefill_prepared(ctypes.byref(d), None, FAKE, 4, None, FAKE, None, 0, None) == -1
+    assert L.aq_prefill_prepare(ctypes.byref(fake_packed(bK=96)), FAKE, need, None) == -3
