@@ -92,6 +92,11 @@ def parse():
                          "projections resident in HBM; quantization + linear per projection) at "
                          "M = 1, 8, 32, 64: enqueued ahead, captured in a HIP graph, and host-paced "
                          "wall-clock; print a markdown table")
+    ap.add_argument("--model-14b", action="store_true",
+                    help="only time the Qwen3-14B-shaped model workload (40 layers x 4 packed projections): "
+                         "a 65536-token prompt prefilled in 8 chunks of 8192 through all 160 projections, "
+                         "with the long-prompt operands built per call or prepared once and kept resident, "
+                         "then one batch-32 decode step; print a markdown table")
     ap.add_argument("--chunked-prefill", action="store_true",
                     help="only time a long prompt prefilled in chunks through Qwen3-14B-shaped projections: "
                          "the temporary INT8 operand prepared with every chunk (aq_linear_prefill) or once "
@@ -541,6 +546,103 @@ def model_step(aq, gen, torch, reps: int = 10):
     print("\n".join(rows))
 
 
+def model_14b(aq, gen, torch):
+    """The Qwen3-14B-shaped workload: 40 layers x (qkv 7168x5120, o 5120x5120,
+    gate_up 34816x5120, down 5120x17408), model-wide 30% INT8 tiles, packed
+    and resident.  Prefill: 8 chunks of 8192 tokens, chunk-major (each chunk
+    through all 160 projections, as a chunked prompt runs), per call the
+    activation quantization and the prefill linear; the long-prompt operands
+    are either built by every call or prepared once for all 160 projections
+    and kept resident (memory the 288 GB of HBM has room for), the
+    preparation timed on its own.  Then one batch-32 decode step over the
+    160 projections.  Launches are enqueued back to back; HIP events time
+    each part.  The prepared route's last outputs are compared bit for bit
+    with the per-call route's."""
+    from mixed_precision_int_amd.model import pack_model
+    dev = torch.device("cuda", 0)
+    maps = gen.qwen14b_maps()
+    model = pack_model(gen.QWEN14B, maps, lambda l, name, N, K: gen.device_weights(N, K, gen.seed_for(5, l, name)))
+    torch.cuda.synchronize()
+    print(f"packed model {model.nbytes() / 1e9:.3f} GB", flush=True)
+    M, chunks = 8192, 8
+    xs = {name: gen.device_acts_heavy_tail(M, K, seed=gen.act_seed(5, 0, name, 0)) for name, N, K in gen.QWEN14B}
+    q = {name: (torch.empty((M, K), dtype=torch.int8, device=dev), torch.empty((M,), dtype=torch.float32, device=dev))
+         for name, N, K in gen.QWEN14B}
+    ys = {name: torch.empty((M, N), dtype=torch.float32, device=dev) for name, N, K in gen.QWEN14B}
+    need = max(aq.aq_workspace_bytes(pw, M, aq.AQ_PHASE_PREFILL) for _, _, pw in model)
+    shared_ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+    ops = chunks * sum(2 * M * pw.N * pw.K for _, _, pw in model)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def prefill_per_call():
+        for _ in range(chunks):
+            for l, name, pw in model:
+                qx, sx = q[name]
+                aq.aq_quant_act(xs[name], qx, sx)
+                aq.aq_linear_prefill(pw, qx, sx, None, ys[name], shared_ws)
+
+    t_a = timed(prefill_per_call)
+    last_a = ys["down"].clone()
+    print(f"prefill, operand per call: {t_a:.1f} ms", flush=True)
+    wss = {}
+    for l, name, pw in model:
+        n = aq.aq_workspace_bytes(pw, M, aq.AQ_PHASE_PREFILL)
+        wss[(l, name)] = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+    resident = sum(w.numel() for w in wss.values() if w is not None)
+
+    def prepare_all():
+        for l, name, pw in model:
+            if wss[(l, name)] is not None:
+                aq.aq_prefill_prepare(pw, wss[(l, name)])
+
+    def prefill_prepared():
+        for _ in range(chunks):
+            for l, name, pw in model:
+                qx, sx = q[name]
+                aq.aq_quant_act(xs[name], qx, sx)
+                aq.aq_linear_prefill_prepared(pw, qx, sx, wss[(l, name)], None, ys[name])
+
+    t_p = timed(prepare_all)
+    t_b = timed(prefill_prepared)
+    same = bool(torch.equal(ys["down"], last_a))
+    print(f"prefill, prepared once: {t_p:.1f} + {t_b:.1f} ms", flush=True)
+    del wss, xs, q, ys, shared_ws
+    torch.cuda.empty_cache()
+    Md = 32
+    xd = {name: gen.device_acts_outliers(Md, K, seed=gen.act_seed(5, 0, name, 9)) for name, N, K in gen.QWEN14B}
+    qd = {name: aq.aq_quant_act(xd[name]) for name, N, K in gen.QWEN14B}
+    yd = {name: torch.empty((Md, N), dtype=torch.float32, device=dev) for name, N, K in gen.QWEN14B}
+    dneed = max(aq.aq_workspace_bytes(pw, Md, aq.AQ_PHASE_DECODE) for _, _, pw in model)
+    dws = torch.zeros(max(16, dneed), dtype=torch.uint8, device=dev)
+    dbytes = sum(linear_bytes(pw.plan, Md) for _, _, pw in model)
+
+    def decode_step():
+        for l, name, pw in model:
+            qx, sx = qd[name]
+            aq.aq_quant_act(xd[name], qx, sx)
+            aq.aq_linear_decode(pw, qx, sx, None, 0, yd[name], dws)
+
+    decode_step()
+    t_d = min(timed(decode_step) for _ in range(3))
+    rows = [f"Packed model: {model.nbytes() / 1e9:.3f} GB resident; prepared operands: {resident / 1e9:.2f} GB.", "",
+            "| part | ms | rate |", "|---|---|---|",
+            f"| 65536-token prefill, 8 x 8192 chunks, operand built by every call | {t_a:.1f} | {ops / t_a / 1e9:.0f} TOPS |",
+            f"| operands of all 160 projections prepared once | {t_p:.1f} | |",
+            f"| 65536-token prefill over the prepared operands | {t_b:.1f} | {ops / t_b / 1e9:.0f} TOPS |",
+            f"| prepared total (preparation + prefill); outputs equal to the per-call route: {same} | {t_p + t_b:.1f} | "
+            f"{ops / (t_p + t_b) / 1e9:.0f} TOPS |",
+            f"| batch-32 decode step, 160 projections (best of 3) | {t_d:.3f} | {dbytes / t_d / 1e6:.0f} GB/s |"]
+    print("\n".join(rows))
+
+
 def chunked_prefill(aq, gen, torch):
     """A 16K-token prompt prefilled in chunks of 1024 or 8192 tokens through
     Qwen3-14B-shaped projections (30% INT8 tiles in bands): the long-prompt
@@ -742,6 +844,9 @@ def main():
         ceilings(torch)
         return
     aq.lib()
+    if args.model_14b:
+        model_14b(aq, gen, torch)
+        return
     if args.chunked_prefill:
         chunked_prefill(aq, gen, torch)
         return
