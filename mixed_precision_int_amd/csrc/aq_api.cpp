@@ -413,7 +413,7 @@ aq_status run_row_transform(int kind, const float *src, int M, int K, const int8
   aq_status st = check_tables(t);
   if (st != AQ_OK) return st;
   if (!aligned16(src) || !aligned16(dst) || (bias && !aligned16(bias))) return AQ_ERR_ALIGN;
-  if ((long long)M * K > (1LL << 40) || (K / 64 + 15) / 16 > 65535) return AQ_ERR_SHAPE;
+  if ((long long)M * K > (1LL << 40)) return AQ_ERR_SHAPE;
   return aq::launch_transform(kind, src, dst, M, K, seeds, nullptr, bias, *t,
                               static_cast<hipStream_t>(stream)) == hipSuccess
              ? AQ_OK
@@ -444,6 +444,7 @@ aq_status aq_quant_act_transformed(const float *X, int M, int K, const int8_t *v
   aq_status st = check_tables(tables_host);
   if (st != AQ_OK) return st;
   if (!aligned16(X) || !aligned16(qx) || !aligned4(sx)) return AQ_ERR_ALIGN;
+  if ((long long)M * K > (1LL << 40)) return AQ_ERR_SHAPE;
   return aq::launch_quant_act_transformed(X, M, K, vseeds, *tables_host, qx, sx,
                                           static_cast<hipStream_t>(stream)) == hipSuccess
              ? AQ_OK
