@@ -34,8 +34,10 @@ eq. 19 counterpart; the per-token form above is the default path.
 
 Parity status: every function here is pinned by tests/test_oracle_*.py
 (hand-worked fixtures under tests/golden/, closed forms, brute force and
-invariants).  Parity with numbers printed on the pages is unpinned for the
-linear outputs themselves: the pages print no per-layer input/output example.
+invariants).  The pages print no per-layer input/output example, so no pin
+of the linear outputs uses numbers printed there; those outputs are pinned by
+the hand-worked 2 x 2-tile fixture, brute-force sums and the textbook
+special cases (uniform maps, a single tile column).
 """
 
 from __future__ import annotations
