@@ -48,6 +48,10 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 constexpr int kBM = 256, kBN = 256, kBK = 128, kNP = 8;
 
+// Cache policy of the output stores: non-temporal (bit 1), so the FP32
+// outputs, never read again here, leave the caches to the operand slabs.
+constexpr int kStoreNT = 2;
+
 // s_waitcnt: all vector-memory and LDS/scalar accesses of this wave done.
 constexpr int kWaitAll = (7 << 4);
 
@@ -252,8 +256,8 @@ __global__ __launch_bounds__(512, 1) void prefill_big_kernel(const BigArgs a) {
           const float v0 = fmaf(F[fm][0][4 * e4 + e3], sv[e3], b0);
           const float v1 = fmaf(F[fm][1][4 * e4 + e3], sv[e3], b1);
           if (live && (full || m0 + mrel < a.M)) {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), rY, y_lane, soff, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), rY, y_lane + 128u, soff, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), rY, y_lane, soff, kStoreNT);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), rY, y_lane + 128u, soff, kStoreNT);
           }
         }
       }

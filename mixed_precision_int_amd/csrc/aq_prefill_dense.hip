@@ -339,7 +339,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
           const size_t n = (size_t)rw * 64 + fn * 32 + (lane & 31);
           float v = F[fm][fn][e] * sxm;
           if (a.bias) v += a.bias[n];
-          a.Y[(size_t)m * a.N + n] = v;
+          // non-temporal: the outputs are not read again here, and keeping them
+          // out of the caches leaves room for the operand slabs other blocks re-read
+          __builtin_nontemporal_store(v, a.Y + (size_t)m * a.N + n);
         }
       }
   }
