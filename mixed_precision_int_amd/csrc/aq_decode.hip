@@ -40,15 +40,17 @@
 //            is in flight; when they do not fit, lanes read them from global
 //            memory instead.
 //
-// Products (the pages split decode the same way, Table 5):
-//   M = 1 : v_dot4_i32_i8 on the vector ALU (a 4-way byte dot product); a
-//           lane accumulates its 32 columns per tile and the four k-groups
-//           are summed across lanes (swizzle / permute) before the split
-//           reduction;
-//   M > 1 : v_mfma_i32_16x16x64_i8 with up to 16 tokens as the A operand and
-//           the 16 weight rows as the B operand, C[token 4g+e][row i16]; per
-//           extra token the byte dot products would cost the vector ALU and
-//           LDS a full operand pass each.
+// Products (the pages split decode by M too, Table 5, with byte dot
+// products for one token):
+//   MFMA  : v_mfma_i32_16x16x64_i8 with up to 16 tokens as the A operand and
+//           the 16 weight rows as the B operand, C[token 4g+e][row i16]; for
+//           every M of the per-token route, one token included (the padding
+//           rows cost the matrix core, not the vector ALU or the memory
+//           path, and measured 1-3% faster than the dot products);
+//   VALU  : v_dot4_i32_i8 (a 4-way byte dot product) for the one-token
+//           grouped route; a lane accumulates its 32 columns per tile and
+//           the four k-groups are summed across lanes (swizzle / permute)
+//           before the split reduction.
 // Each tile's INT32 product is rescaled by its per-row FP32 scale into FP32
 // accumulators (eq. 19).  INT4 tiles are widened x16 (see w4_lo16), so their
 // scale is multiplied by the exact factor 1/16.
@@ -767,7 +769,11 @@ DecodePlan plan_decode(const PackedView &w, int M, int split) {
   p.MG = mgroups(w, M);
   p.waves = waves_of(w, M);
   p.mchunks = mchunks_of(w, M);
-  p.mode = M <= kValuMaxM ? kValu : kMfma;
+  // Products on MFMA for every M (with one token, 15 of the 16 A-operand rows
+  // are padding, yet it measured 1-3% faster than the vector-ALU dot
+  // products); launch_decode keeps the vector ALU for the one-token grouped
+  // route, where it measured about 1% faster.
+  p.mode = kMfma;
   p.Z = 1;
   p.ylaunch = p.mchunks;
   p.xstride = 0;
@@ -829,8 +835,9 @@ size_t decode_workspace_bytes(const PackedView &w, int M, int split) {
 hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx, int M,
                          const float *bias, float *Y, int split, void *ws, int32_t *P,
                          hipStream_t stream, bool grouped) {
-  const DecodePlan p = plan_decode(w, M, split);
+  DecodePlan p = plan_decode(w, M, split);
   if (!decode_plan_ok(p, w) || p.ylaunch < 1) return hipErrorInvalidValue;
+  if (grouped && M <= kValuMaxM) p.mode = kValu;
   DecodeArgs args;
   args.labels = w.labels; args.off4 = w.off4; args.off8 = w.off8;
   args.w4 = w.w4; args.w8 = w.w8; args.s4 = w.s4; args.s8 = w.s8;
