@@ -106,6 +106,24 @@ template <> struct DArgs<true> : DecodeArgs { uint32_t meta[kInlineWords]; };
 
 __device__ __forceinline__ v4i load16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
 
+// Weight panels: with NT the loads are non-temporal, so that a projection
+// streamed once per call does not evict what the caches hold for others.
+template <bool NT>
+__device__ __forceinline__ v4i wload16(const void *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+  else return load16(p);
+}
+template <bool NT>
+__device__ __forceinline__ uint2 wload8(const void *p) {
+  if constexpr (NT) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    return make_uint2(v.x, v.y);
+  } else {
+    return *reinterpret_cast<const uint2 *>(p);
+  }
+}
+
 // Device-coherent FP32x4 store / load (agent-scope relaxed atomics, one per
 // element): visible across the whole GPU without cache maintenance.
 __device__ __forceinline__ void store_coherent(float4 *p, float4 v) {
@@ -183,7 +201,7 @@ __device__ __forceinline__ v4i x_operand(const int8_t *row, int colbase, int g, 
 }
 
 template <int BK, int MODE, int MG, int WAVES, int RG, int DEPTH, int XMODE, bool PARTIALS, bool INL,
-          bool GRP>
+          bool GRP, bool WNT>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) {
   constexpr int KS = BK / 64;    // MFMA steps (16-byte operands per lane) per tile
   constexpr int S = WAVES / RG;  // splits per row group
@@ -339,27 +357,27 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
             /* 2u + g/2, nibble g % 2 */                                                         \
             if (is4) {                                                                          \
               const uint8_t *base = w4p + (size_t)idx * 4096 + (g >> 1) * 1024 + rowoff;        \
-              W[d][0] = load16(base);                                                           \
-              W[d][1] = load16(base + 2048);                                                    \
+              W[d][0] = wload16<WNT>(base);                                                           \
+              W[d][1] = wload16<WNT>(base + 2048);                                                    \
             } else {                                                                            \
               const uint8_t *base = w8p + (size_t)idx * 8192 + g * 1024 + rowoff;               \
-              W[d][0] = load16(base);                                                           \
-              W[d][1] = load16(base + 4096);                                                    \
+              W[d][0] = wload16<WNT>(base);                                                           \
+              W[d][1] = wload16<WNT>(base + 4096);                                                    \
             }                                                                                   \
           } else if (BK == 128) {                                                               \
             if (is4) {                                                                          \
-              W[d][0] = load16(w4p + (size_t)idx * 4096 + g * 1024 + rowoff);                   \
+              W[d][0] = wload16<WNT>(w4p + (size_t)idx * 4096 + g * 1024 + rowoff);                   \
             } else {                                                                            \
               const uint8_t *base = w8p + (size_t)idx * 8192 + (2 * g) * 1024 + rowoff;         \
-              W[d][0] = load16(base);                                                           \
-              W[d][1] = load16(base + 1024);                                                    \
+              W[d][0] = wload16<WNT>(base);                                                           \
+              W[d][1] = wload16<WNT>(base + 1024);                                                    \
             }                                                                                   \
           } else {                                                                              \
             if (is4) {                                                                          \
-              const uint2 lo = load8(w4p + (size_t)idx * 2048 + (g >> 1) * 1024 + rowoff + 8 * (g & 1)); \
+              const uint2 lo = wload8<WNT>(w4p + (size_t)idx * 2048 + (g >> 1) * 1024 + rowoff + 8 * (g & 1)); \
               W[d][0] = v4i{(int)lo.x, (int)lo.y, 0, 0};                                        \
             } else {                                                                            \
-              W[d][0] = load16(w8p + (size_t)idx * 4096 + g * 1024 + rowoff);                   \
+              W[d][0] = wload16<WNT>(w8p + (size_t)idx * 4096 + g * 1024 + rowoff);                   \
             }                                                                                   \
           }                                                                                     \
           SC[d] = (is4 ? a.s4 : a.s8)[(size_t)idx * 64 + rg * 16 + i16];                        \
@@ -663,32 +681,48 @@ void launch_one(Kern kern, dim3 grid, dim3 block, size_t lds, hipStream_t stream
 
 // Grid: row blocks (4R/RG) along x, token chunks along y, column chunks
 // along z.
-template <int BK, int MODE, int MG, int WAVES, int DEPTH, int XMODE, bool PARTIALS, bool INL, bool GRP>
+template <int BK, int MODE, int MG, int WAVES, int DEPTH, int XMODE, bool PARTIALS, bool INL, bool GRP,
+          bool WNT>
 void launch_rg(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL> &args) {
   const dim3 block(WAVES * 64);
   const int y = args.ychunks, z = p.Z;
   switch (p.RG) {
-    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS, INL, GRP>, dim3(R, y, z), block, p.lds, stream, args); break;
-    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS, INL, GRP>, dim3(R * 2, y, z), block, p.lds, stream, args); break;
-    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS, INL, GRP>, dim3(R * 4, y, z), block, p.lds, stream, args); break;
+    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS, INL, GRP, WNT>, dim3(R, y, z), block, p.lds, stream, args); break;
+    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS, INL, GRP, WNT>, dim3(R * 2, y, z), block, p.lds, stream, args); break;
+    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS, INL, GRP, WNT>, dim3(R * 4, y, z), block, p.lds, stream, args); break;
   }
 }
 
+// Weights are loaded non-temporally when the call passes over them once
+// (one token chunk): measured 4-10% faster where they stream from HBM.  A
+// call of several token chunks re-reads them, and the later chunks find them
+// in the last-level cache only if the first chunk's loads allocated there.
 template <int BK, bool PARTIALS, bool INL, bool GRP>
 void launch_mode(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL> &args) {
   if (p.mode == kValu) {
-    launch_rg<BK, kValu, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP>(p, R, stream, args);
+    launch_rg<BK, kValu, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP, true>(p, R, stream, args);
     return;
   }
   if (p.xmode == kXPriv) {
-    launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP>(p, R, stream, args);
+    launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP, true>(p, R, stream, args);
     return;
   }
-  switch (p.MG) {
-    case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, PARTIALS, INL, GRP>(p, R, stream, args); break;
-    case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, PARTIALS, INL, GRP>(p, R, stream, args); break;
-    case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, PARTIALS, INL, GRP>(p, R, stream, args); break;
-    default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, PARTIALS, INL, GRP>(p, R, stream, args); break;
+  if (PARTIALS || p.mchunks == 1) {
+    switch (p.MG) {
+      case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, PARTIALS, INL, GRP, true>(p, R, stream, args); break;
+      case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, PARTIALS, INL, GRP, true>(p, R, stream, args); break;
+      case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, PARTIALS, INL, GRP, true>(p, R, stream, args); break;
+      default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, PARTIALS, INL, GRP, true>(p, R, stream, args); break;
+    }
+    return;
+  }
+  if constexpr (!PARTIALS) {
+    switch (p.MG) {
+      case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, false, INL, GRP, false>(p, R, stream, args); break;
+      case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, false, INL, GRP, false>(p, R, stream, args); break;
+      case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, false, INL, GRP, false>(p, R, stream, args); break;
+      default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, false, INL, GRP, false>(p, R, stream, args); break;
+    }
   }
 }
 
