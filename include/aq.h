@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AQ_ABI_VERSION 6
+#define AQ_ABI_VERSION 7
 
 typedef enum aq_status {
   AQ_OK = 0,
@@ -354,6 +354,21 @@ aq_status aq_transform_rows(const float *X, int M, int K, const int8_t *vseeds,
 aq_status aq_transform_out(const float *Yt, int M, int N, const int8_t *useeds,
                            const aq_transform_tables *tables_host, const float *bias, float *Y,
                            void *stream);
+
+/* The transformed layer's prefill linear (App. B.1 eq. 4 around App. E.3
+ * eq. 19): Y = Y~ U + bias, Y~ the
+ * aq_linear_prefill product of the transformed operands (W~ packed, qx / sx
+ * from aq_quant_act_transformed).  Long prompts (the long-prompt route of
+ * aq_linear_prefill) apply U in the GEMM's epilogue, where each wave holds
+ * the 64 outputs of a tile row per token, before the token scale and the
+ * bias; shorter prompts run the linear and then aq_transform_out.  Within
+ * FP32 rounding of aq_linear_prefill followed by aq_transform_out.
+ *   useeds   device INT8 [N/64];  tables_host as for the transforms
+ * Other arguments, workspace and errors as aq_linear_prefill. */
+aq_status aq_linear_prefill_transformed(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                                        const float *bias, const int8_t *useeds,
+                                        const aq_transform_tables *tables_host, float *Y, void *ws,
+                                        size_t ws_bytes, void *stream);
 
 /* aq_quant_act of X~ = X V in one pass: the same codes and scales as
  * aq_transform_rows followed by aq_quant_act, bit for bit, with the

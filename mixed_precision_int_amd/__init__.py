@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     aq_quant_act_grouped,
     aq_linear_prefill,
     aq_linear_prefill_prepared,
+    aq_linear_prefill_transformed,
     aq_prefill_prepare,
     aq_linear_tile_partials,
     aq_pack_weights,

@@ -30,7 +30,7 @@ EXPORTS = ["aq_abi_version", "aq_status_string", "aq_labels_from_map", "aq_plan_
            "aq_quant_act_grouped", "aq_linear_decode_grouped", "aq_linear_prefill_grouped",
            "aq_linear_tile_partials_grouped", "aq_pack_weights_mse",
            "aq_transform_rows", "aq_transform_out", "aq_transform_weights", "aq_quant_act_transformed",
-           "aq_prefill_prepare", "aq_linear_prefill_prepared"]
+           "aq_prefill_prepare", "aq_linear_prefill_prepared", "aq_linear_prefill_transformed"]
 
 
 class AqError(RuntimeError):
@@ -100,6 +100,8 @@ def lib() -> ctypes.CDLL:
         "aq_transform_rows": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
         "aq_transform_out": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp, vp]),
         "aq_prefill_prepare": (i32, [ctypes.POINTER(AqPacked), vp, sz, vp]),
+        "aq_linear_prefill_transformed": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp,
+                                                ctypes.POINTER(AqTransformTables), vp, vp, sz, vp]),
         "aq_linear_prefill_prepared": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
         "aq_quant_act_transformed": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp, vp]),
         "aq_transform_weights": (i32, [vp, i32, i32, vp, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
@@ -513,4 +515,22 @@ def aq_transform_weights(W, useeds, vseeds, tables, out=None, stream=None):
                                       ctypes.c_void_p(sv.data_ptr()), ctypes.byref(t),
                                       ctypes.c_void_p(out.data_ptr()), _stream(stream)),
            "aq_transform_weights")
+    return out
+
+
+def aq_linear_prefill_transformed(pw: PackedWeights, qx, sx, useeds, tables, bias=None, out=None, ws=None,
+                                  stream=None):
+    """Y = Y~ U + bias for a transformed layer (long prompts apply U inside
+    the GEMM): FP32 [M, N]."""
+    import torch
+    M = qx.shape[0]
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=qx.device)
+    ws, ws_bytes = _workspace(pw, M, AQ_PHASE_PREFILL, ws, qx.device)
+    sd = _seeds_dev(useeds, pw.N // 64, qx.device)
+    t = _tables(tables)
+    _check(lib().aq_linear_prefill_transformed(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias),
+                                               ctypes.c_void_p(sd.data_ptr()), ctypes.byref(t), _ptr(out),
+                                               _ptr(ws), ws_bytes, _stream(stream)),
+           "aq_linear_prefill_transformed")
     return out

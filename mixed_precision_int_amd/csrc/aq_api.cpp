@@ -469,4 +469,37 @@ aq_status aq_transform_weights(const float *W, int N, int K, const int8_t *useed
              : AQ_ERR_HIP;
 }
 
+aq_status aq_linear_prefill_transformed(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                                        const float *bias, const int8_t *useeds,
+                                        const aq_transform_tables *tables_host, float *Y, void *ws,
+                                        size_t ws_bytes, void *stream) {
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  st = check_linear_io(W, qx, sx, M, bias, Y);
+  if (st != AQ_OK || M == 0) return st;
+  if (!useeds) return AQ_ERR_NULL;
+  st = check_tables(tables_host);
+  if (st != AQ_OK) return st;
+  const aq::PackedView v = aq::view_of(*W);
+  st = check_workspace(ws, ws_bytes, aq::prefill_workspace_bytes(v, M));
+  if (st != AQ_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (aq::prefill_long(v, M)) {
+    // the long-prompt GEMM applies U in its epilogue
+    const int8_t *E = v.w8;
+    const float *Es = v.s8;
+    if (v.T4 > 0 && aq::launch_expand(v, ws, s, &E, &Es) != hipSuccess) return AQ_ERR_HIP;
+    return aq::launch_prefill_dense(E, Es, v.N, v.K, v.bK, qx, sx, M, bias, Y, nullptr, s, useeds,
+                                    tables_host) == hipSuccess
+               ? AQ_OK
+               : AQ_ERR_HIP;
+  }
+  // short prompts: the linear, then the output transform, which adds the bias
+  if (aq::launch_prefill(v, qx, sx, M, nullptr, Y, nullptr, s) != hipSuccess) return AQ_ERR_HIP;
+  return aq::launch_transform(aq::kTransformOut, Y, Y, M, v.N, useeds, nullptr, bias, *tables_host, s) ==
+                 hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
 }  // extern "C"

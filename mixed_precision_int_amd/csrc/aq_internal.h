@@ -60,9 +60,14 @@ hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx
 // Long-prefill GEMM over INT8 tiles in logical tile order: E holds tile
 // (r, j) at (r*C + j) * 64*bK bytes (b_K/16 panels of [64][16]) and Es its
 // 64 FP32 row scales at (r*C + j) * 64.  P != nullptr writes INT32 products.
+// useeds (device, R seeds) and tables, when given, apply the output
+// transform of App. B.1 (Y = Y~ U) in the epilogue, before the token scale
+// and the bias.
 hipError_t launch_prefill_dense(const int8_t *E, const float *Es, int N, int K, int bK,
                                 const int8_t *qx, const float *sx, int M, const float *bias,
-                                float *Y, int32_t *P, hipStream_t stream);
+                                float *Y, int32_t *P, hipStream_t stream,
+                                const int8_t *useeds = nullptr,
+                                const aq_transform_tables *tables = nullptr);
 
 // Persistent 256 x 256-tile variant of the long-prefill GEMM (b_K = 128,
 // N >= 6144, at least one tile per compute unit, M*N < 2^29); same operands;

@@ -42,6 +42,16 @@ namespace {
 #define AQ_DENSE_S 3
 #endif
 
+// The output transform of App. B.1 (Y = Y~ U, U_r = Phi_{u_r}^T per 64-row
+// tile row): the six signed permutations, perm rows and sign masks (bit i
+// set: element i negated).
+// Sign tables as bit masks, one 32-bit word per half of the block: bit l of
+// word f is set where element 32 f + l is flipped.
+struct OutTables {
+  uint8_t perm[kTransformSeeds][64];
+  uint32_t dlm[kTransformSeeds][2], drm[kTransformSeeds][2];
+};
+
 struct DenseArgs {
   const int8_t *qx;
   const int8_t *E;
@@ -50,7 +60,48 @@ struct DenseArgs {
   float *Y;
   int32_t *P;
   int N, K, R, C, M, MB, NB;
+  const int8_t *useeds;  // output transform: per tile row seed (-1 .. 6), or null
+  OutTables ot;
 };
+
+__device__ __forceinline__ float sflip(float v, uint32_t bit) {
+  return __uint_as_float(__float_as_uint(v) ^ (bit << 31));
+}
+
+// Phi_s on the 64 outputs of one tile row for one token: element
+// i = 32 fn + l32 is register fn of lane l32 of the lane's half-wave.
+// D_R, then H_64 (stages h = 1 .. 16 across lanes, 32 across the two
+// registers, then 1/8), then P (position i takes element perm[i]), then
+// D_L; a seed outside -1 .. 6 gives NaN.
+__device__ __forceinline__ void phi_pair(float &v0, float &v1, int s, int lane, uint32_t dr0,
+                                         uint32_t dr1, uint32_t dl0, uint32_t dl1, int src0, int src1,
+                                         bool hi0, bool hi1) {
+  if (s < 0) return;
+  const int l32 = lane & 31;
+  if (s >= 1) {
+    v0 = sflip(v0, dr0);
+    v1 = sflip(v1, dr1);
+  }
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+    const float p0 = __shfl_xor(v0, h), p1 = __shfl_xor(v1, h);
+    v0 = (l32 & h) ? p0 - v0 : v0 + p0;
+    v1 = (l32 & h) ? p1 - v1 : v1 + p1;
+  }
+  {
+    const float a0 = v0, a1 = v1;
+    v0 = (a0 + a1) * 0.125f;
+    v1 = (a0 - a1) * 0.125f;
+  }
+  if (s >= 1) {
+    const float w00 = __int_as_float(__builtin_amdgcn_ds_bpermute(src0, __float_as_int(v0)));
+    const float w01 = __int_as_float(__builtin_amdgcn_ds_bpermute(src0, __float_as_int(v1)));
+    const float w10 = __int_as_float(__builtin_amdgcn_ds_bpermute(src1, __float_as_int(v0)));
+    const float w11 = __int_as_float(__builtin_amdgcn_ds_bpermute(src1, __float_as_int(v1)));
+    v0 = sflip(hi0 ? w01 : w00, dl0);
+    v1 = sflip(hi1 ? w11 : w10, dl1);
+  }
+}
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -62,7 +113,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds, uint3
 // loads of this wave are outstanding and all LDS/scalar accesses are done.
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
-template <int BK, int WM, int WN, int S, bool PARTIALS>
+template <int BK, int WM, int WN, int S, bool PARTIALS, bool XFORM>
 __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const DenseArgs a) {
   constexpr int NW = WM * WN;
   constexpr int BM = 64 * WM, BN = 64 * WN;
@@ -327,6 +378,38 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
         }
     }
     if (rw >= a.R) return;
+    if constexpr (XFORM) {
+      // Y = Y~ U on this wave's tile row (the 64 outputs of a token sit in
+      // one half-wave), before the token scale and the bias
+      const int s = a.useeds[rw];
+      if (s < -1 || s > kTransformSeeds) {
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) F[fm][0][e] = F[fm][1][e] = __builtin_nanf("");
+      } else if (s >= 0) {
+        const int l32 = lane & 31;
+        uint32_t dl0 = 0, dl1 = 0, dr0 = 0, dr1 = 0;
+        int src0 = 0, src1 = 0;
+        bool hi0 = false, hi1 = false;
+        if (s >= 1) {
+          dr0 = (a.ot.drm[s - 1][0] >> l32) & 1u;
+          dr1 = (a.ot.drm[s - 1][1] >> l32) & 1u;
+          dl0 = (a.ot.dlm[s - 1][0] >> l32) & 1u;
+          dl1 = (a.ot.dlm[s - 1][1] >> l32) & 1u;
+          const int j0 = a.ot.perm[s - 1][l32], j1 = a.ot.perm[s - 1][32 + l32];
+          src0 = 4 * ((lane & 32) | (j0 & 31));
+          src1 = 4 * ((lane & 32) | (j1 & 31));
+          hi0 = j0 >= 32;
+          hi1 = j1 >= 32;
+        }
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            phi_pair(F[fm][0][e], F[fm][1][e], s, lane, dr0, dr1, dl0, dl1, src0, src1, hi0, hi1);
+      }
+    }
 #pragma unroll
     for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
@@ -351,9 +434,11 @@ template <int BK, int WM, int WN, int S>
 hipError_t launch_dense_cfg(const DenseArgs &args, bool partials, hipStream_t stream) {
   const dim3 grid(args.MB * args.NB), block(64 * WM * WN);
   if (partials)
-    hipLaunchKernelGGL((prefill_dense_kernel<BK, WM, WN, S, true>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((prefill_dense_kernel<BK, WM, WN, S, true, false>), grid, block, 0, stream, args);
+  else if (args.useeds)
+    hipLaunchKernelGGL((prefill_dense_kernel<BK, WM, WN, S, false, true>), grid, block, 0, stream, args);
   else
-    hipLaunchKernelGGL((prefill_dense_kernel<BK, WM, WN, S, false>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((prefill_dense_kernel<BK, WM, WN, S, false, false>), grid, block, 0, stream, args);
   return hipGetLastError();
 }
 
@@ -361,9 +446,20 @@ hipError_t launch_dense_cfg(const DenseArgs &args, bool partials, hipStream_t st
 
 hipError_t launch_prefill_dense(const int8_t *E, const float *Es, int N, int K, int bK,
                                 const int8_t *qx, const float *sx, int M, const float *bias,
-                                float *Y, int32_t *P, hipStream_t stream) {
+                                float *Y, int32_t *P, hipStream_t stream, const int8_t *useeds,
+                                const TransformTables *tables) {
   constexpr int WM = AQ_DENSE_WM, WN = AQ_DENSE_WN, S = AQ_DENSE_S;
   DenseArgs args;
+  args.useeds = useeds;
+  args.ot = OutTables{};
+  if (useeds && tables) {
+    for (int r = 0; r < kTransformSeeds; ++r)
+      for (int e = 0; e < 64; ++e) {
+        args.ot.perm[r][e] = tables->perm[r][e];
+        if (tables->dl[r][e] < 0) args.ot.dlm[r][e >> 5] |= 1u << (e & 31);
+        if (tables->dr[r][e] < 0) args.ot.drm[r][e >> 5] |= 1u << (e & 31);
+      }
+  }
   args.qx = qx; args.E = E; args.Es = Es; args.sx = sx; args.bias = bias; args.Y = Y; args.P = P;
   args.N = N; args.K = K; args.R = N / 64; args.C = K / bK; args.M = M;
   args.MB = (M + 64 * WM - 1) / (64 * WM);

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(aqlib):
 
 
 def test_abi_version_and_status_strings(aqlib):
-    assert B.aq_abi_version() == 6
+    assert B.aq_abi_version() == 7
     for code in list(B.STATUS) + [-99]:
         assert aqlib.aq_status_string(code)
 
@@ -259,3 +259,15 @@ def test_prepared_prefill_rejected(aqlib):
     assert pp(d, 0) == 0
     assert L.aq_linear_prefill_prepared(ctypes.byref(d), None, FAKE, 4, None, FAKE, None, 0, None) == -1
     assert L.aq_prefill_prepare(ctypes.byref(fake_packed(bK=96)), FAKE, need, None) == -3
+
+
+def test_prefill_transformed_rejected(aqlib):
+    from workloads import gen
+    L = B.lib()
+    t = B.transform_tables(*gen.transform_tables())
+    d = fake_packed()
+    f = lambda **k: L.aq_linear_prefill_transformed(ctypes.byref(d), FAKE, FAKE, k.get("M", 4), None,
+                                                    k.get("us", FAKE), k.get("t", ctypes.byref(t)), FAKE,
+                                                    k.get("ws", None), k.get("n", 0), None)
+    assert f(M=0) == 0 and f(us=None) == -1 and f(t=None) == -1
+    assert f(M=1024) == -6                     # long prompt with INT4 tiles: the operand workspace

@@ -222,3 +222,70 @@ def test_transforms_full_prefill_size_sampled(proj):
     assert_bits_equal(sx.cpu().numpy()[rows], sx_r, f"{proj}: scales")
     ref = O.transform_out(Yt[rows], us, TABLES) + b.astype(np.float64)[None, :]
     assert_blocks_close(Y.cpu().numpy()[rows], ref, f"{proj}: Y", src=Yt[rows])
+
+
+@pytest.mark.parametrize("N,K,bK,M,bias", [(256, 1024, 128, 1030, True), (320, 2560, 128, 2048, False),
+                                           (256, 640, 64, 1040, True), (192, 768, 128, 100, True),
+                                           (6144, 2560, 128, 2048, True)])
+def test_prefill_transformed(N, K, bK, M, bias):
+    """Y = Y~ U + bias with U applied inside the long-prompt GEMM's epilogue
+    (M >= 1024; the short route runs the two calls): within FP32 rounding of
+    aq_linear_prefill followed by aq_transform_out (per 64-block,
+    |difference|_2 <= 1e-5 |y~|_2: the token scale is applied after U instead
+    of before), and every seed value on some tile row."""
+    rng = np.random.default_rng(N + K + M)
+    W = gen.weights(rng, N, K)
+    R, C = N // 64, K // bK
+    z = gen.map_uniform(rng, R, C, 0.35)
+    X = gen.acts_heavy_tail(rng, M, K)
+    us = every_seed(rng, R)
+    b = to_dev(rng.standard_normal(N).astype(np.float32)) if bias else None
+    say(f"  prefill_transformed {N}x{K}/bK{bK}/M{M}")
+    pw = aq.aq_pack_weights(to_dev(W), aq.aq_labels_from_map(z.astype(np.uint8)), 64, bK)
+    qx, sx = aq.aq_quant_act(to_dev(X))
+    Yt = aq.aq_linear_prefill(pw, qx, sx)
+    ref = aq.aq_transform_out(Yt, us, TABLES, bias=b)
+    Y = aq.aq_linear_prefill_transformed(pw, qx, sx, us, TABLES, bias=b)
+    Y2 = aq.aq_linear_prefill_transformed(pw, qx, sx, us, TABLES, bias=b)
+    torch.cuda.synchronize()
+    assert_blocks_close(Y.cpu().numpy(), ref.cpu().numpy().astype(np.float64), f"{N}x{K}/M{M}", rel=1e-5,
+                        src=Yt.cpu().numpy())
+    # every wave of every launch takes the same sign tables: repeated calls agree bit for bit
+    assert torch.equal(Y, Y2), f"{N}x{K}/M{M}: repeated calls differ"
+
+
+def test_prefill_transformed_against_oracle():
+    """The fused route end to end on sampled rows: W~ = U W V packed, X~
+    quantized in one pass, Y = Y~ U + bias from the GEMM epilogue, against the
+    oracle's transformed layer."""
+    N, K, M = 320, 2560, 1030
+    rng = np.random.default_rng(17)
+    W = gen.weights(rng, N, K)
+    X = gen.acts_outliers(rng, M, K, 25, 25.0)
+    z = gen.map_uniform(rng, N // 64, K // 128, 0.35)
+    us, vs = every_seed(rng, N // 64), every_seed(rng, K // 64)
+    b = rng.standard_normal(N).astype(np.float32)
+    rows = np.array([0, 1, 63, 64, 511, 1029])
+    Wt_r = O.transform_weights(W, us, vs, TABLES)
+    codes, sW = O.quant_weights(Wt_r, z, 64, 128)
+    qx_r, sx_r = O.quant_act(O.transform_rows(X[rows], vs, TABLES))
+    P = O.tile_partials(qx_r, codes, 128)
+    y_ref = O.transform_out(O.linear_from_partials(P, sx_r, sW), us, TABLES) + b.astype(np.float64)[None, :]
+    pw = aq.aq_pack_weights(aq.aq_transform_weights(to_dev(W), us, vs, TABLES),
+                            aq.aq_labels_from_map(z.astype(np.uint8)), 64, 128)
+    qx, sx = aq.aq_quant_act_transformed(to_dev(X), vs, TABLES)
+    Y = aq.aq_linear_prefill_transformed(pw, qx, sx, us, TABLES, bias=to_dev(b))
+    torch.cuda.synchronize()
+    yt_norm = O.linear_from_partials(P, sx_r, sW)
+    assert_blocks_close(Y.cpu().numpy()[rows], y_ref, "fused transformed prefill", rel=1e-4, src=yt_norm)
+
+
+def test_prefill_transformed_bad_seed():
+    """A seed outside -1 .. 6 turns its tile row's outputs NaN; the others
+    are finite."""
+    rng = np.random.default_rng(3)
+    W = gen.weights(rng, 128, 256)
+    pw = aq.aq_pack_weights(to_dev(W), aq.aq_labels_from_map(np.full((2, 2), 4, np.uint8)), 64, 128)
+    qx, sx = aq.aq_quant_act(to_dev(gen.acts_heavy_tail(rng, 1024, 256)))
+    Y = aq.aq_linear_prefill_transformed(pw, qx, sx, np.array([0, 9], np.int8), TABLES).cpu().numpy()
+    assert np.isfinite(Y[:, :64]).all() and np.isnan(Y[:, 64:]).all()
