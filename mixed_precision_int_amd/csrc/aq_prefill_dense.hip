@@ -68,38 +68,86 @@ __device__ __forceinline__ float sflip(float v, uint32_t bit) {
   return __uint_as_float(__float_as_uint(v) ^ (bit << 31));
 }
 
-// Phi_s on the 64 outputs of one tile row for one token: element
-// i = 32 fn + l32 is register fn of lane l32 of the lane's half-wave.
-// D_R, then H_64 (stages h = 1 .. 16 across lanes, 32 across the two
-// registers, then 1/8), then P (position i takes element perm[i]), then
-// D_L; a seed outside -1 .. 6 gives NaN.
-__device__ __forceinline__ void phi_pair(float &v0, float &v1, int s, int lane, uint32_t dr0,
-                                         uint32_t dr1, uint32_t dl0, uint32_t dl1, int src0, int src1,
-                                         bool hi0, bool hi1) {
-  if (s < 0) return;
+// Lane exchange v[lane ^ h] inside a 16-lane row through DPP: quad
+// permutes for h = 1, 2; h = 4 as the half-row mirror (lane ^ 7) then the
+// quad reversal (^ 3); h = 8 as the row mirror (^ 15) then the half-row
+// mirror (^ 7).  Every lane is written (row and bank masks full).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int H>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (H == 1) return dpp<0xB1>(v);
+  else if constexpr (H == 2) return dpp<0x4E>(v);
+  else if constexpr (H == 4) return dpp<0x1B>(dpp<0x141>(v));
+  else if constexpr (H == 8) return dpp<0x141>(dpp<0x140>(v));
+  else return __shfl_xor(v, H);
+}
+
+// One butterfly stage over all of a wave's register pairs at once, so the
+// exchanges of the 64 registers are in flight together.
+template <int H>
+__device__ __forceinline__ void butterfly(float (&F)[2][2][16], int l32) {
+  float p[2][2][16];
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p[fm][fn][e] = lane_xor<H>(F[fm][fn][e]);
+  const bool up = (l32 & H) != 0;
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) F[fm][fn][e] = up ? p[fm][fn][e] - F[fm][fn][e] : F[fm][fn][e] + p[fm][fn][e];
+}
+
+// Phi_s (s >= 0) on the 64 outputs of one tile row for every token of the
+// wave: element i = 32 fn + l32 of a token is register fn of lane l32 of the
+// token's half-wave.  D_R, then H_64 (stages h = 1 .. 16 across lanes, 32
+// across the two registers, then 1/8), then P (position i takes element
+// perm[i]), then D_L.
+__device__ __forceinline__ void phi_tile(float (&F)[2][2][16], int s, int lane, uint32_t dr0, uint32_t dr1,
+                                         uint32_t dl0, uint32_t dl1, int src0, int src1, bool hi0, bool hi1) {
   const int l32 = lane & 31;
   if (s >= 1) {
-    v0 = sflip(v0, dr0);
-    v1 = sflip(v1, dr1);
-  }
 #pragma unroll
-  for (int h = 1; h < 32; h <<= 1) {
-    const float p0 = __shfl_xor(v0, h), p1 = __shfl_xor(v1, h);
-    v0 = (l32 & h) ? p0 - v0 : v0 + p0;
-    v1 = (l32 & h) ? p1 - v1 : v1 + p1;
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        F[fm][0][e] = sflip(F[fm][0][e], dr0);
+        F[fm][1][e] = sflip(F[fm][1][e], dr1);
+      }
   }
-  {
-    const float a0 = v0, a1 = v1;
-    v0 = (a0 + a1) * 0.125f;
-    v1 = (a0 - a1) * 0.125f;
-  }
+  butterfly<1>(F, l32);
+  butterfly<2>(F, l32);
+  butterfly<4>(F, l32);
+  butterfly<8>(F, l32);
+  butterfly<16>(F, l32);
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float a0 = F[fm][0][e], a1 = F[fm][1][e];
+      F[fm][0][e] = (a0 + a1) * 0.125f;
+      F[fm][1][e] = (a0 - a1) * 0.125f;
+    }
   if (s >= 1) {
-    const float w00 = __int_as_float(__builtin_amdgcn_ds_bpermute(src0, __float_as_int(v0)));
-    const float w01 = __int_as_float(__builtin_amdgcn_ds_bpermute(src0, __float_as_int(v1)));
-    const float w10 = __int_as_float(__builtin_amdgcn_ds_bpermute(src1, __float_as_int(v0)));
-    const float w11 = __int_as_float(__builtin_amdgcn_ds_bpermute(src1, __float_as_int(v1)));
-    v0 = sflip(hi0 ? w01 : w00, dl0);
-    v1 = sflip(hi1 ? w11 : w10, dl1);
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v0 = __float_as_int(F[fm][0][e]), v1 = __float_as_int(F[fm][1][e]);
+        const float w00 = __int_as_float(__builtin_amdgcn_ds_bpermute(src0, v0));
+        const float w01 = __int_as_float(__builtin_amdgcn_ds_bpermute(src0, v1));
+        const float w10 = __int_as_float(__builtin_amdgcn_ds_bpermute(src1, v0));
+        const float w11 = __int_as_float(__builtin_amdgcn_ds_bpermute(src1, v1));
+        F[fm][0][e] = sflip(hi0 ? w01 : w00, dl0);
+        F[fm][1][e] = sflip(hi1 ? w11 : w10, dl1);
+      }
   }
 }
 
@@ -403,11 +451,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
           hi0 = j0 >= 32;
           hi1 = j1 >= 32;
         }
-#pragma unroll
-        for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            phi_pair(F[fm][0][e], F[fm][1][e], s, lane, dr0, dr1, dl0, dl1, src0, src1, hi0, hi1);
+        phi_tile(F, s, lane, dr0, dr1, dl0, dl1, src0, src1, hi0, hi1);
       }
     }
 #pragma unroll
