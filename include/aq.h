@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AQ_ABI_VERSION 7
+#define AQ_ABI_VERSION 8
 
 typedef enum aq_status {
   AQ_OK = 0,
@@ -272,6 +272,15 @@ aq_status aq_linear_tile_partials(const aq_packed *W, const int8_t *qx, int M, i
  * eq. 6 at 8 bits, and eq. 19 with one activation scale per 64-feature
  * group (a b_K = 128 tile holds two). */
 
+/* Host only.  Shape of the App. B.3 activation-scale array for M rows of K
+ * features: *bM receives b_M (1 when M == 1, otherwise 16), *rows the
+ * number of b_M-row groups ceil(M / b_M), *cols the number of 64-feature
+ * groups K / 64.  The array that aq_quant_act_grouped writes and the
+ * *_grouped linears read is FP32 [rows][cols].  M == 0 gives rows = 0.
+ * AQ_ERR_NULL if an output pointer is NULL; AQ_ERR_SHAPE if M < 0, K <= 0
+ * or K is not a multiple of 64.  Does not touch the GPU. */
+aq_status aq_act_group_shape(int M, int K, int *bM, int *rows, int *cols);
+
 /* Activation quantization with App. B.3 groups: for each group A of b_M rows
  * (rows past M are App. B.3's zero padding) and features 64c .. 64c+63,
  * s = max(max(0, max A) / 127, max(0, -min A) / 128, 1e-12) in FP64 (eq. 6),
@@ -279,7 +288,8 @@ aq_status aq_linear_tile_partials(const aq_packed *W, const int8_t *qx, int M, i
  * scale FP32(s).
  *   X    device FP32 [M][K], K a multiple of 64
  *   qx   device INT8 [M][K]
- *   sxg  device FP32 [ceil(M/b_M)][K/64]: group (g, c) at g*(K/64) + c
+ *   sxg  device FP32 [ceil(M/b_M)][K/64] (aq_act_group_shape): group (g, c)
+ *        at g*(K/64) + c
  * M == 0 is a no-op. */
 aq_status aq_quant_act_grouped(const float *X, int M, int K, int8_t *qx, float *sxg, void *stream);
 

@@ -17,7 +17,7 @@ from .binding import (  # noqa: F401
     aq_alloc_packed,
     aq_decode_split,
     aq_labels_from_map,
-    act_group_rows,
+    aq_act_group_shape,
     aq_linear_decode,
     aq_linear_decode_grouped,
     aq_linear_prefill_grouped,

@@ -30,7 +30,8 @@ EXPORTS = ["aq_abi_version", "aq_status_string", "aq_labels_from_map", "aq_plan_
            "aq_quant_act_grouped", "aq_linear_decode_grouped", "aq_linear_prefill_grouped",
            "aq_linear_tile_partials_grouped", "aq_pack_weights_mse",
            "aq_transform_rows", "aq_transform_out", "aq_transform_weights", "aq_quant_act_transformed",
-           "aq_prefill_prepare", "aq_linear_prefill_prepared", "aq_linear_prefill_transformed"]
+           "aq_prefill_prepare", "aq_linear_prefill_prepared", "aq_linear_prefill_transformed",
+           "aq_act_group_shape"]
 
 
 class AqError(RuntimeError):
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
         "aq_linear_prefill": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
         "aq_linear_tile_partials": (i32, [ctypes.POINTER(AqPacked), vp, i32, i32, vp, vp, sz, vp]),
         "aq_quant_act_grouped": (i32, [vp, i32, i32, vp, vp, vp]),
+        "aq_act_group_shape": (i32, [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                     ctypes.POINTER(i32)]),
         "aq_pack_weights_mse": (i32, [vp, vp, ctypes.POINTER(AqPacked), vp]),
         "aq_linear_decode_grouped": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp, sz, vp]),
         "aq_linear_prefill_grouped": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
@@ -343,21 +346,26 @@ def aq_linear_tile_partials(pw: PackedWeights, qx, phase: int, out=None, ws=None
 
 # ---------------------------------------------------------------- App. B.3 activation groups
 
-def act_group_rows(M: int) -> int:
-    """b_M of App. B.3: 1 for a single token, else 16."""
-    return 1 if M == 1 else 16
+def aq_act_group_shape(M: int, K: int) -> tuple[int, int, int]:
+    """(b_M, rows, cols) of the App. B.3 activation-scale array for M rows of
+    K features, as the library defines them (host only)."""
+    bM, rows, cols = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().aq_act_group_shape(M, K, ctypes.byref(bM), ctypes.byref(rows), ctypes.byref(cols)),
+           "aq_act_group_shape")
+    return bM.value, rows.value, cols.value
 
 
 def aq_quant_act_grouped(X, qx=None, sxg=None, stream=None):
-    """INT8 codes [M, K] and FP32 group scales [ceil(M/b_M), K/64] of device
-    FP32 X [M, K] (one scale per 64 features x b_M rows, eq. 6)."""
+    """INT8 codes [M, K] and FP32 group scales [rows, cols] of device FP32
+    X [M, K], shaped by aq_act_group_shape (one scale per 64 features x b_M
+    rows, eq. 6)."""
     import torch
     M, K = X.shape
-    G = -(-M // act_group_rows(M))
+    _, G, KG = aq_act_group_shape(M, K)
     if qx is None:
         qx = torch.empty((M, K), dtype=torch.int8, device=X.device)
     if sxg is None:
-        sxg = torch.empty((G, K // 64), dtype=torch.float32, device=X.device)
+        sxg = torch.empty((G, KG), dtype=torch.float32, device=X.device)
     _check(lib().aq_quant_act_grouped(ctypes.c_void_p(X.data_ptr()), M, K, ctypes.c_void_p(qx.data_ptr()),
                                       ctypes.c_void_p(sxg.data_ptr()), _stream(stream)),
            "aq_quant_act_grouped")

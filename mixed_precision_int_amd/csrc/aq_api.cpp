@@ -227,6 +227,16 @@ aq_status aq_quant_act(const float *X, int M, int K, int8_t *qx, float *sx, void
              : AQ_ERR_HIP;
 }
 
+aq_status aq_act_group_shape(int M, int K, int *bM, int *rows, int *cols) {
+  if (!bM || !rows || !cols) return AQ_ERR_NULL;
+  if (M < 0 || K <= 0 || K % aq::kActGroupK) return AQ_ERR_SHAPE;
+  const int b = aq::act_group_rows(M);
+  *bM = b;
+  *rows = M / b + (M % b != 0);
+  *cols = K / aq::kActGroupK;
+  return AQ_OK;
+}
+
 aq_status aq_quant_act_grouped(const float *X, int M, int K, int8_t *qx, float *sxg, void *stream) {
   if (M < 0 || K <= 0 || K % 64) return AQ_ERR_SHAPE;
   if (M == 0) return AQ_OK;

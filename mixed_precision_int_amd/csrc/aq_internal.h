@@ -52,6 +52,12 @@ hipError_t launch_quant_act(const float *X, int M, int K, int8_t *qx, float *sx,
 hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx, int M,
                          const float *bias, float *Y, int split, void *ws, int32_t *P,
                          hipStream_t stream, bool grouped = false);
+// App. B.3 activation groups: 64 features x b_M rows, b_M = 1 for a single
+// token and 16 otherwise.  The one place the rule lives on the host side;
+// the grouped quantizer's launch, the grouped decode launch and
+// aq_act_group_shape take it from here.
+constexpr int kActGroupK = 64;
+inline int act_group_rows(int M) { return M == 1 ? 1 : 16; }
 hipError_t launch_quant_act_grouped(const float *X, int M, int K, int8_t *qx, float *sxg,
                                     hipStream_t stream);
 hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx, int M,

@@ -148,9 +148,10 @@ hipError_t launch_quant_act(const float *X, int M, int K, int8_t *qx, float *sx,
 hipError_t launch_quant_act_grouped(const float *X, int M, int K, int8_t *qx, float *sxg,
                                     hipStream_t stream) {
   const dim3 block(256);
-  const int gx = (K / 64 + 3) / 4;
-  if (M == 1)
-    hipLaunchKernelGGL(quant_act_grouped_kernel<1>, dim3(gx, 1), block, 0, stream, X, M, K, qx, sxg);
+  const int gx = (K / kActGroupK + 3) / 4;
+  const int bM = act_group_rows(M);
+  if (bM == 1)
+    hipLaunchKernelGGL(quant_act_grouped_kernel<1>, dim3(gx, M), block, 0, stream, X, M, K, qx, sxg);
   else
     hipLaunchKernelGGL(quant_act_grouped_kernel<16>, dim3(gx, (M + 15) / 16), block, 0, stream, X, M, K,
                        qx, sxg);

@@ -28,9 +28,26 @@ def test_exports_every_declared_symbol(aqlib):
 
 
 def test_abi_version_and_status_strings(aqlib):
-    assert B.aq_abi_version() == 7
+    assert B.aq_abi_version() == 8
     for code in list(B.STATUS) + [-99]:
         assert aqlib.aq_status_string(code)
+
+
+def test_act_group_shape_matches_oracle(aqlib):
+    # App. B.3: b_M = 1 for one token, 16 otherwise; ceil(M / b_M) x K/64 scales
+    for M, K in [(1, 64), (1, 3072), (2, 128), (15, 64), (16, 64), (17, 640), (2048, 2560), (0, 64)]:
+        bM, rows, cols = B.aq_act_group_shape(M, K)
+        assert bM == O.act_group_rows(M)
+        assert (rows, cols) == (-(-M // bM), K // O.ACT_GROUP_K)
+        if M:
+            _, sxg = O.quant_act_grouped(np.zeros((M, K)))
+            assert sxg.shape == (rows, cols)
+    for M, K in [(-1, 64), (4, 0), (4, 96)]:
+        with pytest.raises(B.AqError) as e:
+            B.aq_act_group_shape(M, K)
+        assert e.value.status == -2
+    x = ctypes.c_int()
+    assert aqlib.aq_act_group_shape(4, 64, None, ctypes.byref(x), ctypes.byref(x)) == -1
 
 
 def test_labels_match_oracle(aqlib):

@@ -408,6 +408,47 @@ def test_storage_order_does_not_change_output():
     assert np.array_equal(y1, y2)
 
 
+def check_abs_contrib_hand():
+    """The componentwise error scale of eq. 19 (sum of the terms' magnitudes),
+    per token and with the App. B.3 groups, on hand-worked values."""
+    g = _gold("abs_contrib_hand.json")
+    t = g["per_token"]
+    got = O.abs_contrib(np.array(t["P"]), np.array(t["sx"], np.float32), np.array(t["sW"], np.float32))
+    assert got.tolist() == t["expected"]
+    h = _gold("hand_2x2.json")
+    P = np.array(h["P"])
+    sW = np.array([[1.0, 1.0], [1.0, 0.5]], np.float32)   # rows' scales of the 2x2 fixture
+    assert O.abs_contrib(P, np.array(h["sx"], np.float32), sW).tolist() == g["hand_2x2"]["expected"]
+    gr = g["grouped"]
+    sxg, sWg = np.array(gr["sxg"], np.float32), np.array(gr["sW"], np.float32)
+    assert O.abs_contrib_grouped(np.array(gr["P_one_token"]), sxg, sWg, 64).tolist() == gr["expected_one_token_bk64"]
+    assert O.abs_contrib_grouped(np.array(gr["P_four_groups"]), np.array(gr["sxg_four_groups"], np.float32),
+                                 sWg, 128).tolist() == gr["expected_four_groups_bk128"]
+    assert O.abs_contrib_grouped(np.array(gr["P_two_tokens"]), sxg, sWg, 64).tolist() == \
+        gr["expected_two_tokens_bk64"]
+
+
+def test_abs_contrib_hand():
+    check_abs_contrib_hand()
+
+
+def check_mse_hand():
+    """Eq. 7 fitted scales and the codes they give, on hand-worked segments at
+    8 and 4 bits whose fitted codes differ from the absmax codes."""
+    g = _gold("mse_scale_hand.json")
+    W = _dense((g["N"], g["K"]), g["W_nonzero"])
+    codes, sW = O.quant_weights_mse(W, np.array(g["zmap"]), g["bN"], g["bK"])
+    assert np.array_equal(codes, _dense((g["N"], g["K"]), g["codes_nonzero"]).astype(np.int64))
+    assert sW.tolist() == g["sW"]
+    # the absmax route gives other codes on the same segments
+    ca, _ = O.quant_weights(W, np.array(g["zmap"]), g["bN"], g["bK"])
+    assert np.array_equal(ca, _dense((g["N"], g["K"]), g["absmax_codes_nonzero"]).astype(np.int64))
+
+
+def test_mse_hand():
+    check_mse_hand()
+
+
 def test_empty_token_batch():
     qx, sx = O.quant_act(np.zeros((0, 64), np.float32))
     assert qx.shape == (0, 64) and sx.shape == (0,)
@@ -446,9 +487,23 @@ MUTATIONS = {
     "epilogue_drops_bias": ("linear_from_partials", lambda P, sx, sW, bias=None: sum(
         (np.asarray(sx, np.float64)[:, None] * np.asarray(sW, np.float64)[None, :, j]) * P[:, :, j]
         for j in range(P.shape[2]))),
+    "abs_contrib_drops_abs": ("abs_contrib", lambda P, sx, sW: sum(
+        (np.asarray(sx, np.float64)[:, None] * np.asarray(sW, np.float64)[None, :, j]) * P[:, :, j]
+        for j in range(P.shape[2]))),
+    "abs_contrib_drops_act_scale": ("abs_contrib", lambda P, sx, sW: sum(
+        np.abs(np.asarray(sW, np.float64)[None, :, j] * P[:, :, j]) for j in range(P.shape[2]))),
+    "abs_contrib_grouped_tile_of_group": ("abs_contrib_grouped", lambda P, sxg, sW, bK: sum(
+        np.abs(np.asarray(sxg, np.float64)[np.arange(P.shape[0]) // O.act_group_rows(P.shape[0])][:, c][:, None]
+               * np.asarray(sW, np.float64)[None, :, min(c, sW.shape[1] - 1)] * P[:, :, c])
+        for c in range(P.shape[2]))),
+    "mse_codes_with_absmax_scale": ("quant_weights_mse", lambda W, z, bN, bK: (
+        O.quant_weights(W, z, bN, bK)[0],
+        np.array([[np.float32(O.mse_scale(W[n, j * bK:(j + 1) * bK], int(z[n // bN, j])))
+                   for j in range(W.shape[1] // bK)] for n in range(W.shape[0])], np.float32))),
 }
 
 PIN_CHECKS = [check_quantize_ties, check_hand_2x2, check_panel_order, check_eq16, check_eq17,
+              check_abs_contrib_hand, check_mse_hand,
               check_weight_scale_properties, check_partials_brute,
               lambda: check_dequant_matmul(5, True)]
 
