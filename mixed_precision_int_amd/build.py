@@ -10,6 +10,7 @@ instructions are disabled for all device code.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -41,13 +42,48 @@ def compile_flags() -> list[str]:
     ]
 
 
+# Kernels allowed to use scratch (private) memory.  Every other kernel must
+# be spill-free: the long-prompt GEMM counts its outstanding vector-memory
+# operations by hand at each column boundary, and a kernel that spills adds
+# memory operations the count was not written for (and loses time to them).
+# The debug tile-product variants store INT32 products inside the column
+# loop and spill by design; they are never on the timed path.
+SCRATCH_ALLOWED = [
+    re.compile(r"prefill_dense_kernelILi\d+ELi\d+ELi\d+ELi\d+ELb1E"),   # debug products
+    re.compile(r"prefill_kernelILi\d+ELi\d+ELi\d+ELb1E"),                # debug products
+    re.compile(r"prefill_big_kernelILb1E"),                              # debug products
+    # The persistent 256 x 256 GEMM spills 8 B/lane at 256 VGPRs.  Its column
+    # boundary waits for all of the wave's memory operations (vmcnt(0),
+    # lgkmcnt(0)), so no hand count depends on the spill's loads and stores.
+    re.compile(r"prefill_big_kernelILb0E"),
+]
+
+
+def scratch_report(stderr: str) -> list[tuple[str, int]]:
+    """(kernel, scratch bytes per lane) from hipcc's kernel-resource-usage
+    remarks."""
+    names = re.findall(r"remark: Function Name: (\S+)", stderr)
+    sizes = [int(x) for x in re.findall(r"remark: +ScratchSize \[bytes/lane\]: (\d+)", stderr)]
+    if len(names) != len(sizes):
+        raise RuntimeError("could not parse the kernel-resource-usage remarks")
+    return list(zip(names, sizes))
+
+
 def _compile(src: str) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [hipcc(), *compile_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".hip"):
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")
+    if src.endswith(".hip"):
+        bad = [(n, b) for n, b in scratch_report(res.stderr)
+               if b > 0 and not any(p.search(n) for p in SCRATCH_ALLOWED)]
+        if bad:
+            raise RuntimeError(f"{src}: kernels that spill to scratch memory: " +
+                               ", ".join(f"{n} ({b} B/lane)" for n, b in bad))
     return obj
 
 

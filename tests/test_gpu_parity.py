@@ -96,17 +96,30 @@ def test_llama3b_decode_linears(proj):
 
 @pytest.mark.parametrize("proj", [p[0] for p in gen.QWEN4B])
 def test_qwen4b_prefill_linears_sampled_rows(proj):
-    """Full M = 2048 through both kernels in the benchmarked launch shape;
-    outputs and tile products compared on 48 sampled token rows (every
-    128-row block boundary region, the last row included)."""
+    """Full M = 2048 in the benchmarked launch shape, i.e. the long-prompt
+    route (the temporary INT8 operand, then the 256 x 128 or the persistent
+    256 x 256 GEMM): the INT32 tile products of the whole 2048-row call are
+    gathered on the device at 48 sampled token rows (every 128-row block
+    boundary region, the last row included) and compared bit-exact with the
+    oracle; the outputs of the whole call on the same rows meet the bar.  The
+    same rows gathered first (a 48-row call, the short route) are checked
+    too."""
     d = gen.qwen4b_prefill(proj, 2048)
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([[0, 127, 128, 1023, 2047], rng.choice(2048, 43, replace=False)]))
     c = Case(d["W"], d["zmap"], d["X"], name=d["name"])
     ref = c.ref(rows)
     c.check_all(rows=rows, phases=("prefill",))
-    # the whole 2048-row call, then the sampled rows of its output
     qx_d, sx_d = c.qx_d, c.sx_d
+    M = qx_d.shape[0]
+    assert M >= 1024, "the benchmarked prompt takes the long route"
+    rows_d = torch.from_numpy(rows).cuda()
+    P = aq.aq_linear_tile_partials(c.pw, qx_d, aq.AQ_PHASE_PREFILL)
+    P_rows = P.index_select(0, rows_d).cpu().numpy().astype(np.int64)
+    del P
+    bad = np.argwhere(P_rows != ref["P_rows"])
+    assert bad.size == 0, f"{c.name}: {len(bad)} long-route tile products differ, first {bad[:4].tolist()}"
+    say(f"  {c.name}: long-route tile products of the M={M} call bit-exact on {len(rows)} rows")
     Y = aq.aq_linear_prefill(c.pw, qx_d, sx_d)
     torch.cuda.synchronize()
     from tests.parity import assert_output_close

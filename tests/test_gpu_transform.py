@@ -254,18 +254,27 @@ def test_prefill_transformed(N, K, bK, M, bias):
     assert torch.equal(Y, Y2), f"{N}x{K}/M{M}: repeated calls differ"
 
 
-def test_prefill_transformed_against_oracle():
+@pytest.mark.parametrize("N,K,M", [(320, 2560, 1030), (6144, 2560, 2048)])
+def test_prefill_transformed_against_oracle(N, K, M):
     """The fused route end to end on sampled rows: W~ = U W V packed, X~
     quantized in one pass, Y = Y~ U + bias from the GEMM epilogue, against the
-    oracle's transformed layer."""
-    N, K, M = 320, 2560, 1030
-    rng = np.random.default_rng(17)
+    oracle's transformed layer.  6144 x 2560 at M = 2048 is the Qwen3-4B qkv
+    shape at the benchmarked prompt length: 96 tile rows (both tile-row
+    waves of every 256 x 128 block, every seed value) and sampled token rows
+    in each of the four 64-row waves of a block, in first, middle and last
+    blocks."""
+    rng = np.random.default_rng(17 + N)
     W = gen.weights(rng, N, K)
     X = gen.acts_outliers(rng, M, K, 25, 25.0)
     z = gen.map_uniform(rng, N // 64, K // 128, 0.35)
     us, vs = every_seed(rng, N // 64), every_seed(rng, K // 64)
     b = rng.standard_normal(N).astype(np.float32)
-    rows = np.array([0, 1, 63, 64, 511, 1029])
+    if M == 1030:
+        rows = np.array([0, 1, 63, 64, 511, 1029])
+    else:
+        rows = np.unique(np.concatenate([[0, 63, 64, 127, 128, 191, 192, 255, 1024, 1100, 1170, 1250, M - 1],
+                                         rng.choice(M, 7, replace=False)]))
+    say(f"  fused transformed prefill {N}x{K}/M{M} against the oracle, rows {rows.tolist()}")
     Wt_r = O.transform_weights(W, us, vs, TABLES)
     codes, sW = O.quant_weights(Wt_r, z, 64, 128)
     qx_r, sx_r = O.quant_act(O.transform_rows(X[rows], vs, TABLES))
