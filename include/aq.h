@@ -222,6 +222,26 @@ aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx
                            const float *bias, float *Y, int split, void *ws, size_t ws_bytes,
                            void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * aq_linear_decode with the workspace taken from a device array inside the
+ * library, AQ_DECODE_SCRATCH_BYTES (8 MiB) per GPU, held from the first call
+ * on a GPU until the process ends.  The call allocates nothing.  The same
+ * kernels, hence the same Y bit for bit, as aq_linear_decode with a
+ * workspace.
+ *  - A call whose workspace (aq_workspace_bytes(W, M, 0, split)) exceeds
+ *    AQ_DECODE_SCRATCH_BYTES returns AQ_ERR_WORKSPACE and launches nothing
+ *    (every shape up to 5120 x 17408 fits at M <= 64).
+ *  - The first call on a GPU finds the array's address and enqueues on
+ *    `stream` a small kernel that zeroes its arrival counters; every call
+ *    leaves them zero again.
+ *  - All calls on one GPU share the array: calls that overlap in time on
+ *    one GPU (other streams, other threads) race and must not be issued.
+ * Other arguments and errors as aq_linear_decode. */
+#define AQ_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
+aq_status aq_linear_decode_noalloc(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                                   const float *bias, float *Y, int split, void *stream);
+
 /* Compute-bound phase (Sec. 3.3 "Prefill weight reuse"; App. E.3): the same
  * Y as aq_linear_decode, computed with INT8 matrix-core (MFMA) tiles that
  * reuse each weight tile across many activation rows.  Short prompts

@@ -19,6 +19,8 @@ from .binding import (  # noqa: F401
     aq_labels_from_map,
     aq_act_group_shape,
     aq_linear_decode,
+    aq_linear_decode_noalloc,
+    AQ_DECODE_SCRATCH_BYTES,
     aq_linear_decode_grouped,
     aq_linear_prefill_grouped,
     aq_linear_tile_partials_grouped,

@@ -31,7 +31,7 @@ EXPORTS = ["aq_abi_version", "aq_status_string", "aq_labels_from_map", "aq_plan_
            "aq_linear_tile_partials_grouped", "aq_pack_weights_mse",
            "aq_transform_rows", "aq_transform_out", "aq_transform_weights", "aq_quant_act_transformed",
            "aq_prefill_prepare", "aq_linear_prefill_prepared", "aq_linear_prefill_transformed",
-           "aq_act_group_shape"]
+           "aq_act_group_shape", "aq_linear_decode_noalloc"]
 
 
 class AqError(RuntimeError):
@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
         "aq_decode_split": (i32, [ctypes.POINTER(AqPacked), i32]),
         "aq_linear_decode": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp, sz, vp]),
         "aq_linear_prefill": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
+        "aq_linear_decode_noalloc": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp]),
         "aq_linear_tile_partials": (i32, [ctypes.POINTER(AqPacked), vp, i32, i32, vp, vp, sz, vp]),
         "aq_quant_act_grouped": (i32, [vp, i32, i32, vp, vp, vp]),
         "aq_act_group_shape": (i32, [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
@@ -283,6 +284,20 @@ def aq_linear_decode(pw: PackedWeights, qx, sx, bias=None, split: int = 0, out=N
     _check(lib().aq_linear_decode(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias),
                                   _ptr(out), split, _ptr(ws), ws_bytes, _stream(stream)),
            "aq_linear_decode")
+    return out
+
+
+AQ_DECODE_SCRATCH_BYTES = 8 << 20
+
+
+def aq_linear_decode_noalloc(pw: PackedWeights, qx, sx, out, bias=None, split: int = 0, stream=None):
+    """aq_linear_decode with the library's own device scratch in place of a
+    workspace: the C call allocates nothing; the caller provides `out`
+    (FP32 [M, N])."""
+    M = qx.shape[0]
+    _check(lib().aq_linear_decode_noalloc(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias),
+                                          _ptr(out), split, _stream(stream)),
+           "aq_linear_decode_noalloc")
     return out
 
 

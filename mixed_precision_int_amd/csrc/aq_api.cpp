@@ -281,6 +281,24 @@ aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx
              : AQ_ERR_HIP;
 }
 
+aq_status aq_linear_decode_noalloc(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                                   const float *bias, float *Y, int split, void *stream) {
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  st = check_linear_io(W, qx, sx, M, bias, Y);
+  if (st != AQ_OK || M == 0) return st;
+  const aq::PackedView v = aq::view_of(*W);
+  if (split < 0 || (split > 0 && !aq::decode_split_supported(v, M, split))) return AQ_ERR_ARG;
+  if (!aq::decode_plan_ok(aq::plan_decode(v, M, split), v)) return AQ_ERR_SHAPE;
+  const size_t need = aq::decode_workspace_bytes(v, M, split);
+  if (need > aq::kDecodeScratchBytes) return AQ_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void *ws = nullptr;
+  if (need > 0 && aq::decode_scratch(s, &ws) != hipSuccess) return AQ_ERR_HIP;
+  return aq::launch_decode(v, qx, sx, M, bias, Y, split, ws, nullptr, s) == hipSuccess ? AQ_OK
+                                                                                        : AQ_ERR_HIP;
+}
+
 aq_status aq_linear_decode_grouped(const aq_packed *W, const int8_t *qx, const float *sxg, int M,
                                    const float *bias, float *Y, int split, void *ws, size_t ws_bytes,
                                    void *stream) {

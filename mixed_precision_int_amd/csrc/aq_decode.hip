@@ -56,6 +56,7 @@
 // scale is multiplied by the exact factor 1/16.
 
 #include <cstring>
+#include <mutex>
 
 #include "aq_device.h"
 #include "aq_internal.h"
@@ -796,7 +797,46 @@ void choose_chunks(const PackedView &w, int M, int MG, int *RG, int *Z) {
   }
 }
 
+// Scratch of the allocation-free decode entry point: the chunked-K
+// workspace (arrival counters at the head, then the chunks' FP32 sums) in a
+// file-scope device array, one copy per GPU, kept until the process ends.
+// Host code reaches it only through the address hipGetSymbolAddress returns
+// for the current device (decode_scratch); the array's name is not a device
+// address on the host.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *__restrict__ p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t decode_scratch(hipStream_t stream, void **out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // the arrival counters must start at zero; every decode call leaves them
+    // zero.  A fill kernel, not a memset, so that a first call made under
+    // stream capture records a kernel node.
+    constexpr int words = kDecodeCounters;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream, static_cast<uint32_t *>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 DecodePlan plan_decode(const PackedView &w, int M, int split) {
   DecodePlan p;

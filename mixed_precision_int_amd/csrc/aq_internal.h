@@ -126,6 +126,12 @@ bool decode_plan_ok(const DecodePlan &p, const PackedView &w);
 int decode_split(const PackedView &w, int M);
 bool decode_split_supported(const PackedView &w, int M, int S);
 size_t decode_workspace_bytes(const PackedView &w, int M, int split);
+// The allocation-free decode's device scratch (AQ_DECODE_SCRATCH_BYTES):
+// its address on the current device, found once per device with
+// hipGetSymbolAddress; the first call on a device also enqueues, on
+// `stream`, a fill kernel that zeroes the arrival counters at its head.
+constexpr size_t kDecodeScratchBytes = AQ_DECODE_SCRATCH_BYTES;
+hipError_t decode_scratch(hipStream_t stream, void **out);
 
 // Block transforms of App. B.1 (kind: rows = X V, out = Y~ U, weights =
 // U W V); seeds2 is the per-tile-row seed array of the weight transform.
