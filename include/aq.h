@@ -182,6 +182,15 @@ aq_status aq_quant_act(const float *X, int M, int K, int8_t *qx, float *sx, void
  *   workspace (e.g. a zero-filled allocation); every decode call leaves them
  *   zero, so one workspace serves calls of any projection.  Decode calls
  *   that share a workspace must not run concurrently.
+ *   The hand-over between chunks rests on the gfx950 memory system, not on
+ *   C++ release/acquire: each workgroup writes its sums with device-scope
+ *   stores (sc1), waits until they have completed (vmcnt(0)) before the
+ *   barrier that precedes a relaxed device-scope fetch-add of its row
+ *   block's counter, and the workgroup that arrives last reads the sums with
+ *   device-scope loads.  Device-scope accesses bypass the caches that are
+ *   not coherent across the GPU, so a completed store is visible to every
+ *   later device-scope load and no cache write-back or invalidation is
+ *   issued.
  *   Prefill needs one for a long prompt (M >= 1024) on a projection that
  *   holds INT4 tiles: the temporary INT8 operand of App. E.3 (Prefill), N*K
  *   bytes of INT8 tiles in logical tile order, rounded up to 256, plus

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libaq.so")
-SOURCES = ["aq_api.cpp", "aq_pack.hip", "aq_quant_act.hip", "aq_decode.hip", "aq_prefill.hip",
+SOURCES = ["aq_api.cpp", "aq_plan.cpp", "aq_pack.hip", "aq_quant_act.hip", "aq_decode.hip", "aq_prefill.hip",
            "aq_expand.hip", "aq_prefill_dense.hip", "aq_prefill_big.hip", "aq_transform.hip"]
 ARCH = "gfx950"
 

@@ -64,18 +64,6 @@
 namespace aq {
 namespace {
 
-constexpr int kLdsBudget = 160 * 1024;  // LDS per workgroup on gfx950
-constexpr int kValuMaxM = 1;            // largest M on the vector-ALU path
-constexpr int kPrivMaxM = 4;            // largest M with per-wave activation slices
-constexpr int kPrivDepth = 8;           // tiles per batch with per-wave activation slices
-constexpr int kDecodeCounters = 65536;  // arrival counters at the head of a decode workspace
-constexpr int kInlineWords = 896;       // metadata words that may travel in the kernel arguments
-constexpr int kMetaStride = 6;          // words per tile row in the host metadata image
-enum { kValu = 0, kMfma = 1 };
-// Where the MFMA/VALU activation operands come from: a per-wave LDS slice
-// of the batch, or the workgroup's LDS copy of its tokens' chunk columns.
-enum { kXPriv = 0, kXShared = 1 };
-
 struct DecodeArgs {
   const uint8_t *labels;
   const int32_t *off4, *off8;
@@ -732,71 +720,6 @@ bool inline_meta(const PackedView &w) {
   return w.meta && w.C <= 128 && kMetaStride * w.R <= kInlineWords;
 }
 
-// Packed tiles of more than 16 MB: a projection too large to stay in the
-// on-chip caches between calls.
-bool streams_from_hbm(const PackedView &w) {
-  return (long long)w.T4 * 64 * w.bK / 2 + (long long)w.T8 * 64 * w.bK > (16LL << 20);
-}
-
-// Token groups of 16 per workgroup, waves per workgroup, token chunks.  Up
-// to 64 tokens share one pass over the weights; on projections that stream
-// from HBM, groups of at most 32 tokens (16 waves, one token chunk after
-// another) measure faster at M = 33..128 than 48 or 64 tokens on 8 waves.
-int mgroups(const PackedView &w, int M) {
-  const int g = M >= 49 ? 4 : (M + 15) / 16;
-  return streams_from_hbm(w) && g > 2 ? 2 : g;
-}
-int waves_of(const PackedView &w, int M) { return mgroups(w, M) <= 2 ? 16 : 8; }
-int mchunks_of(const PackedView &w, int M) {
-  const int MG = mgroups(w, M);
-  return (M + 16 * MG - 1) / (16 * MG);
-}
-
-// LDS row stride of one token's chunk of cz tile columns.
-int chunk_stride(int cz, int bK) { return ((cz * bK + 255) / 256) * 256; }
-
-// Bytes of the staged token rows of a chunk of cz columns.
-size_t chunk_lds(int MG, int cz, int bK) { return (size_t)16 * MG * chunk_stride(cz, bK); }
-
-// Fewest chunks whose token rows fit in LDS.
-int chunks_to_fit(const PackedView &w, int MG) {
-  for (int z = 1; z < w.C; ++z)
-    if (chunk_lds(MG, (w.C + z - 1) / z, w.bK) <= (size_t)kLdsBudget) return z;
-  return w.C;
-}
-
-// Row groups per workgroup without chunking: the fewest that still let the
-// whole grid (4R/RG workgroups, one per CU at this occupancy) run in a single
-// round on the 256 CUs; more row groups per workgroup means fewer, longer
-// splits.
-int rowgroups_unchunked(const PackedView &w) {
-  const int cus = 256;
-  if (4 * w.R <= cus) return 1;
-  if (2 * w.R <= cus) return 2;
-  return 4;
-}
-
-// Adaptive row groups and chunks for the shared-activation MFMA path.
-// When the tokens' activations over all K fit in LDS the call is not
-// chunked (the row-group rule above).  Otherwise the workgroup takes a whole
-// 64-row tile row (RG = 4: every staged activation byte feeds 64 weight rows)
-// and the columns are cut into the fewest chunks that fit.  Measured on the
-// 3B-14B projection shapes at M = 8..64: more chunks (to occupy more CUs)
-// lose, since every chunked workgroup adds a serial stage-load-store-count
-// chain, and fewer row groups per workgroup lose to the extra activation
-// staging.
-void choose_chunks(const PackedView &w, int M, int MG, int *RG, int *Z) {
-  (void)M;
-  const int zfit = chunks_to_fit(w, MG);
-  if (zfit == 1) {
-    *RG = rowgroups_unchunked(w);
-    *Z = 1;
-  } else {
-    *RG = 4;
-    *Z = zfit;
-  }
-}
-
 // Scratch of the allocation-free decode entry point: the chunked-K
 // workspace (arrival counters at the head, then the chunks' FP32 sums) in a
 // file-scope device array, one copy per GPU, kept until the process ends.
@@ -836,74 +759,6 @@ hipError_t decode_scratch(hipStream_t stream, void **out) {
   }
   *out = addr[dev];
   return hipSuccess;
-}
-
-DecodePlan plan_decode(const PackedView &w, int M, int split) {
-  DecodePlan p;
-  p.MG = mgroups(w, M);
-  p.waves = waves_of(w, M);
-  p.mchunks = mchunks_of(w, M);
-  // Products on MFMA for every M (with one token, 15 of the 16 A-operand rows
-  // are padding, yet it measured 1-3% faster than the vector-ALU dot
-  // products); launch_decode keeps the vector ALU for the one-token grouped
-  // route, where it measured about 1% faster.
-  p.mode = kMfma;
-  p.Z = 1;
-  p.ylaunch = p.mchunks;
-  p.xstride = 0;
-  p.ws_bytes = 0;
-  p.cnt_bytes = 0;
-  const size_t red = (size_t)p.waves * p.MG * 64 * sizeof(float4);
-  // Products: vector ALU for one token, MFMA otherwise.  Activations: a
-  // per-wave LDS slice of each batch for M <= 4 (no workgroup barrier),
-  // else the block's 16*MG token rows over its chunk of columns.
-  if (M <= kPrivMaxM) {
-    p.xmode = kXPriv;
-    p.RG = split > 0 ? p.waves / split : rowgroups_unchunked(w);
-    p.lds = (size_t)p.waves * M * kPrivDepth * w.bK + red;
-    p.mchunks = 1;
-  } else {
-    p.xmode = kXShared;
-    if (split > 0) {
-      p.RG = p.waves / split;
-      p.Z = chunks_to_fit(w, p.MG);
-    } else {
-      choose_chunks(w, M, p.MG, &p.RG, &p.Z);
-    }
-    const int cz = (w.C + p.Z - 1) / p.Z;
-    p.xstride = chunk_stride(cz, w.bK);
-    const size_t xb = chunk_lds(p.MG, cz, w.bK);
-    p.lds = xb > red ? xb : red;  // the reduction buffer reuses the token rows
-    if (p.Z > 1) {
-      // counters at a fixed place and size, so that calls of any layout can
-      // share one workspace; more token chunks than counters allow take
-      // several launches along the token axis
-      const int blocks = w.R * 4 / p.RG;
-      p.ylaunch = p.mchunks < kDecodeCounters / blocks ? p.mchunks : kDecodeCounters / blocks;
-      p.cnt_bytes = (size_t)kDecodeCounters * 4;
-      p.ws_bytes = p.cnt_bytes + (size_t)w.R * 4 * p.ylaunch * p.Z * p.MG * 64 * sizeof(float4);
-    }
-  }
-  p.S = p.waves / p.RG;
-  if (p.mode == kValu || p.xmode == kXPriv) p.ylaunch = 1;
-  if (p.ylaunch > 65535) p.ylaunch = 65535;  // grid y limit
-  return p;
-}
-
-bool decode_plan_ok(const DecodePlan &p, const PackedView &w) {
-  if ((long long)w.C * p.Z * p.S >= (1LL << 31)) return false;  // 32-bit split bounds
-  return p.Z == 1 || w.R * 4 / p.RG <= kDecodeCounters;
-}
-
-int decode_split(const PackedView &w, int M) { return plan_decode(w, M, 0).S; }
-
-bool decode_split_supported(const PackedView &w, int M, int S) {
-  const int W = waves_of(w, M);
-  return S == W || S == W / 2 || S == W / 4;
-}
-
-size_t decode_workspace_bytes(const PackedView &w, int M, int split) {
-  return plan_decode(w, M, split).ws_bytes;
 }
 
 hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx, int M,

@@ -61,12 +61,6 @@ __global__ __launch_bounds__(256) void expand_kernel(const PackedView w, int lab
 
 }  // namespace
 
-size_t expand_bytes(const PackedView &w) {
-  const size_t e = (size_t)w.N * w.K;               // INT8 tiles
-  const size_t s = (size_t)w.R * w.C * 64 * 4;      // FP32 scales
-  return ((e + 255) & ~(size_t)255) + s;
-}
-
 void expand_layout(const PackedView &w, const void *ws, const int8_t **E, const float **Es) {
   const int8_t *e = static_cast<const int8_t *>(ws);
   *E = e;

@@ -106,6 +106,20 @@ inline size_t prefill_workspace_bytes(const PackedView &w, int M) {
   return prefill_long(w, M) && w.T4 > 0 ? expand_bytes(w) : 0;
 }
 
+// Decode geometry shared by the kernels (aq_decode.hip) and the host
+// planner (aq_plan.cpp).
+constexpr int kLdsBudget = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int kValuMaxM = 1;            // largest M on the vector-ALU path
+constexpr int kPrivMaxM = 4;            // largest M with per-wave activation slices
+constexpr int kPrivDepth = 8;           // tiles per batch with per-wave activation slices
+constexpr int kDecodeCounters = 65536;  // arrival counters at the head of a decode workspace
+constexpr int kInlineWords = 896;       // metadata words that may travel in the kernel arguments
+constexpr int kMetaStride = 6;          // words per tile row in the host metadata image
+enum { kValu = 0, kMfma = 1 };
+// Where the MFMA/VALU activation operands come from: a per-wave LDS slice
+// of the batch, or the workgroup's LDS copy of its tokens' chunk columns.
+enum { kXPriv = 0, kXShared = 1 };
+
 // Launch plan of one decode call: products on the vector ALU or MFMA, where
 // the activation operands live, token groups of 16 per workgroup, waves,
 // row groups RG and splits S = waves / RG per workgroup, input-column

@@ -392,24 +392,6 @@ __global__ __launch_bounds__(512, 1) void prefill_big_kernel(const BigArgs a) {
 
 }  // namespace
 
-// Compute units of the current device (one persistent workgroup each).
-int compute_units() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
-  return n;
-}
-
-// Taken for wide projections (N >= 6144) with at least one tile per compute
-// unit: measured faster than the 256 x 128 kernel there (Qwen3-14B-shaped
-// gate_up and qkv at M = 8192), and not on narrower ones.
-bool prefill_big_fits(int N, int K, int bK, int M) {
-  if (bK != kBK || N < 6144) return false;
-  const long long tiles = (long long)((M + kBM - 1) / kBM) * ((N / 64 + 3) / 4);
-  return K / bK >= 2 && tiles >= compute_units() && (long long)M * N < (1LL << 29);
-}
-
 hipError_t launch_prefill_big(const int8_t *E, const float *Es, int N, int K, const int8_t *qx,
                               const float *sx, int M, const float *bias, float *Y, int32_t *P,
                               hipStream_t stream) {
