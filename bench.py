@@ -316,14 +316,56 @@ def cpu_baseline(budget_s: float):
             O.linear_from_partials(O.tile_partials(qx, codes, 128), sx, sW)
             t_pre += time.perf_counter() - t0
             ops += 2 * 64 * N * K
+    dec_bps, pre_ops = nbytes / t_dec, ops / t_pre
     return dict(
-        value=round(nbytes / t_dec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+        value=round(dec_bps / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
         sample=(f"decode linears of the 4 Llama-3.2-3B-shaped projections at M=1,4,16, "
                 f"{reps} pass(es), {t_dec:.1f} s; numpy FP64 oracle, 1 thread"),
-        prefill=dict(value=round(ops / t_pre / 1e12, 6), unit="TOPS",
+        prefill=dict(value=round(pre_ops / 1e12, 6), unit="TOPS",
                      sample=f"64 token rows x all outputs of the 4 Qwen3-4B-shaped projections, {t_pre:.1f} s"),
+        extrapolated_s=oracle_full_config_seconds(dec_bps, pre_ops),
+        cpu_model=cpu_model(),
         host_cores_available=len(os.sched_getaffinity(0)),
     )
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_full_config_seconds(dec_bps: float, pre_ops: float) -> dict:
+    """Time the single-threaded oracle would take on the whole of each larger
+    workload, extrapolated (not run) from the rates measured on the sample:
+    decode by algorithmic bytes, prefill by integer operations.  Bytes count
+    the packed weights with their scales and metadata (eq. 18 with per-row
+    scales), the INT8 activations and their scales, and the FP32 outputs."""
+    from oracle import aq_oracle as O
+    from workloads import gen
+
+    def step_bytes(geometry, maps, M):
+        total = 0
+        for layer in maps:
+            for (name, N, K), z in zip(geometry, layer):
+                t4, t8 = int((z == 4).sum()), int((z == 8).sum())
+                total += O.packed_bytes_rowscale(t4, t8, N // 64, K // 128, 64, 128) + M * K + 4 * M + 4 * M * N
+        return total
+
+    m8, m14 = gen.dense8b_maps(), gen.qwen14b_maps()
+    q4_ops = sum(2 * PREFILL_M * N * K for _, N, K in gen.QWEN4B)
+    q14_ops = sum(2 * 65536 * N * K for _, N, K in gen.QWEN14B) * len(m14)
+    out = {"qwen3_4b_prefill_m2048": round(q4_ops / pre_ops, 1)}
+    for M in (1, 8, 32, 64):
+        out[f"dense8b_decode_step_m{M}"] = round(step_bytes(gen.DENSE8B, m8, M) / dec_bps, 1)
+    out["qwen14b_prefill_64k"] = round(q14_ops / pre_ops, 1)
+    out["qwen14b_decode_step_m32"] = round(step_bytes(gen.QWEN14B, m14, 32) / dec_bps, 1)
+    return out
 
 
 def split_comparison(aq, torch, dec, ws, reps: int = 48):
