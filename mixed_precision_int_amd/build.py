@@ -87,6 +87,21 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(PKG, "probes", "issue_rates.hip")
+PROBE_BIN = os.path.join(PKG, "probes", "issue_rates")
+
+
+def build_probe() -> str:
+    """The issue-rate probe (a standalone program, measurement only; not part
+    of libaq.so).  Its MFMAs take their accumulators in VGPRs, as the GEMM's
+    do, so that the rescale reads them without copies."""
+    cmd = [hipcc(), *compile_flags(), "-mllvm", "-amdgpu-mfma-vgpr-form=1", PROBE_SRC, "-o", PROBE_BIN]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the issue-rate probe:\n{res.stderr}")
+    return PROBE_BIN
+
+
 def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
@@ -96,8 +111,9 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    build_probe()
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PROBE_BIN}")
     return LIB_PATH
 
 

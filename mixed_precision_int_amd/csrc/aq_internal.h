@@ -76,7 +76,7 @@ hipError_t launch_prefill_dense(const int8_t *E, const float *Es, int N, int K, 
                                 const aq_transform_tables *tables = nullptr);
 
 // Persistent 256 x 256-tile variant of the long-prefill GEMM (b_K = 128,
-// N >= 6144, at least one tile per compute unit, M*N < 2^29); same operands;
+// N >= 6144, tiles for at least half of the compute units, M*N < 2^29); same operands;
 // P != nullptr writes INT32 products instead of Y.
 int compute_units();
 bool prefill_big_fits(int N, int K, int bK, int M);

@@ -161,14 +161,18 @@ int compute_units() {
   return n;
 }
 
-// Taken for wide projections (N >= 6144) with at least one tile per compute
-// unit: measured faster than the 256 x 128 kernel there (Qwen3-14B-shaped
-// gate_up and qkv at M = 8192), and not on narrower ones.
+// Taken for wide projections (N >= 6144) with tiles for at least half of
+// the compute units.  Its 256 x 256 tiles do about 30% more per CU-second
+// than the 256 x 128 kernel: on Qwen3-4B-shaped gate_up at M = 2048 (608
+// tiles, 2.4 rounds) it takes 179 us against 192 us for the 256 x 128
+// kernel's 4.75 rounds, and on qkv (192 tiles on 256 CUs) 61 us against
+// 68 us for two rounds of 256 x 128 blocks; likewise on Qwen3-14B-shaped
+// gate_up and qkv at M = 8192.  Narrower projections give too few tiles.
 bool prefill_big_fits(int N, int K, int bK, int M) {
   constexpr int kBM = 256, kBK = 128;  // the persistent kernel's tile: 256 tokens x 4 tile rows
   if (bK != kBK || N < 6144) return false;
   const long long tiles = (long long)((M + kBM - 1) / kBM) * ((N / 64 + 3) / 4);
-  return K / bK >= 2 && tiles >= compute_units() && (long long)M * N < (1LL << 29);
+  return K / bK >= 2 && 2 * tiles >= compute_units() && (long long)M * N < (1LL << 29);
 }
 
 }  // namespace aq
