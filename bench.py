@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-models", action="store_true",
+                    help="skip the whole-model fields (8B-class decode steps, Qwen3-14B-shaped chunk and step)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -700,6 +702,109 @@ def model_14b(aq, gen, torch):
     print("\n".join(rows))
 
 
+def model_fields(aq, gen, torch, reps: int = 5) -> dict:
+    """Compact whole-model figures for the bench line (after the timed
+    region, outside ms_per_step): the 8B-class model's decode step over all
+    144 resident projections at M = 1 and 64 (launches enqueued behind a GPU
+    hold, mean of `reps` steps), then the Qwen3-14B-shaped model's one
+    8192-token prefill chunk through all 160 projections (operand built by
+    every call) and one batch-32 decode step (best of 3).  Each step
+    quantizes every projection's activations and runs its linear; rates are
+    algorithmic bytes or 2MNK operations over the step."""
+    from mixed_precision_int_amd.model import pack_model
+    dev = torch.device("cuda", 0)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    per_us = sleep_cycles_per_us(torch)
+    out = {}
+
+    def timed_ahead(step, n):
+        step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step()
+        host_us = (time.perf_counter() - t0) * 1e6
+        torch.cuda.synchronize()
+        a, b = E(), E()
+        torch.cuda._sleep(int(per_us * (host_us * n * 1.5 + 2000)))
+        a.record()
+        for _ in range(n):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    def decode_step_fn(model, geometry, M, seed_cfg, salt):
+        xs = {name: gen.device_acts_outliers(M, K, gen.act_seed(seed_cfg, 0, name, salt)) for name, N, K in geometry}
+        bufs = {name: (torch.empty((M, K), dtype=torch.int8, device=dev),
+                       torch.empty((M,), dtype=torch.float32, device=dev),
+                       torch.empty((M, N), dtype=torch.float32, device=dev)) for name, N, K in geometry}
+        need = max(aq.aq_workspace_bytes(pw, M, aq.AQ_PHASE_DECODE) for _, _, pw in model)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+
+        def step():
+            for _, name, pw in model:
+                qx, sx, Y = bufs[name]
+                aq.aq_quant_act(xs[name], qx, sx)
+                aq.aq_linear_decode(pw, qx, sx, None, 0, Y, ws)
+        return step, sum(linear_bytes(pw.plan, M) for _, _, pw in model)
+
+    model = pack_model(gen.DENSE8B, gen.dense8b_maps(),
+                       lambda l, name, N, K: gen.device_weights(N, K, gen.seed_for(4, l, name)))
+    torch.cuda.synchronize()
+    d8 = {"workload": "8B-class dense model (hidden 4096, FFN 14336, 36 layers), all 144 projections resident, "
+                      "one decode step", "packed_gb": round(model.nbytes() / 1e9, 3)}
+    for M in (1, 64):
+        step, nbytes = decode_step_fn(model, gen.DENSE8B, M, 4, M)
+        ms = timed_ahead(step, reps)
+        d8[f"M{M}"] = {"ms_per_step": round(ms, 3), "GB/s": round(nbytes / ms / 1e6, 1),
+                       "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        del step
+    out["dense8b_decode"] = d8
+    del model
+    torch.cuda.empty_cache()
+
+    model = pack_model(gen.QWEN14B, gen.qwen14b_maps(),
+                       lambda l, name, N, K: gen.device_weights(N, K, gen.seed_for(5, l, name)))
+    torch.cuda.synchronize()
+    q14 = {"workload": "Qwen3-14B-shaped model (hidden 5120, FFN 17408, 40 layers), all 160 projections "
+                       "resident", "packed_gb": round(model.nbytes() / 1e9, 3)}
+    M = 8192
+    xs = {name: gen.device_acts_heavy_tail(M, K, seed=gen.act_seed(5, 0, name, 0)) for name, N, K in gen.QWEN14B}
+    q = {name: (torch.empty((M, K), dtype=torch.int8, device=dev), torch.empty((M,), dtype=torch.float32, device=dev))
+         for name, N, K in gen.QWEN14B}
+    ys = {name: torch.empty((M, N), dtype=torch.float32, device=dev) for name, N, K in gen.QWEN14B}
+    need = max(aq.aq_workspace_bytes(pw, M, aq.AQ_PHASE_PREFILL) for _, _, pw in model)
+    pws = torch.zeros(max(16, need), dtype=torch.uint8, device=dev)
+    ops = sum(2 * M * pw.N * pw.K for _, _, pw in model)
+
+    def chunk():
+        for _, name, pw in model:
+            qx, sx = q[name]
+            aq.aq_quant_act(xs[name], qx, sx)
+            aq.aq_linear_prefill(pw, qx, sx, None, ys[name], pws)
+
+    chunk()
+    torch.cuda.synchronize()
+    a, b = E(), E()
+    a.record()
+    chunk()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    q14["prefill_chunk_8192"] = {"ms": round(ms, 2), "TOPS": round(ops / ms / 1e9, 1),
+                                 "frac": round(ops / ms / 1e9 / INT8_PEAK_TOPS, 4)}
+    del xs, q, ys, pws
+    torch.cuda.empty_cache()
+    step, nbytes = decode_step_fn(model, gen.QWEN14B, 32, 5, 9)
+    ms = min(timed_ahead(step, 1) for _ in range(3))
+    q14["decode_step_M32"] = {"ms": round(ms, 3), "GB/s": round(nbytes / ms / 1e6, 1),
+                              "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    out["qwen14b"] = q14
+    del model, step
+    torch.cuda.empty_cache()
+    return out
+
+
 def chunked_prefill(aq, gen, torch):
     """A 16K-token prompt prefilled in chunks of 1024 or 8192 tokens through
     Qwen3-14B-shaped projections (30% INT8 tiles in bands): the long-prompt
@@ -1037,6 +1142,11 @@ def main():
             "prefill_segment_ms": _med_min([p_seg[i].elapsed_time(p_seg[i + 1]) for i in range(K)]),
         },
     }
+    if not args.no_models:
+        try:
+            out["models"] = model_fields(aq, gen, torch)
+        except Exception as e:  # the headline line is printed regardless
+            out["models"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
