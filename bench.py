@@ -446,10 +446,12 @@ def grouped_comparison(aq, torch, dec, ws, pre, reps: int = 48):
         qg, sg = aq.aq_quant_act_grouped(x)
         pws = torch.empty(max(16, aq.aq_workspace_bytes(pw, PREFILL_M, aq.AQ_PHASE_PREFILL)), dtype=torch.uint8,
                           device=x.device)
+        gws = torch.zeros(max(16, aq.aq_workspace_bytes(pw, PREFILL_M, aq.AQ_PHASE_PREFILL_GROUPED)),
+                          dtype=torch.uint8, device=x.device)
         t = [timed([(lambda: aq.aq_quant_act(x, qx, sx))] * 4),
              timed([(lambda: aq.aq_linear_prefill(pw, qx, sx, None, Y, pws))] * 4),
              timed([(lambda: aq.aq_quant_act_grouped(x, qg, sg))] * 4),
-             timed([(lambda: aq.aq_linear_prefill_grouped(pw, qg, sg, None, Y))] * 4)]
+             timed([(lambda: aq.aq_linear_prefill_grouped(pw, qg, sg, None, Y, gws))] * 4)]
         ops = 2 * PREFILL_M * pw.plan.N * pw.plan.K
         rows.append(f"| prefill {proj} {pw.plan.N}x{pw.plan.K} | {PREFILL_M} | " + " | ".join(f"{v:.2f}" for v in t)
                     + f" | {ops / t[3] / 1e6:.0f} TOPS |")

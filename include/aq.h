@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AQ_ABI_VERSION 8
+#define AQ_ABI_VERSION 9
 
 typedef enum aq_status {
   AQ_OK = 0,
@@ -109,9 +109,12 @@ typedef struct aq_packed {
   uint32_t *meta_host;    /* host, meta_bytes, optional                     */
 } aq_packed;
 
-/* Phase selector for aq_workspace_bytes / aq_linear_tile_partials. */
+/* Phase selector for aq_workspace_bytes / aq_linear_tile_partials;
+ * AQ_PHASE_PREFILL_GROUPED sizes the workspace of aq_linear_prefill_grouped
+ * and aq_linear_tile_partials_grouped. */
 #define AQ_PHASE_DECODE 0
 #define AQ_PHASE_PREFILL 1
+#define AQ_PHASE_PREFILL_GROUPED 2
 
 /* ABI version of the loaded library (AQ_ABI_VERSION). */
 int aq_abi_version(void);
@@ -332,18 +335,29 @@ aq_status aq_linear_decode_grouped(const aq_packed *W, const int8_t *qx, const f
                                    const float *bias, float *Y, int split, void *ws, size_t ws_bytes,
                                    void *stream);
 
-/* The same product for any prompt length, computed by the decode kernels
- * (INT8 MFMA over up to 64 tokens per workgroup, token chunks one after
- * another); identical to aq_linear_decode_grouped with split 0, including
- * its workspace rule. */
+/* The same product for any prompt length.  Long prompts (the long route of
+ * aq_linear_prefill, at b_K = 128) run the long-prompt GEMM: the temporary
+ * INT8 operand (App. E.3 Prefill), then the 256 x 128 MFMA GEMM with the two
+ * 64-feature halves of every 128-column tile kept as separate INT32
+ * products, each rescaled by its activation-group scale times the row's
+ * weight scale (eq. 19 per group).  Shorter prompts run the decode kernels
+ * (up to 64 tokens per workgroup, token chunks one after another), exactly
+ * as aq_linear_decode_grouped with split 0.
+ *   ws    at least aq_workspace_bytes(W, M, AQ_PHASE_PREFILL_GROUPED, 0)
+ *         bytes, 16-byte aligned (NULL when that is 0): the temporary operand
+ *         on the long route, else the decode workspace (its counters zero, as
+ *         for aq_linear_decode), else AQ_ERR_WORKSPACE */
 aq_status aq_linear_prefill_grouped(const aq_packed *W, const int8_t *qx, const float *sxg, int M,
                                     const float *bias, float *Y, void *ws, size_t ws_bytes,
                                     void *stream);
 
 /* Debug: the INT32 group products P[m, n, c] of the grouped eq. 19, written
- * as INT32 [M][N][K/64] row-major by the grouped decode kernels. */
-aq_status aq_linear_tile_partials_grouped(const aq_packed *W, const int8_t *qx, int M, int32_t *P,
-                                          void *stream);
+ * as INT32 [M][N][K/64] row-major by the kernels aq_linear_prefill_grouped
+ * takes for M rows (the long-prompt GEMM, or the grouped decode kernels).
+ *   ws    on the long route, a workspace as for aq_linear_prefill_grouped
+ *         (otherwise unused) */
+aq_status aq_linear_tile_partials_grouped(const aq_packed *W, const int8_t *qx, int M, int32_t *P, void *ws,
+                                          size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Tile-aligned orthogonal transforms (App. B.1, eq. 4).

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaq.so")
 
 AQ_PHASE_DECODE = 0
 AQ_PHASE_PREFILL = 1
+AQ_PHASE_PREFILL_GROUPED = 2
 
 STATUS = {0: "AQ_OK", -1: "AQ_ERR_NULL", -2: "AQ_ERR_SHAPE", -3: "AQ_ERR_TILE", -4: "AQ_ERR_MAP",
           -5: "AQ_ERR_ALIGN", -6: "AQ_ERR_WORKSPACE", -7: "AQ_ERR_HIP", -8: "AQ_ERR_ARG"}
@@ -100,7 +101,7 @@ def lib() -> ctypes.CDLL:
         "aq_pack_weights_mse": (i32, [vp, vp, ctypes.POINTER(AqPacked), vp]),
         "aq_linear_decode_grouped": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp, sz, vp]),
         "aq_linear_prefill_grouped": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
-        "aq_linear_tile_partials_grouped": (i32, [ctypes.POINTER(AqPacked), vp, i32, vp, vp]),
+        "aq_linear_tile_partials_grouped": (i32, [ctypes.POINTER(AqPacked), vp, i32, vp, vp, sz, vp]),
         "aq_transform_rows": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
         "aq_transform_out": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp, vp]),
         "aq_prefill_prepare": (i32, [ctypes.POINTER(AqPacked), vp, sz, vp]),
@@ -404,30 +405,45 @@ def aq_linear_decode_grouped(pw: PackedWeights, qx, sxg, bias=None, split: int =
     return out
 
 
+def _grouped_workspace(pw: PackedWeights, M: int, ws, device, stream=None):
+    """The workspace of the grouped prefill for M rows: the library sizes it;
+    a workspace as large as the long-prompt one belongs to the long route
+    (the temporary operand), any other to the decode kernels (the stream's
+    zeroed decode workspace, whose counters must stay apart from operands)."""
+    import torch
+    need = aq_workspace_bytes(pw, M, AQ_PHASE_PREFILL_GROUPED)
+    if ws is None and need:
+        if aq_workspace_bytes(pw, M, AQ_PHASE_PREFILL) == need:
+            ws = torch.empty(need, dtype=torch.uint8, device=device)
+        else:
+            ws = decode_workspace(need, device, stream)
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
+
+
 def aq_linear_prefill_grouped(pw: PackedWeights, qx, sxg, bias=None, out=None, ws=None, stream=None):
-    """Any-length linear with App. B.3 group scales (the decode kernels)."""
+    """Any-length linear with App. B.3 group scales: the long-prompt GEMM for
+    long prompts, else the decode kernels."""
     import torch
     M = qx.shape[0]
     if out is None:
         out = torch.empty((M, pw.N), dtype=torch.float32, device=qx.device)
-    need = aq_workspace_bytes(pw, M, AQ_PHASE_DECODE, 0)
-    if ws is None and need:
-        ws = decode_workspace(need, qx.device, stream)
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    ws, ws_bytes = _grouped_workspace(pw, M, ws, qx.device, stream)
     _check(lib().aq_linear_prefill_grouped(ctypes.byref(pw.desc), _ptr(qx), _ptr(sxg), M, _ptr(bias),
                                            _ptr(out), _ptr(ws), ws_bytes, _stream(stream)),
            "aq_linear_prefill_grouped")
     return out
 
 
-def aq_linear_tile_partials_grouped(pw: PackedWeights, qx, out=None, stream=None):
-    """INT32 group products P [M, N, K/64] of the grouped eq. 19."""
+def aq_linear_tile_partials_grouped(pw: PackedWeights, qx, out=None, ws=None, stream=None):
+    """INT32 group products P [M, N, K/64] of the grouped eq. 19, from the
+    kernels aq_linear_prefill_grouped takes for M rows."""
     import torch
     M = qx.shape[0]
     if out is None:
         out = torch.empty((M, pw.N, pw.K // 64), dtype=torch.int32, device=qx.device)
-    _check(lib().aq_linear_tile_partials_grouped(ctypes.byref(pw.desc), _ptr(qx), M, _ptr(out),
-                                                 _stream(stream)), "aq_linear_tile_partials_grouped")
+    ws, ws_bytes = _grouped_workspace(pw, M, ws, qx.device, stream)
+    _check(lib().aq_linear_tile_partials_grouped(ctypes.byref(pw.desc), _ptr(qx), M, _ptr(out), _ptr(ws),
+                                                 ws_bytes, _stream(stream)), "aq_linear_tile_partials_grouped")
     return out
 
 

@@ -82,6 +82,20 @@ hipError_t run_prefill(const aq::PackedView &v, const int8_t *qx, const float *s
   return aq::launch_prefill_dense(E, Es, v.N, v.K, v.bK, qx, sx, M, bias, Y, P, s);
 }
 
+// Long grouped prefill: the temporary operand as for run_prefill, then the
+// 256 x 128 GEMM with App. B.3 activation groups (Y, or the INT32 group
+// products into P).
+hipError_t run_prefill_grouped(const aq::PackedView &v, const int8_t *qx, const float *sxg, int M,
+                               const float *bias, float *Y, int32_t *P, void *ws, hipStream_t s) {
+  const int8_t *E = v.w8;
+  const float *Es = v.s8;
+  if (v.T4 > 0) {
+    const hipError_t e = aq::launch_expand(v, ws, s, &E, &Es);
+    if (e != hipSuccess) return e;
+  }
+  return aq::launch_prefill_dense_grouped(E, Es, v.N, v.K, qx, sxg, M, bias, Y, P, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -258,6 +272,8 @@ size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split) {
   if (check_packed(W) != AQ_OK || M <= 0) return 0;
   const aq::PackedView v = aq::view_of(*W);
   if (phase == AQ_PHASE_PREFILL) return aq::prefill_workspace_bytes(v, M);
+  if (phase == AQ_PHASE_PREFILL_GROUPED)
+    return aq::prefill_grouped_long(v, M) ? aq::prefill_workspace_bytes(v, M) : aq::decode_workspace_bytes(v, M, 0);
   if (phase != AQ_PHASE_DECODE) return 0;
   if (split < 0 || (split > 0 && !aq::decode_split_supported(v, M, split))) return 0;
   return aq::decode_workspace_bytes(v, M, split);
@@ -320,11 +336,23 @@ aq_status aq_linear_decode_grouped(const aq_packed *W, const int8_t *qx, const f
 aq_status aq_linear_prefill_grouped(const aq_packed *W, const int8_t *qx, const float *sxg, int M,
                                     const float *bias, float *Y, void *ws, size_t ws_bytes,
                                     void *stream) {
-  return aq_linear_decode_grouped(W, qx, sxg, M, bias, Y, 0, ws, ws_bytes, stream);
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  const aq::PackedView v = aq::view_of(*W);
+  if (!aq::prefill_grouped_long(v, M))
+    return aq_linear_decode_grouped(W, qx, sxg, M, bias, Y, 0, ws, ws_bytes, stream);
+  st = check_linear_io(W, qx, sxg, M, bias, Y);
+  if (st != AQ_OK) return st;
+  st = check_workspace(ws, ws_bytes, aq::prefill_workspace_bytes(v, M));
+  if (st != AQ_OK) return st;
+  return run_prefill_grouped(v, qx, sxg, M, bias, Y, nullptr, ws, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
 }
 
-aq_status aq_linear_tile_partials_grouped(const aq_packed *W, const int8_t *qx, int M, int32_t *P,
-                                          void *stream) {
+aq_status aq_linear_tile_partials_grouped(const aq_packed *W, const int8_t *qx, int M, int32_t *P, void *ws,
+                                          size_t ws_bytes, void *stream) {
   aq_status st = check_packed(W);
   if (st != AQ_OK) return st;
   if (M < 0) return AQ_ERR_SHAPE;
@@ -333,6 +361,14 @@ aq_status aq_linear_tile_partials_grouped(const aq_packed *W, const int8_t *qx, 
   if (!aligned16(qx) || !aligned4(P)) return AQ_ERR_ALIGN;
   const aq::PackedView v = aq::view_of(*W);
   if ((long long)M * v.N * (v.K / 64) > (1LL << 40)) return AQ_ERR_SHAPE;
+  if (aq::prefill_grouped_long(v, M)) {
+    st = check_workspace(ws, ws_bytes, aq::prefill_workspace_bytes(v, M));
+    if (st != AQ_OK) return st;
+    return run_prefill_grouped(v, qx, nullptr, M, nullptr, nullptr, P, ws, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? AQ_OK
+               : AQ_ERR_HIP;
+  }
   if (!aq::decode_plan_ok(aq::plan_decode(v, M, 0), v)) return AQ_ERR_SHAPE;
   return aq::launch_decode(v, qx, nullptr, M, nullptr, nullptr, 0, nullptr, P,
                            static_cast<hipStream_t>(stream), true) == hipSuccess

@@ -75,6 +75,13 @@ hipError_t launch_prefill_dense(const int8_t *E, const float *Es, int N, int K, 
                                 const int8_t *useeds = nullptr,
                                 const aq_transform_tables *tables = nullptr);
 
+// The long-prefill GEMM with the pages' activation groups (App. B.3; b_K =
+// 128, M >= 2): sxg [ceil(M/16)][K/64]; P != nullptr writes the INT32
+// group products [M][N][K/64] instead of Y.
+hipError_t launch_prefill_dense_grouped(const int8_t *E, const float *Es, int N, int K, const int8_t *qx,
+                                        const float *sxg, int M, const float *bias, float *Y, int32_t *P,
+                                        hipStream_t stream);
+
 // Persistent 256 x 256-tile variant of the long-prefill GEMM (b_K = 128,
 // N >= 6144, tiles for at least half of the compute units, M*N < 2^29); same operands;
 // P != nullptr writes INT32 products instead of Y.
@@ -102,6 +109,9 @@ inline bool prefill_long(const PackedView &w, int M) {
   return M >= kLongPrefillM && (long long)M * w.K < (1LL << 31) &&
          (long long)w.N * w.K < (1LL << 31);
 }
+// Grouped activations (App. B.3) take the long-prompt GEMM for long prompts
+// at b_K = 128; otherwise the decode kernels.
+inline bool prefill_grouped_long(const PackedView &w, int M) { return w.bK == 128 && prefill_long(w, M); }
 inline size_t prefill_workspace_bytes(const PackedView &w, int M) {
   return prefill_long(w, M) && w.T4 > 0 ? expand_bytes(w) : 0;
 }

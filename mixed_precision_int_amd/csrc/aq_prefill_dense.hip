@@ -62,6 +62,10 @@ struct DenseArgs {
   int N, K, R, C, M, MB, NB;
   const int8_t *useeds;  // output transform: per tile row seed (-1 .. 6), or null
   OutTables ot;
+  // App. B.3 activation groups (GRP): scales [ceil(M/16)][K/64], group (g, c)
+  // at g * kg64 + c; ng16 = ceil(M/16) rows
+  const float *sxg;
+  int kg64, ng16;
 };
 
 __device__ __forceinline__ float sflip(float v, uint32_t bit) {
@@ -161,8 +165,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds, uint3
 // loads of this wave are outstanding and all LDS/scalar accesses are done.
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
-template <int BK, int WM, int WN, int S, bool PARTIALS, bool XFORM>
+// GRP: the pages' activation groups (App. B.3): one activation scale per 16
+// token rows x 64 features, so a 128-column tile's product splits into two
+// 64-feature halves (k-steps 0-1 and 2-3), each rescaled with the product of
+// its activation scale and the row's weight scale (eq. 19 per group).
+template <int BK, int WM, int WN, int S, bool PARTIALS, bool XFORM, bool GRP>
 __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const DenseArgs a) {
+  static_assert(!GRP || (BK == 128 && !XFORM), "grouped activations: b_K = 128, no output transform");
   constexpr int NW = WM * WN;
   constexpr int BM = 64 * WM, BN = 64 * WN;
   constexpr int NP = BK / 16;        // 16-byte chunks per row of a column; panels per tile
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
   constexpr int B_PW = B_BYTES / 1024 / NW;
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "even DMA split");
   static_assert(S >= 2 && S <= 4, "stages");
-  constexpr int PER_COL = A_PW + B_PW + 1;   // VMEM loads a wave issues per column
+  constexpr int PER_COL = A_PW + B_PW + 1 + (GRP ? 1 : 0);  // VMEM loads a wave issues per column
   static_assert((S - 2) * PER_COL <= 63, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) int8_t As0[A_BYTES];
@@ -188,6 +197,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
   __shared__ __attribute__((aligned(1024))) float Ss1[NW * 64];
   __shared__ __attribute__((aligned(1024))) float Ss2[S > 2 ? NW * 64 : 4];
   __shared__ __attribute__((aligned(1024))) float Ss3[S > 3 ? NW * 64 : 4];
+  // GRP: per-wave slots of the column's activation-group scales (8 used)
+  __shared__ __attribute__((aligned(256))) float Xg0[GRP ? NW * 64 : 4];
+  __shared__ __attribute__((aligned(256))) float Xg1[GRP ? NW * 64 : 4];
+  __shared__ __attribute__((aligned(256))) float Xg2[GRP && S > 2 ? NW * 64 : 4];
+  __shared__ __attribute__((aligned(256))) float Xg3[GRP && S > 3 ? NW * 64 : 4];
 
   // Rasterization: hardware places block k on XCD k % 8; logical block
   // L = (k % 8) * (G / 8) + k / 8 gives each XCD a contiguous range, walked
@@ -224,25 +238,28 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
   // scalar offset).  A: LDS chunk c = (wave*A_PW + i)*64 + lane of the slab is
   // row c / NP, physical chunk c % NP, which holds logical chunk
   // (c % NP) ^ ((row >> 1) & (NP - 1)).  Rows past M read row M - 1.
-  uint32_t a_voff[A_PW];
-#pragma unroll
-  for (int i = 0; i < A_PW; ++i) {
-    const int c = (wave * A_PW + i) * 64 + lane;
+  auto a_off = [&](int i, int ln) -> uint32_t {
+    const int c = (wave * A_PW + i) * 64 + ln;
     const int row = c / NP, pp = c % NP;
     const int p = pp ^ ((row >> 1) & (NP - 1));
-    a_voff[i] = (uint32_t)min(m0 + row, a.M - 1) * (uint32_t)a.K + (uint32_t)p * 16u;
-  }
+    return (uint32_t)min(m0 + row, a.M - 1) * (uint32_t)a.K + (uint32_t)p * 16u;
+  };
   // B: instruction bi = wave*B_PW + i moves panel bi % NP of tile row
   // r0 + bi / NP; tile rows past R read tile row R - 1.
-  uint32_t b_voff[B_PW];
-#pragma unroll
-  for (int i = 0; i < B_PW; ++i) {
+  auto b_off = [&](int i, int ln) -> uint32_t {
     const int bi = wave * B_PW + i;
     const int r = min(r0 + bi / NP, a.R - 1);
-    b_voff[i] = ((uint32_t)r * (uint32_t)a.C) * (uint32_t)(64 * BK) + (uint32_t)(bi % NP) * 1024u +
-                (uint32_t)lane * 16u;
-  }
-  const uint32_t s_voff = ((uint32_t)min(rw, a.R - 1) * (uint32_t)a.C * 64u + lane) * 4u;
+    return ((uint32_t)r * (uint32_t)a.C) * (uint32_t)(64 * BK) + (uint32_t)(bi % NP) * 1024u + (uint32_t)ln * 16u;
+  };
+  auto s_off = [&](int ln) -> uint32_t {
+    return ((uint32_t)min(rw, a.R - 1) * (uint32_t)a.C * 64u + (uint32_t)ln) * 4u;
+  };
+  uint32_t a_voff[A_PW], b_voff[B_PW];
+#pragma unroll
+  for (int i = 0; i < A_PW; ++i) a_voff[i] = a_off(i, lane);
+#pragma unroll
+  for (int i = 0; i < B_PW; ++i) b_voff[i] = b_off(i, lane);
+  const uint32_t s_voff = s_off(lane);
 
   // ---- per-lane fragment read offsets inside a stage.  Logical chunk
   // p = 2u + h of row `row` sits at physical chunk p ^ sw(row); since 2u and h
@@ -269,6 +286,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
 
   float scp0 = 0.f, scp1 = 0.f;  // scales of the column being rescaled
   float scn0 = 0.f, scn1 = 0.f;  // scales of the column being multiplied
+  // GRP: activation-group scales of the wave's four 16-row groups (rows
+  // m0 + wm*64 + 16 q, q = 2 fm + half), for the two 64-feature groups of the
+  // column being multiplied (xc) and the second group's of the previous
+  // column (xp); wave-uniform, kept in scalar registers.  They arrive with
+  // the column's other loads: lane l of a wave moves the scale of row group
+  // (l >> 1) & 3, feature group l & 1 into the wave's slot.
+  float xp[4] = {};
+  const __amdgpu_buffer_rsrc_t rX =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(GRP && a.sxg ? (const void *)a.sxg : (const void *)a.qx), 0,
+                                        0x7FFFFFFF, 0x00020000);
+  const uint32_t x_voff = GRP && a.sxg
+                              ? ((uint32_t)min((m0 + wm * 64) / 16 + ((lane >> 1) & 3), a.ng16 - 1) *
+                                     (uint32_t)a.kg64 + (uint32_t)(lane & 1)) * 4u
+                              : 0u;
+  auto stageX = [&](int s) -> float * {
+    return (s == 0 ? Xg0 : s == 1 ? Xg1 : s == 2 ? Xg2 : Xg3) + wave * 64;
+  };
 
   // issue the loads of column j into stage s
   auto issue = [&](int j, int s) {
@@ -281,6 +315,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
     for (int i = 0; i < B_PW; ++i)
       dma16(rE, Bs_ + (wave * B_PW + i) * 1024, b_voff[i], (uint32_t)j * (64 * BK));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)stageS(s), 4, s_voff, (uint32_t)j * 256u, 0, 0);
+    if constexpr (GRP)  // (the debug products pass no scales: a harmless read of qx)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_ptr_t)stageX(s), 4, x_voff, a.sxg ? (uint32_t)j * 8u : 0u,
+                                               0, 0);
   };
 
   float F[2][2][16];
@@ -315,11 +352,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
     // after the barrier, in every wave, and stage (j-1) % S is free
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((S - 2) * PER_COL));
     __builtin_amdgcn_s_barrier();
+    if constexpr (GRP && !PARTIALS) {
+      // the previous column's second-group scales, from its stage slot
+      // before the issue below refills that stage
+      const float *xs_ = stageX((q + S - 1) % S);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xp[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(xs_[2 * i + 1])));
+    }
     issue(min(j + S - 1, a.C - 1), (q + S - 1) % S);
     scp0 = scn0;
     scp1 = scn1;
     scn0 = stageS(s)[lane & 31];
     scn1 = stageS(s)[32 + (lane & 31)];
+    // GRP: the activation-group scales of the previous column's second group
+    // (rescaled during k-steps 0-1) and of this column's (first group during
+    // k-steps 2-3, second after the column)
 
     const int8_t *As_ = stageA(s);
     const int8_t *Bs_ = stageB(s);
@@ -338,6 +385,40 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
           fa[nb][f] = *reinterpret_cast<const v4i *>(As_ + (af0[f] ^ (32 * (u + 1))));
           fb[nb][f] = *reinterpret_cast<const v4i *>(Bs_ + bf0[f] + (u + 1) * 2048);
         }
+      }
+      if constexpr (GRP) {
+        // k-steps 0-1: the first 64-feature group into set 0; 2-3: the second
+        // into set 1.  Set 1 holds the previous column's second group until
+        // its rescale (k-steps 0-1) is done; set 0 is rescaled in k-steps 2-3.
+        const int hs = u >> 1;
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < 2; ++fn)
+            acc[hs][fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                fa[cb][fm], fb[cb][fn], (u & 1) == 0 ? v16i{0} : acc[hs][fm][fn], 0, 0, 0);
+        if constexpr (!PARTIALS) {
+          // this k-step rescales fragment row fm = u & 1 of the other set;
+          // its two 16-row groups (rows 8 (e / 4) + 4 h + (e & 3): e >= 8 is
+          // the second) take the products of their activation scale and the
+          // row's weight scale
+          const int fm = u & 1;
+          float pr[2][2];
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const float x = hs == 0 ? xp[2 * fm + hf]
+                                    : __int_as_float(__builtin_amdgcn_readfirstlane(
+                                          __float_as_int(stageX(s)[2 * (2 * fm + hf)])));
+            pr[hf][0] = x * (hs == 0 ? scp0 : scn0);
+            pr[hf][1] = x * (hs == 0 ? scp1 : scn1);
+          }
+#pragma unroll
+          for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              F[fm][fn][e] = fmaf((float)acc[hs ^ 1][fm][fn][e], pr[e >= 8][fn], F[fm][fn][e]);
+        }
+        continue;
       }
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm)
@@ -363,21 +444,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
       // and k-step 0 fragment reads, VALU rescale work while those reads are
       // in flight, then per MFMA a slice of the rescale and one fragment read
       // of the next k-step, so that the MFMA and VALU pipes overlap.
+      // (GRP: twice the rescale work, 16 VALU per MFMA, plus the scale products)
+      constexpr int VPM = GRP ? (256 - 16) / (4 * KS) : (128 - 16) / (4 * KS);
       __builtin_amdgcn_sched_group_barrier(0x020, A_PW + B_PW + 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, GRP ? 32 : 16, 0);
 #pragma unroll
       for (int u = 0; u < KS; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, (128 - 16) / (4 * KS), 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
           if (u + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
     }
     if constexpr (PARTIALS) {
       // 32x32 MFMA result: column (output n) = lane & 31, row (token) =
-      // 8 (e / 4) + 4 (lane >> 5) + (e & 3).
+      // 8 (e / 4) + 4 (lane >> 5) + (e & 3).  GRP: the two 64-feature groups'
+      // products, P[m][n][2 j + g].
       if (rw < a.R) {
 #pragma unroll
         for (int fm = 0; fm < 2; ++fm)
@@ -387,7 +471,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
             for (int e = 0; e < 16; ++e) {
               const int m = m0 + wm * 64 + fm * 32 + 8 * (e / 4) + 4 * h + (e & 3);
               const size_t n = (size_t)rw * 64 + fn * 32 + (lane & 31);
-              if (m < a.M) a.P[((size_t)m * a.N + n) * a.C + j] = acc[par][fm][fn][e];
+              if (m < a.M) {
+                if constexpr (GRP) {
+                  a.P[((size_t)m * a.N + n) * a.kg64 + 2 * j] = acc[0][fm][fn][e];
+                  a.P[((size_t)m * a.N + n) * a.kg64 + 2 * j + 1] = acc[1][fm][fn][e];
+                } else {
+                  a.P[((size_t)m * a.N + n) * a.C + j] = acc[par][fm][fn][e];
+                }
+              }
             }
       }
     }
@@ -408,7 +499,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
     // the last column's products
     const int lastpar = ((a.C - 1) % U) & 1;  // parity of column C - 1
     const float l0 = scn0, l1 = scn1;
-    if (lastpar == 0) {
+    if constexpr (GRP) {
+      // the last column's second 64-feature group (set 1); its stage is
+      // (C - 1) % S, never refilled past the end
+      const float *xs_ = stageX((a.C - 1) % S);
+      float xl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xl[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(xs_[2 * i + 1])));
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float x = xl[2 * fm + (e >= 8)];
+          F[fm][0][e] = fmaf((float)acc[1][fm][0][e], x * l0, F[fm][0][e]);
+          F[fm][1][e] = fmaf((float)acc[1][fm][1][e], x * l1, F[fm][1][e]);
+        }
+    } else if (lastpar == 0) {
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
@@ -460,11 +566,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
       for (int e = 0; e < 16; ++e) {
         const int m = m0 + wm * 64 + fm * 32 + 8 * (e / 4) + 4 * h + (e & 3);
         if (m >= a.M) continue;
-        const float sxm = a.sx[m];
+        const float sxm = GRP ? 1.0f : a.sx[m];  // GRP: the group scales are in F already
 #pragma unroll
         for (int fn = 0; fn < 2; ++fn) {
           const size_t n = (size_t)rw * 64 + fn * 32 + (lane & 31);
-          float v = F[fm][fn][e] * sxm;
+          float v = GRP ? F[fm][fn][e] : F[fm][fn][e] * sxm;
           if (a.bias) v += a.bias[n];
           // non-temporal: the outputs are not read again here, and keeping them
           // out of the caches leaves room for the operand slabs other blocks re-read
@@ -478,11 +584,11 @@ template <int BK, int WM, int WN, int S>
 hipError_t launch_dense_cfg(const DenseArgs &args, bool partials, hipStream_t stream) {
   const dim3 grid(args.MB * args.NB), block(64 * WM * WN);
   if (partials)
-    hipLaunchKernelGGL((prefill_dense_kernel<BK, WM, WN, S, true, false>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((prefill_dense_kernel<BK, WM, WN, S, true, false, false>), grid, block, 0, stream, args);
   else if (args.useeds)
-    hipLaunchKernelGGL((prefill_dense_kernel<BK, WM, WN, S, false, true>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((prefill_dense_kernel<BK, WM, WN, S, false, true, false>), grid, block, 0, stream, args);
   else
-    hipLaunchKernelGGL((prefill_dense_kernel<BK, WM, WN, S, false, false>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((prefill_dense_kernel<BK, WM, WN, S, false, false, false>), grid, block, 0, stream, args);
   return hipGetLastError();
 }
 
@@ -510,6 +616,27 @@ hipError_t launch_prefill_dense(const int8_t *E, const float *Es, int N, int K, 
   args.NB = (args.R + WN - 1) / WN;
   if (bK == 128) return launch_dense_cfg<128, WM, WN, S>(args, P != nullptr, stream);
   return launch_dense_cfg<64, WM, WN, S>(args, P != nullptr, stream);
+}
+
+hipError_t launch_prefill_dense_grouped(const int8_t *E, const float *Es, int N, int K, const int8_t *qx,
+                                        const float *sxg, int M, const float *bias, float *Y, int32_t *P,
+                                        hipStream_t stream) {
+  constexpr int WM = AQ_DENSE_WM, WN = AQ_DENSE_WN, S = AQ_DENSE_S;
+  DenseArgs args{};
+  args.qx = qx; args.E = E; args.Es = Es; args.sx = nullptr; args.bias = bias; args.Y = Y; args.P = P;
+  args.N = N; args.K = K; args.R = N / 64; args.C = K / 128; args.M = M;
+  args.MB = (M + 64 * WM - 1) / (64 * WM);
+  args.NB = (args.R + WN - 1) / WN;
+  args.useeds = nullptr;
+  args.sxg = sxg;
+  args.kg64 = K / 64;
+  args.ng16 = (M + 15) / 16;
+  const dim3 grid(args.MB * args.NB), block(64 * WM * WN);
+  if (P)
+    hipLaunchKernelGGL((prefill_dense_kernel<128, WM, WN, S, true, false, true>), grid, block, 0, stream, args);
+  else
+    hipLaunchKernelGGL((prefill_dense_kernel<128, WM, WN, S, false, false, true>), grid, block, 0, stream, args);
+  return hipGetLastError();
 }
 
 }  // namespace aq

@@ -164,6 +164,22 @@ int main() {
                                           nullptr, (float *)dev(8192), 0, c->wd, c->nd, nullptr); }, &c,
                       "aq_linear_decode_grouped");
       }
+      {
+        const size_t wg = aq_workspace_bytes(&f.p, M, AQ_PHASE_PREFILL_GROUPED, 0);
+        std::vector<unsigned char> wsg(wg + 256);
+        unsigned char *wsg_a = wsg.data() + (256 - (uintptr_t)wsg.data() % 256) % 256;
+        struct G { Fake *f; int M; void *w; size_t n; } gc{&f, M, wg ? wsg_a : nullptr, wg};
+        expect_launch([](void *v) { G *c = (G *)v;
+          return aq_linear_prefill_grouped(&c->f->p, (const int8_t *)dev(0), (const float *)dev(4096), c->M,
+                                           nullptr, (float *)dev(8192), c->w, c->n, nullptr); }, &gc,
+                      "aq_linear_prefill_grouped");
+        expect_launch([](void *v) { G *c = (G *)v;
+          return aq_linear_tile_partials_grouped(&c->f->p, (const int8_t *)dev(0), c->M, (int32_t *)dev(8192),
+                                                 c->w, c->n, nullptr); }, &gc, "aq_linear_tile_partials_grouped");
+        if (wg)
+          CHECK(aq_linear_prefill_grouped(&f.p, (const int8_t *)dev(0), (const float *)dev(4096), M, nullptr,
+                                          (float *)dev(8192), wsg_a, wg - 1, nullptr) == AQ_ERR_WORKSPACE);
+      }
       // rejected before any launch
       const int before = g_launches;
       if (wd) CHECK(aq_linear_decode(&f.p, (const int8_t *)dev(0), (const float *)dev(4096), M, nullptr,

@@ -35,6 +35,10 @@ hipError_t launch_prefill_dense(const int8_t *, const float *, int, int, int, co
                                 const aq_transform_tables *) {
   return launched();
 }
+hipError_t launch_prefill_dense_grouped(const int8_t *, const float *, int, int, const int8_t *, const float *, int,
+                                        const float *, float *, int32_t *, hipStream_t) {
+  return launched();
+}
 hipError_t launch_prefill_big(const int8_t *, const float *, int, int, const int8_t *, const float *, int,
                               const float *, float *, int32_t *, hipStream_t) {
   return launched();

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(aqlib):
 
 
 def test_abi_version_and_status_strings(aqlib):
-    assert B.aq_abi_version() == 8
+    assert B.aq_abi_version() == 9
     for code in list(B.STATUS) + [-99]:
         assert aqlib.aq_status_string(code)
 
@@ -199,8 +199,8 @@ def test_grouped_entry_points_rejected(aqlib):
     assert dg(M=0) == 0 and dg(qx=None) == -1 and dg(qx=FAKE + 1) == -5
     assert dg(split=3) == -8
     assert L.aq_linear_prefill_grouped(ctypes.byref(d), FAKE, None, 4, None, FAKE, None, 0, None) == -1
-    assert L.aq_linear_tile_partials_grouped(ctypes.byref(d), FAKE, 0, FAKE, None) == 0
-    assert L.aq_linear_tile_partials_grouped(ctypes.byref(d), None, 4, FAKE, None) == -1
+    assert L.aq_linear_tile_partials_grouped(ctypes.byref(d), FAKE, 0, FAKE, None, 0, None) == 0
+    assert L.aq_linear_tile_partials_grouped(ctypes.byref(d), None, 4, FAKE, None, 0, None) == -1
     big = fake_packed(N=256, K=65536, T4=4 * 512 - 3, T8=3)
     assert L.aq_linear_decode_grouped(ctypes.byref(big), FAKE, FAKE, 64, None, FAKE, 0, None, 0, None) == -6
 

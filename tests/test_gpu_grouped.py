@@ -114,3 +114,54 @@ def test_grouped_large_projection_sampled():
     assert_output_close(Y[:, torch.from_numpy(cols).cuda()].cpu().numpy(),
                         O.linear_from_group_partials(P_r, sxg_r, sW, 128),
                         O.abs_contrib_grouped(P_r, sxg_r, sW, 128), "grouped-19456x2560/M48")
+
+
+@pytest.mark.parametrize("N,K,M,kind", [(192, 1536, 1030, "mixed"),    # a partial N block, ragged M
+                                        (256, 1024, 2048, "all_int4"),
+                                        (320, 2560, 1024, "all_int8")])  # W8 in place: no operand
+def test_grouped_long_route(N, K, M, kind):
+    """Long prompts take the long-prompt GEMM with the two 64-feature halves
+    of every tile kept apart (App. B.3 groups in eq. 19): group products of
+    every row bit-exact, outputs within the bar, with a bias."""
+    run_case(N, K, 128, M, kind=kind, bias=True, phases=("prefill",))
+
+
+def test_grouped_long_route_full_size_sampled():
+    """Qwen3-4B-shaped qkv (6144 x 2560) at M = 2048 on the long route: the
+    INT32 group products of the whole call gathered on the device at sampled
+    token rows (every 16-row group boundary region, each of a block's four
+    64-row waves) bit-exact, and the outputs of the whole call on those rows
+    within the bar."""
+    d = gen.qwen4b_prefill("qkv", 2048)
+    W, z, X = d["W"], d["zmap"], d["X"]
+    M = X.shape[0]
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, 15, 16, 63, 64, 127, 128, 191, 255, 1024, M - 1],
+                                     rng.choice(M, 9, replace=False)]))
+    codes, sW = O.quant_weights(W, z, 64, 128)
+    qx_r, sxg_r = O.quant_act_grouped(X)
+    P_r = O.group_partials(qx_r[rows], codes)
+    # the grouped eq. 19 on the sampled rows: scales of each row's 16-row group
+    sxr = sxg_r[rows // 16]
+    y_r = np.zeros((len(rows), W.shape[0]))
+    c_r = np.zeros_like(y_r)
+    for c in range(K_GROUPS(X)):
+        t = (sxr[:, c].astype(np.float64)[:, None] * sW[None, :, c // 2].astype(np.float64)) * P_r[:, :, c]
+        y_r += t
+        c_r += np.abs(t)
+    pw = aq.aq_pack_weights(to_dev(W), aq.aq_labels_from_map(z.astype(np.uint8)), 64, 128)
+    qx, sxg = aq.aq_quant_act_grouped(to_dev(X))
+    assert aq.aq_workspace_bytes(pw, M, aq.AQ_PHASE_PREFILL_GROUPED) == aq.aq_workspace_bytes(pw, M, aq.AQ_PHASE_PREFILL)
+    rows_d = torch.from_numpy(rows).cuda()
+    P = aq.aq_linear_tile_partials_grouped(pw, qx)
+    P_g = P.index_select(0, rows_d).cpu().numpy().astype(np.int64)
+    del P
+    bad = np.argwhere(P_g != P_r)
+    assert bad.size == 0, f"grouped qkv/M2048: {len(bad)} group products differ, first {bad[:4].tolist()}"
+    Y = aq.aq_linear_prefill_grouped(pw, qx, sxg)
+    torch.cuda.synchronize()
+    assert_output_close(Y.index_select(0, rows_d).cpu().numpy(), y_r, c_r, "grouped qkv/M2048 (long route)")
+
+
+def K_GROUPS(X):
+    return X.shape[1] // 64
