@@ -461,11 +461,10 @@ def grouped_comparison(aq, torch, dec, ws, pre, reps: int = 48):
 def transformed_comparison(aq, gen, torch, dec, ws, pre, reps: int = 48):
     """Cost of the online App. B.1 transforms: per call the transform of the
     activations (X V), quantization, both in one pass, the linear, the
-    output transform (Y~ U), and for prefill the linear with Y~ U applied in
-    its GEMM epilogue, each timed alone; "added" is (one pass - quantization
-    + the output transform's cost: Y~ U alone for decode, the fused linear's
-    excess over the plain one for prefill) over the untransformed
-    quantization + linear.
+    output transform (Y~ U) alone, and the linear with Y~ U applied in its
+    epilogue (decode and long-prompt GEMM), each timed alone; "added" is (one
+    pass - quantization + the fused linear's excess over the plain one) over
+    the untransformed quantization + linear.
     Decode runs on the 24 weight copies (HBM-resident weights); the linear's
     time does not depend on the weight values, so the untransformed packed
     copies stand in for packed W~."""
@@ -489,17 +488,22 @@ def transformed_comparison(aq, gen, torch, dec, ws, pre, reps: int = 48):
             "| Y~ U rate |",
             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     rng = np.random.default_rng(77)
+    # the transformed decode hands tile rows over through its own (larger) workspace
+    xws = torch.zeros(max(16, max(aq.aq_workspace_bytes(copies[0], M, aq.AQ_PHASE_DECODE_TRANSFORMED)
+                                  for _, copies, _, _ in dec for M in DECODE_M)), dtype=torch.uint8,
+                      device=dec[0][2][DECODE_M[0]].device)
     todo = [(f"decode {proj}", copies, xs[M], bufs[M], M,
              lambda c, q, s, Y, copies=copies: aq.aq_linear_decode(copies[c % N_COPIES], q, s, None, 0, Y, ws), reps,
-             None)
+             lambda c, q, s, us, Y, copies=copies: aq.aq_linear_decode_transformed(
+                 copies[c % N_COPIES], q, s, us, tables, out=Y, ws=xws))
             for proj, copies, xs, bufs in dec for M in DECODE_M]
     for proj, pw, x, bufs in pre:
         pws = torch.empty(max(16, aq.aq_workspace_bytes(pw, PREFILL_M, aq.AQ_PHASE_PREFILL)), dtype=torch.uint8,
                           device=x.device)
         todo.append((f"prefill {proj}", [pw], x, bufs, PREFILL_M,
                      lambda c, q, s, Y, pw=pw, pws=pws: aq.aq_linear_prefill(pw, q, s, None, Y, pws), 8,
-                     lambda q, s, us, Y, pw=pw, pws=pws: aq.aq_linear_prefill_transformed(pw, q, s, us, tables,
-                                                                                        out=Y, ws=pws)))
+                     lambda c, q, s, us, Y, pw=pw, pws=pws: aq.aq_linear_prefill_transformed(pw, q, s, us, tables,
+                                                                                           out=Y, ws=pws)))
     for name, copies, X, (qx, sx, Y), M, lin, n, fused in todo:
         N, K = copies[0].plan.N, copies[0].plan.K
         vs = torch.from_numpy(gen.transform_seeds(rng, K // 64)).to(X.device)
@@ -510,7 +514,7 @@ def transformed_comparison(aq, gen, torch, dec, ws, pre, reps: int = 48):
              timed([(lambda: aq.aq_quant_act_transformed(X, vs, tables, qx, sx))] * n),
              timed([(lambda c=c: lin(c, qx, sx, Y)) for c in range(n)]),
              timed([(lambda: aq.aq_transform_out(Y, us, tables, out=Y))] * n)]
-        tf = timed([(lambda: fused(qx, sx, us, Y))] * n) if fused else None
+        tf = timed([(lambda c=c: fused(c, qx, sx, us, Y)) for c in range(n)]) if fused else None
         # with the fused epilogue, the output transform's cost is its excess over the plain linear
         added = (t[2] - t[1] + (tf - t[3] if fused else t[4])) / (t[1] + t[3])
         rows.append(f"| {name} {N}x{K} | {M} | " + " | ".join(f"{v:.2f}" for v in t)

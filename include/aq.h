@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AQ_ABI_VERSION 9
+#define AQ_ABI_VERSION 10
 
 typedef enum aq_status {
   AQ_OK = 0,
@@ -111,10 +111,12 @@ typedef struct aq_packed {
 
 /* Phase selector for aq_workspace_bytes / aq_linear_tile_partials;
  * AQ_PHASE_PREFILL_GROUPED sizes the workspace of aq_linear_prefill_grouped
- * and aq_linear_tile_partials_grouped. */
+ * and aq_linear_tile_partials_grouped, AQ_PHASE_DECODE_TRANSFORMED that of
+ * aq_linear_decode_transformed (workspace sizes only). */
 #define AQ_PHASE_DECODE 0
 #define AQ_PHASE_PREFILL 1
 #define AQ_PHASE_PREFILL_GROUPED 2
+#define AQ_PHASE_DECODE_TRANSFORMED 3
 
 /* ABI version of the loaded library (AQ_ABI_VERSION). */
 int aq_abi_version(void);
@@ -422,6 +424,32 @@ aq_status aq_linear_prefill_transformed(const aq_packed *W, const int8_t *qx, co
                                         const float *bias, const int8_t *useeds,
                                         const aq_transform_tables *tables_host, float *Y, void *ws,
                                         size_t ws_bytes, void *stream);
+
+/* The transformed layer's decode linear (App. B.1 eq. 4 in the epilogue of
+ * App. E.3 eq. 19): Y = (Y~ U) + bias, Y~ the aq_linear_decode product of
+ * the transformed operands.  After the ordered split sum and the token
+ * scale, the workgroup that holds the last part of a 64-row tile row
+ * applies Phi_{u_r} to its 64 outputs per token, then adds the bias: bit for
+ * bit aq_linear_decode (bias NULL) with the same split followed by
+ * aq_transform_out (bias), in one launch.  When the decode plan spreads a
+ * tile row over several workgroups (row groups in different workgroups, or
+ * column chunks), their sums meet in the workspace as for chunked K, with
+ * one arrival counter per tile row and token chunk.  split = 0 takes the
+ * adaptive split of aq_linear_decode, except that it keeps a tile row's four
+ * row groups in one workgroup (split Wv/4) where each wave's share of the
+ * row then still fits one batch of weight loads.
+ *   useeds   device INT8 [N/64];  tables_host as for the transforms
+ *   ws       device workspace of at least
+ *            aq_workspace_bytes(W, M, AQ_PHASE_DECODE_TRANSFORMED, split)
+ *            bytes, 16-byte aligned, counters zero (NULL when that is 0),
+ *            else AQ_ERR_WORKSPACE; decode and transformed decode calls may
+ *            share one workspace (neither leaves a counter set)
+ * Other arguments and errors as aq_linear_decode.  Multi-chunk calls (more
+ * than 64 tokens) load the weights non-temporally in every chunk. */
+aq_status aq_linear_decode_transformed(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                                       const float *bias, const int8_t *useeds,
+                                       const aq_transform_tables *tables_host, float *Y, int split,
+                                       void *ws, size_t ws_bytes, void *stream);
 
 /* aq_quant_act of X~ = X V in one pass: the same codes and scales as
  * aq_transform_rows followed by aq_quant_act, bit for bit, with the

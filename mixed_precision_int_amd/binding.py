@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaq.so")
 AQ_PHASE_DECODE = 0
 AQ_PHASE_PREFILL = 1
 AQ_PHASE_PREFILL_GROUPED = 2
+AQ_PHASE_DECODE_TRANSFORMED = 3
 
 STATUS = {0: "AQ_OK", -1: "AQ_ERR_NULL", -2: "AQ_ERR_SHAPE", -3: "AQ_ERR_TILE", -4: "AQ_ERR_MAP",
           -5: "AQ_ERR_ALIGN", -6: "AQ_ERR_WORKSPACE", -7: "AQ_ERR_HIP", -8: "AQ_ERR_ARG"}
@@ -32,7 +33,7 @@ EXPORTS = ["aq_abi_version", "aq_status_string", "aq_labels_from_map", "aq_plan_
            "aq_linear_tile_partials_grouped", "aq_pack_weights_mse",
            "aq_transform_rows", "aq_transform_out", "aq_transform_weights", "aq_quant_act_transformed",
            "aq_prefill_prepare", "aq_linear_prefill_prepared", "aq_linear_prefill_transformed",
-           "aq_act_group_shape", "aq_linear_decode_noalloc"]
+           "aq_act_group_shape", "aq_linear_decode_noalloc", "aq_linear_decode_transformed"]
 
 
 class AqError(RuntimeError):
@@ -108,6 +109,8 @@ def lib() -> ctypes.CDLL:
         "aq_linear_prefill_transformed": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp,
                                                 ctypes.POINTER(AqTransformTables), vp, vp, sz, vp]),
         "aq_linear_prefill_prepared": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
+        "aq_linear_decode_transformed": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp,
+                                               ctypes.POINTER(AqTransformTables), vp, i32, vp, sz, vp]),
         "aq_quant_act_transformed": (i32, [vp, i32, i32, vp, ctypes.POINTER(AqTransformTables), vp, vp, vp]),
         "aq_transform_weights": (i32, [vp, i32, i32, vp, vp, ctypes.POINTER(AqTransformTables), vp, vp]),
     }
@@ -554,6 +557,28 @@ def aq_transform_weights(W, useeds, vseeds, tables, out=None, stream=None):
                                       ctypes.c_void_p(sv.data_ptr()), ctypes.byref(t),
                                       ctypes.c_void_p(out.data_ptr()), _stream(stream)),
            "aq_transform_weights")
+    return out
+
+
+def aq_linear_decode_transformed(pw: PackedWeights, qx, sx, useeds, tables, bias=None, split: int = 0,
+                                 out=None, ws=None, stream=None):
+    """Y = Y~ U + bias for a transformed layer's decode call, U applied in
+    the decode epilogue: FP32 [M, N].  Without `ws` the stream's cached
+    decode workspace is used."""
+    import torch
+    M = qx.shape[0]
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=qx.device)
+    need = aq_workspace_bytes(pw, M, AQ_PHASE_DECODE_TRANSFORMED, split)
+    if ws is None and need:
+        ws = decode_workspace(need, qx.device, stream)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    sd = _seeds_dev(useeds, pw.N // 64, qx.device)
+    t = _tables(tables)
+    _check(lib().aq_linear_decode_transformed(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias),
+                                              ctypes.c_void_p(sd.data_ptr()), ctypes.byref(t), _ptr(out),
+                                              split, _ptr(ws), ws_bytes, _stream(stream)),
+           "aq_linear_decode_transformed")
     return out
 
 

@@ -274,9 +274,9 @@ size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split) {
   if (phase == AQ_PHASE_PREFILL) return aq::prefill_workspace_bytes(v, M);
   if (phase == AQ_PHASE_PREFILL_GROUPED)
     return aq::prefill_grouped_long(v, M) ? aq::prefill_workspace_bytes(v, M) : aq::decode_workspace_bytes(v, M, 0);
-  if (phase != AQ_PHASE_DECODE) return 0;
+  if (phase != AQ_PHASE_DECODE && phase != AQ_PHASE_DECODE_TRANSFORMED) return 0;
   if (split < 0 || (split > 0 && !aq::decode_split_supported(v, M, split))) return 0;
-  return aq::decode_workspace_bytes(v, M, split);
+  return aq::decode_workspace_bytes(v, M, split, phase == AQ_PHASE_DECODE_TRANSFORMED);
 }
 
 aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx, int M,
@@ -529,6 +529,28 @@ aq_status aq_transform_weights(const float *W, int N, int K, const int8_t *useed
   if (w0 < t0 + bytes && t0 < w0 + bytes) return AQ_ERR_ARG;
   return aq::launch_transform(aq::kTransformWeights, W, Wt, N, K, vseeds, useeds, nullptr, *tables_host,
                               static_cast<hipStream_t>(stream)) == hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
+aq_status aq_linear_decode_transformed(const aq_packed *W, const int8_t *qx, const float *sx, int M,
+                                       const float *bias, const int8_t *useeds,
+                                       const aq_transform_tables *tables_host, float *Y, int split,
+                                       void *ws, size_t ws_bytes, void *stream) {
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  st = check_linear_io(W, qx, sx, M, bias, Y);
+  if (st != AQ_OK || M == 0) return st;
+  if (!useeds) return AQ_ERR_NULL;
+  st = check_tables(tables_host);
+  if (st != AQ_OK) return st;
+  const aq::PackedView v = aq::view_of(*W);
+  if (split < 0 || (split > 0 && !aq::decode_split_supported(v, M, split))) return AQ_ERR_ARG;
+  if (!aq::decode_plan_ok(aq::plan_decode(v, M, split, true), v, true)) return AQ_ERR_SHAPE;
+  st = check_workspace(ws, ws_bytes, aq::decode_workspace_bytes(v, M, split, true));
+  if (st != AQ_OK) return st;
+  return aq::launch_decode_transformed(v, qx, sx, M, bias, Y, split, ws, useeds, *tables_host,
+                                       static_cast<hipStream_t>(stream)) == hipSuccess
              ? AQ_OK
              : AQ_ERR_HIP;
 }

@@ -90,8 +90,61 @@ struct DecodeArgs {
 // travels inside the kernel arguments.  The record's place depends only on
 // the workgroup id, so it is fetched with the other arguments and the first
 // weight loads wait for no metadata load of their own.
-template <bool INL> struct DArgs : DecodeArgs {};
-template <> struct DArgs<true> : DecodeArgs { uint32_t meta[kInlineWords]; };
+//   With XF the epilogue applies the output transform of App. B.1 (Y = Y~ U,
+// U_r = Phi_{u_r}^T on the 64 outputs of tile row r): the seeds (device, one
+// per tile row) and the six signed permutations, perm bytes and sign masks
+// (bit e set: element e negated), also in the kernel arguments, which leaves
+// room for the metadata of fewer tile rows.
+struct XfTables {
+  uint8_t perm[kTransformSeeds][64];
+  uint64_t dlm[kTransformSeeds], drm[kTransformSeeds];
+};
+constexpr int kXfWords = sizeof(XfTables) / 4;
+// one word per thread of the smallest workgroup (8 waves), 512 bytes of LDS
+static_assert(sizeof(XfTables) % 4 == 0 && kXfWords <= 512 && sizeof(XfTables) <= 512, "transform tables");
+struct XfArgs {
+  const int8_t *useeds;
+  XfTables xt;
+};
+template <bool INL, bool XF> struct DArgs : DecodeArgs {};
+template <> struct DArgs<true, false> : DecodeArgs { uint32_t meta[kInlineWords]; };
+template <> struct DArgs<false, true> : DecodeArgs { XfArgs xf; };
+template <> struct DArgs<true, true> : DecodeArgs {
+  XfArgs xf;
+  uint32_t meta[kInlineWordsXf];
+};
+static_assert(sizeof(DArgs<true, false>) <= 4096 && sizeof(DArgs<true, true>) <= 4096,
+              "kernel arguments exceed 4 KiB");
+
+// H_64 over the wave for the output transform, lane l holding element l,
+// in the order h = 1, 2, .., 32 (the lane with bit h clear keeps self +
+// partner, its partner partner - self), then the exact 1/8: the FP32
+// sequence of the separate output transform.  Partners through DPP quad
+// permutes (h = 1, 2), ds_swizzle in bit-mask mode (h = 4, 8, 16) and
+// ds_bpermute (h = 32).
+template <int CTRL>
+__device__ __forceinline__ float xf_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int PAT>
+__device__ __forceinline__ float xf_swz(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), PAT));
+}
+__device__ __forceinline__ float xf_fwht64(float v, int lane) {
+  float p = xf_dpp<0xB1>(v);  // lane ^ 1
+  v = (lane & 1) ? p - v : v + p;
+  p = xf_dpp<0x4E>(v);  // lane ^ 2
+  v = (lane & 2) ? p - v : v + p;
+  p = xf_swz<0x101F>(v);  // lane ^ 4
+  v = (lane & 4) ? p - v : v + p;
+  p = xf_swz<0x201F>(v);  // lane ^ 8
+  v = (lane & 8) ? p - v : v + p;
+  p = xf_swz<0x401F>(v);  // lane ^ 16
+  v = (lane & 16) ? p - v : v + p;
+  p = __shfl_xor(v, 32);
+  v = (lane & 32) ? p - v : v + p;
+  return v * 0.125f;
+}
 
 __device__ __forceinline__ v4i load16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
 
@@ -190,8 +243,9 @@ __device__ __forceinline__ v4i x_operand(const int8_t *row, int colbase, int g, 
 }
 
 template <int BK, int MODE, int MG, int WAVES, int RG, int DEPTH, int XMODE, bool PARTIALS, bool INL,
-          bool GRP, bool WNT>
-__global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) {
+          bool GRP, bool WNT, bool XF>
+__global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF> a) {
+  static_assert(!XF || (MODE == kMfma && !PARTIALS && !GRP), "output transform: per-token MFMA route");
   constexpr int KS = BK / 64;    // MFMA steps (16-byte operands per lane) per tile
   constexpr int S = WAVES / RG;  // splits per row group
   constexpr int NT = WAVES * 64;
@@ -223,6 +277,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
     asm volatile("" ::"s"(a.w4), "s"(a.w8), "s"(a.s4), "s"(a.s8), "s"(a.qx), "s"(a.T4), "s"(a.T8),
                  "s"(a.C), "s"(a.K), "s"(a.M), "s"(a.Z));
   }
+  // the tile row's output-transform seed, loaded with the metadata
+  int useed = 0;
+  if constexpr (XF) useed = a.xf.useeds[r];
   const int C = a.C, K = a.K, M = a.M;
   // global split zc*S + sp of Z*S: tile columns floor(C*s/(Z*S)) .. (the
   // planner keeps C*Z*S below 2^31; one chunk: S is a compile-time divisor)
@@ -411,6 +468,26 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
     }
   }
   AQ_DECODE_ISSUE(c0);
+  // Epilogue operands, issued behind the first weight batch so that their
+  // latency hides under the weight stream: the token scales of the lane's
+  // outputs and its bias (with XF the tile row's 64 bias values, one per
+  // lane, and the lane's part of the tile row's transform).
+  float sxv[MG][4];
+  float bv = 0.0f;
+  uint32_t xtw = 0u;  // XF: word tid of the transform tables
+  if constexpr (!PARTIALS && !GRP && MODE == kMfma) {
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = mbase + mg * 16 + 4 * g + e;
+        sxv[mg][e] = m < M ? a.sx[m] : 0.0f;
+      }
+    if (a.bias) bv = a.bias[(size_t)r * 64 + (XF ? lane : rg * 16 + i16)];
+  }
+  if constexpr (XF) {
+    if (tid < kXfWords) xtw = reinterpret_cast<const uint32_t *>(&a.xf.xt)[tid];
+  }
   if (xstage) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS writes done; vmcnt left open
     asm volatile("" ::: "memory");
@@ -598,6 +675,95 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
         }
       }
     }
+    if constexpr (XF) {
+      // Output transform (App. B.1 eq. 4) after the ordered split sum (App.
+      // E.3): per tile row, Y = (sx * Y~) U + bias, the token scale applied
+      // first so that the result is bit for bit that of the linear followed
+      // by the separate output transform.  U mixes the 64 outputs of a tile
+      // row.  When its row groups or column chunks ran in several
+      // workgroups, each workgroup's sums go to the workspace (slot zc of
+      // each of its row groups, device-coherent as for chunked K) and the
+      // last workgroup of the tile row to arrive (arrival counter per tile
+      // row and token chunk, reset by that workgroup) adds every row
+      // group's slots in increasing zc and finishes the tile row.
+      uint32_t *flag = reinterpret_cast<uint32_t *>(smem);
+      uint32_t *xtl = reinterpret_cast<uint32_t *>(smem + 256);  // the transform tables
+      float *ys = reinterpret_cast<float *>(smem + 768);         // [16*MG tokens][64 outputs]
+      constexpr int kParts = 4 / RG;                      // workgroups per tile row and chunk
+      if (kParts * Z > 1) {
+        float4 *pp = a.part + ((size_t)(r * 4 + rg) * gridDim.y + yc) * Z * MG * 64 + lane;
+        if (sp == 0) {
+#pragma unroll
+          for (int mg = 0; mg < MG; ++mg) store_coherent(pp + ((size_t)zc * MG + mg) * 64, F[mg]);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+        if (tid == 0) {
+          uint32_t *cp = a.cnt + (size_t)r * gridDim.y + yc;
+          const uint32_t prev = __hip_atomic_fetch_add(cp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint32_t last = prev == (uint32_t)(kParts * Z - 1) ? 1u : 0u;
+          if (last) __hip_atomic_store(cp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          *flag = last;
+        }
+        __syncthreads();
+        if (*flag == 0u) return;
+        if (wave < 4) {  // wave w takes row group w
+          const float4 *qp = a.part + ((size_t)(r * 4 + wave) * gridDim.y + yc) * Z * MG * 64 + lane;
+#pragma unroll
+          for (int mg = 0; mg < MG; ++mg) {
+            float4 v = load_coherent(qp + mg * 64);
+            for (int z = 1; z < Z; ++z) {
+              const float4 p = load_coherent(qp + ((size_t)z * MG + mg) * 64);
+              v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+            }
+            F[mg] = v;
+          }
+        }
+      } else {
+        // one workgroup per tile row: waves 0 .. 3 (split 0) hold row groups
+        // 0 .. 3; every wave is done with the reduction buffer ys overlaps
+        __syncthreads();
+      }
+      if (wave < 4) {
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) {
+          const float fv[4] = {F[mg].x, F[mg].y, F[mg].z, F[mg].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = mg * 16 + 4 * g + e;
+            // the fused multiply-add with +0 rounds as the linear's sx * sum + 0
+            if (t < xrows) ys[t * 64 + 16 * wave + i16] = fmaf(fv[e], sxv[mg][e], 0.0f);
+          }
+        }
+      }
+      if (tid < kXfWords) xtl[tid] = xtw;
+      __syncthreads();
+      // one token per wave at a time, lane l holding output l of the tile
+      // row: Phi_s = D_L P H D_R (s >= 1), H (s = 0), the identity (s = -1)
+      const XfTables &tl = *reinterpret_cast<const XfTables *>(xtl);
+      const bool bad = useed < -1 || useed > kTransformSeeds;
+      int src = lane;
+      uint32_t fl = 0u, fr = 0u;
+      if (useed >= 1 && !bad) {
+        src = tl.perm[useed - 1][lane];
+        fl = (uint32_t)(tl.dlm[useed - 1] >> lane) & 1u;
+        fr = (uint32_t)(tl.drm[useed - 1] >> lane) & 1u;
+      }
+      for (int t = wave; t < xrows; t += WAVES) {
+        float v = ys[t * 64 + lane];
+        if (bad) {
+          v = __builtin_nanf("");
+        } else if (useed >= 0) {
+          v = __uint_as_float(__float_as_uint(v) ^ (fr << 31));                          // D_R
+          v = xf_fwht64(v, lane);                                                         // H
+          v = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(v)));  // P: from perm[l]
+          v = __uint_as_float(__float_as_uint(v) ^ (fl << 31));                          // D_L
+        }
+        if (a.bias) v += bv;
+        a.Y[(size_t)(mbase + t) * a.N + (size_t)r * 64 + lane] = v;
+      }
+      return;
+    }
     if (Z > 1) {
       // Chunked K: the workgroup's sum goes to slot zc of its row group; the
       // workgroup that completes the row block's set of Z (arrival counter,
@@ -639,8 +805,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
       return;
     }
     const size_t n = (size_t)r * 64 + rg * 16 + i16;
-    const float b = a.bias ? a.bias[n] : 0.0f;
     if (MODE == kValu) {
+      const float b = a.bias ? a.bias[n] : 0.0f;
       if (g == 0) {
         const float fv[4] = {F[0].x, F[0].y, F[0].z, F[0].w};
 #pragma unroll
@@ -648,13 +814,14 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL> a) 
           if (m < M) a.Y[(size_t)m * a.N + n] = GRP ? fv[m] + b : fv[m] * a.sx[m] + b;
       }
     } else {
+      const float b = GRP ? (a.bias ? a.bias[n] : 0.0f) : bv;
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg) {
         const float fv[4] = {F[mg].x, F[mg].y, F[mg].z, F[mg].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = mbase + mg * 16 + 4 * g + e;
-          if (m < M) a.Y[(size_t)m * a.N + n] = GRP ? fv[e] + b : fv[e] * a.sx[m] + b;
+          if (m < M) a.Y[(size_t)m * a.N + n] = GRP ? fv[e] + b : fv[e] * sxv[mg][e] + b;
         }
       }
     }
@@ -671,14 +838,14 @@ void launch_one(Kern kern, dim3 grid, dim3 block, size_t lds, hipStream_t stream
 // Grid: row blocks (4R/RG) along x, token chunks along y, column chunks
 // along z.
 template <int BK, int MODE, int MG, int WAVES, int DEPTH, int XMODE, bool PARTIALS, bool INL, bool GRP,
-          bool WNT>
-void launch_rg(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL> &args) {
+          bool WNT, bool XF>
+void launch_rg(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL, XF> &args) {
   const dim3 block(WAVES * 64);
   const int y = args.ychunks, z = p.Z;
   switch (p.RG) {
-    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS, INL, GRP, WNT>, dim3(R, y, z), block, p.lds, stream, args); break;
-    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS, INL, GRP, WNT>, dim3(R * 2, y, z), block, p.lds, stream, args); break;
-    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS, INL, GRP, WNT>, dim3(R * 4, y, z), block, p.lds, stream, args); break;
+    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS, INL, GRP, WNT, XF>, dim3(R, y, z), block, p.lds, stream, args); break;
+    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS, INL, GRP, WNT, XF>, dim3(R * 2, y, z), block, p.lds, stream, args); break;
+    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS, INL, GRP, WNT, XF>, dim3(R * 4, y, z), block, p.lds, stream, args); break;
   }
 }
 
@@ -686,38 +853,53 @@ void launch_rg(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL> 
 // (one token chunk): measured 4-10% faster where they stream from HBM.  A
 // call of several token chunks re-reads them, and the later chunks find them
 // in the last-level cache only if the first chunk's loads allocated there.
-template <int BK, bool PARTIALS, bool INL, bool GRP>
-void launch_mode(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL> &args) {
-  if (p.mode == kValu) {
-    launch_rg<BK, kValu, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP, true>(p, R, stream, args);
-    return;
+template <int BK, bool PARTIALS, bool INL, bool GRP, bool XF>
+void launch_mode(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL, XF> &args) {
+  if constexpr (!XF) {
+    if (p.mode == kValu) {
+      launch_rg<BK, kValu, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP, true, XF>(p, R, stream, args);
+      return;
+    }
   }
   if (p.xmode == kXPriv) {
-    launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP, true>(p, R, stream, args);
+    launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP, true, XF>(p, R, stream, args);
     return;
   }
-  if (PARTIALS || p.mchunks == 1) {
+  // (the transformed route keeps the non-temporal loads for every call: one
+  // set of kernels fewer to build)
+  if (PARTIALS || XF || p.mchunks == 1) {
     switch (p.MG) {
-      case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, PARTIALS, INL, GRP, true>(p, R, stream, args); break;
-      case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, PARTIALS, INL, GRP, true>(p, R, stream, args); break;
-      case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, PARTIALS, INL, GRP, true>(p, R, stream, args); break;
-      default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, PARTIALS, INL, GRP, true>(p, R, stream, args); break;
+      case 1: launch_rg<BK, kMfma, 1, 16, kSharedDepth1, kXShared, PARTIALS, INL, GRP, true, XF>(p, R, stream, args); break;
+      case 2: launch_rg<BK, kMfma, 2, 16, kSharedDepthN, kXShared, PARTIALS, INL, GRP, true, XF>(p, R, stream, args); break;
+      case 3: launch_rg<BK, kMfma, 3, 8, kSharedDepthN, kXShared, PARTIALS, INL, GRP, true, XF>(p, R, stream, args); break;
+      default: launch_rg<BK, kMfma, 4, 8, kSharedDepthN, kXShared, PARTIALS, INL, GRP, true, XF>(p, R, stream, args); break;
     }
     return;
   }
-  if constexpr (!PARTIALS) {
+  if constexpr (!PARTIALS && !XF) {
     switch (p.MG) {
-      case 1: launch_rg<BK, kMfma, 1, 16, 8, kXShared, false, INL, GRP, false>(p, R, stream, args); break;
-      case 2: launch_rg<BK, kMfma, 2, 16, 6, kXShared, false, INL, GRP, false>(p, R, stream, args); break;
-      case 3: launch_rg<BK, kMfma, 3, 8, 6, kXShared, false, INL, GRP, false>(p, R, stream, args); break;
-      default: launch_rg<BK, kMfma, 4, 8, 6, kXShared, false, INL, GRP, false>(p, R, stream, args); break;
+      case 1: launch_rg<BK, kMfma, 1, 16, kSharedDepth1, kXShared, false, INL, GRP, false, XF>(p, R, stream, args); break;
+      case 2: launch_rg<BK, kMfma, 2, 16, kSharedDepthN, kXShared, false, INL, GRP, false, XF>(p, R, stream, args); break;
+      case 3: launch_rg<BK, kMfma, 3, 8, kSharedDepthN, kXShared, false, INL, GRP, false, XF>(p, R, stream, args); break;
+      default: launch_rg<BK, kMfma, 4, 8, kSharedDepthN, kXShared, false, INL, GRP, false, XF>(p, R, stream, args); break;
     }
   }
 }
 
 // Whether a call passes the metadata inside the kernel arguments.
-bool inline_meta(const PackedView &w) {
-  return w.meta && w.C <= 128 && kMetaStride * w.R <= kInlineWords;
+bool inline_meta(const PackedView &w, bool xform) {
+  return w.meta && w.C <= 128 && kMetaStride * w.R <= (xform ? kInlineWordsXf : kInlineWords);
+}
+
+XfTables xf_tables(const TransformTables &t) {
+  XfTables x{};
+  for (int j = 0; j < kTransformSeeds; ++j)
+    for (int e = 0; e < 64; ++e) {
+      x.perm[j][e] = t.perm[j][e];
+      if (t.dl[j][e] < 0) x.dlm[j] |= 1ull << e;
+      if (t.dr[j][e] < 0) x.drm[j] |= 1ull << e;
+    }
+  return x;
 }
 
 // Scratch of the allocation-free decode entry point: the chunked-K
@@ -761,11 +943,17 @@ hipError_t decode_scratch(hipStream_t stream, void **out) {
   return hipSuccess;
 }
 
-hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx, int M,
-                         const float *bias, float *Y, int split, void *ws, int32_t *P,
-                         hipStream_t stream, bool grouped) {
-  DecodePlan p = plan_decode(w, M, split);
-  if (!decode_plan_ok(p, w) || p.ylaunch < 1) return hipErrorInvalidValue;
+namespace {
+
+// The launches of one decode call (tables != nullptr: with the output
+// transform in the epilogue).
+hipError_t decode_launches(const PackedView &w, const int8_t *qx, const float *sx, int M,
+                           const float *bias, float *Y, int split, void *ws, int32_t *P,
+                           hipStream_t stream, bool grouped, const int8_t *useeds,
+                           const TransformTables *tables) {
+  const bool xf = tables != nullptr;
+  DecodePlan p = plan_decode(w, M, split, xf);
+  if (!decode_plan_ok(p, w, xf) || p.ylaunch < 1) return hipErrorInvalidValue;
   if (grouped && M <= kValuMaxM) p.mode = kValu;
   DecodeArgs args;
   args.labels = w.labels; args.off4 = w.off4; args.off8 = w.off8;
@@ -779,14 +967,20 @@ hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx,
   args.xstride = p.xstride;
   args.cnt = nullptr;
   args.part = nullptr;
-  if (p.Z > 1 && !P) {  // the products need no chunk sums
+  if (p.ws_bytes > 0 && !P) {  // the products need no hand-over
     args.cnt = static_cast<uint32_t *>(ws);
     args.part = reinterpret_cast<float4 *>(static_cast<uint8_t *>(ws) + p.cnt_bytes);
   }
+  XfArgs xa{};
+  if (xf) {
+    xa.useeds = useeds;
+    xa.xt = xf_tables(*tables);
+  }
+  const bool inl = !P && !grouped && inline_meta(w, xf);
   // token ranges of ylaunch chunks of 16*MG tokens, one launch each
   const int mstep = p.ylaunch * 16 * p.MG;
   for (int m0 = 0; m0 < M; m0 += mstep) {
-    DArgs<false> la;
+    DArgs<false, false> la;
     static_cast<DecodeArgs &>(la) = args;
     la.M = M - m0 < mstep ? M - m0 : mstep;
     la.qx = qx + (size_t)m0 * w.K;
@@ -805,8 +999,21 @@ hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx,
     } else if (grouped) {
       if (w.bK == 128) launch_mode<128, false, false, true>(p, w.R, stream, la);
       else launch_mode<64, false, false, true>(p, w.R, stream, la);
-    } else if (inline_meta(w)) {
-      DArgs<true> li;
+    } else if (xf && inl) {
+      DArgs<true, true> li;
+      static_cast<DecodeArgs &>(li) = la;
+      li.xf = xa;
+      std::memcpy(li.meta, w.meta, sizeof(uint32_t) * kMetaStride * w.R);
+      if (w.bK == 128) launch_mode<128, false, true, false>(p, w.R, stream, li);
+      else launch_mode<64, false, true, false>(p, w.R, stream, li);
+    } else if (xf) {
+      DArgs<false, true> lx;
+      static_cast<DecodeArgs &>(lx) = la;
+      lx.xf = xa;
+      if (w.bK == 128) launch_mode<128, false, false, false>(p, w.R, stream, lx);
+      else launch_mode<64, false, false, false>(p, w.R, stream, lx);
+    } else if (inl) {
+      DArgs<true, false> li;
       static_cast<DecodeArgs &>(li) = la;
       std::memcpy(li.meta, w.meta, sizeof(uint32_t) * kMetaStride * w.R);
       if (w.bK == 128) launch_mode<128, false, true, false>(p, w.R, stream, li);
@@ -819,6 +1026,21 @@ hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx,
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const PackedView &w, const int8_t *qx, const float *sx, int M,
+                         const float *bias, float *Y, int split, void *ws, int32_t *P,
+                         hipStream_t stream, bool grouped) {
+  return decode_launches(w, qx, sx, M, bias, Y, split, ws, P, stream, grouped, nullptr, nullptr);
+}
+
+hipError_t launch_decode_transformed(const PackedView &w, const int8_t *qx, const float *sx, int M,
+                                     const float *bias, float *Y, int split, void *ws,
+                                     const int8_t *useeds, const TransformTables &t,
+                                     hipStream_t stream) {
+  return decode_launches(w, qx, sx, M, bias, Y, split, ws, nullptr, stream, false, useeds, &t);
 }
 
 }  // namespace aq

@@ -122,8 +122,11 @@ constexpr int kLdsBudget = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kValuMaxM = 1;            // largest M on the vector-ALU path
 constexpr int kPrivMaxM = 4;            // largest M with per-wave activation slices
 constexpr int kPrivDepth = 8;           // tiles per batch with per-wave activation slices
+constexpr int kSharedDepth1 = 8;        // tiles per batch, shared staging, one token group
+constexpr int kSharedDepthN = 6;        // tiles per batch, shared staging, 2-4 token groups
 constexpr int kDecodeCounters = 65536;  // arrival counters at the head of a decode workspace
 constexpr int kInlineWords = 896;       // metadata words that may travel in the kernel arguments
+constexpr int kInlineWordsXf = 768;     // the same with the output-transform tables beside them
 constexpr int kMetaStride = 6;          // words per tile row in the host metadata image
 enum { kValu = 0, kMfma = 1 };
 // Where the MFMA/VALU activation operands come from: a per-wave LDS slice
@@ -143,13 +146,19 @@ struct DecodePlan {
   int mode, xmode, MG, waves, RG, S, Z, mchunks, ylaunch, xstride;
   size_t lds, cnt_bytes, ws_bytes;
 };
-// split = 0: adaptive; otherwise S, one of the supported values.
-DecodePlan plan_decode(const PackedView &w, int M, int split);
-// false when a chunked plan has more row blocks than arrival counters
-bool decode_plan_ok(const DecodePlan &p, const PackedView &w);
+// split = 0: adaptive; otherwise S, one of the supported values.  xform:
+// the call applies the output transform in its epilogue, which needs the
+// whole 64-row tile row in one workgroup; when the plan spreads a tile row
+// over several workgroups (RG < 4 or Z > 1), their sums meet in the
+// workspace (counters per tile row and token chunk, then the sums) and the
+// last of them finishes the tile row.
+DecodePlan plan_decode(const PackedView &w, int M, int split, bool xform = false);
+// false when a plan that hands sums over needs more arrival counters than
+// the workspace holds
+bool decode_plan_ok(const DecodePlan &p, const PackedView &w, bool xform = false);
 int decode_split(const PackedView &w, int M);
 bool decode_split_supported(const PackedView &w, int M, int S);
-size_t decode_workspace_bytes(const PackedView &w, int M, int split);
+size_t decode_workspace_bytes(const PackedView &w, int M, int split, bool xform = false);
 // The allocation-free decode's device scratch (AQ_DECODE_SCRATCH_BYTES):
 // its address on the current device, found once per device with
 // hipGetSymbolAddress; the first call on a device also enqueues, on
@@ -172,5 +181,14 @@ constexpr int kQuantTransformMaxK = 40768;
 hipError_t launch_quant_act_transformed(const float *X, int M, int K, const int8_t *seeds,
                                         const TransformTables &t, int8_t *qx, float *sx,
                                         hipStream_t stream);
+// Decode with the output transform in the epilogue: the same sums as
+// launch_decode, scaled by sx, then Y~ U per tile row (useeds: device, R
+// seeds), then the bias; bit for bit launch_decode without the bias
+// followed by launch_transform(kTransformOut) with it.  ws as
+// decode_workspace_bytes(w, M, split, true).
+hipError_t launch_decode_transformed(const PackedView &w, const int8_t *qx, const float *sx, int M,
+                                     const float *bias, float *Y, int split, void *ws,
+                                     const int8_t *useeds, const TransformTables &t,
+                                     hipStream_t stream);
 
 }  // namespace aq

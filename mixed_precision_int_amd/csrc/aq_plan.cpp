@@ -78,7 +78,7 @@ void choose_chunks(const PackedView &w, int M, int MG, int *RG, int *Z) {
 
 }  // namespace
 
-DecodePlan plan_decode(const PackedView &w, int M, int split) {
+DecodePlan plan_decode(const PackedView &w, int M, int split, bool xform) {
   DecodePlan p;
   p.MG = mgroups(w, M);
   p.waves = waves_of(w, M);
@@ -127,11 +127,40 @@ DecodePlan plan_decode(const PackedView &w, int M, int split) {
   p.S = p.waves / p.RG;
   if (p.mode == kValu || p.xmode == kXPriv) p.ylaunch = 1;
   if (p.ylaunch > 65535) p.ylaunch = 65535;  // grid y limit
+  if (xform) {
+    // Keep the tile row in one workgroup (4 row groups, no hand-over) when
+    // each wave's share of the row still fits one batch of loads.  Measured
+    // on the Llama-3.2-3B-shaped projections at M = 1..16: the hand-over
+    // (three device-scope round trips, about 1.7 us) costs more than the
+    // slower stream of the fewer, wider workgroups on rows of 24 tile
+    // columns (qkv, o: 6.8 / 6.5 us against 7.3 / 7.0 us at M = 1), less on
+    // rows of 64 (down: 8.6 against 13.7 us).
+    if (split == 0 && p.Z == 1 && p.RG < 4) {
+      const int s4 = p.waves / 4;
+      const int depth = p.xmode == kXPriv ? kPrivDepth : p.MG == 1 ? kSharedDepth1 : kSharedDepthN;
+      if ((w.C + s4 - 1) / s4 <= depth) {
+        p.RG = 4;
+        p.S = s4;
+      }
+    }
+    if ((4 / p.RG) * p.Z > 1) {
+      // one counter per tile row and token chunk of a launch
+      const int cap = kDecodeCounters / w.R;
+      if (p.ylaunch > cap) p.ylaunch = cap;
+      p.cnt_bytes = (size_t)kDecodeCounters * 4;
+      p.ws_bytes = p.cnt_bytes + (size_t)w.R * 4 * p.ylaunch * p.Z * p.MG * 64 * sizeof(float4);
+    }
+    // a flag word, the transform tables, then the tile row's 64 scaled sums
+    // per token
+    const size_t ylds = 768 + (size_t)16 * p.MG * 64 * sizeof(float);
+    if (p.lds < ylds) p.lds = ylds;
+  }
   return p;
 }
 
-bool decode_plan_ok(const DecodePlan &p, const PackedView &w) {
+bool decode_plan_ok(const DecodePlan &p, const PackedView &w, bool xform) {
   if ((long long)w.C * p.Z * p.S >= (1LL << 31)) return false;  // 32-bit split bounds
+  if (xform && (4 / p.RG) * p.Z > 1 && w.R > kDecodeCounters) return false;
   return p.Z == 1 || w.R * 4 / p.RG <= kDecodeCounters;
 }
 
@@ -142,8 +171,8 @@ bool decode_split_supported(const PackedView &w, int M, int S) {
   return S == W || S == W / 2 || S == W / 4;
 }
 
-size_t decode_workspace_bytes(const PackedView &w, int M, int split) {
-  return plan_decode(w, M, split).ws_bytes;
+size_t decode_workspace_bytes(const PackedView &w, int M, int split, bool xform) {
+  return plan_decode(w, M, split, xform).ws_bytes;
 }
 
 size_t expand_bytes(const PackedView &w) {

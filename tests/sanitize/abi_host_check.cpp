@@ -54,6 +54,19 @@ static Fake make(int N, int K, int bK, double frac4, unsigned seed) {
   return f;
 }
 
+// Valid transform tables: signed permutations of 64 elements.
+static aq_transform_tables make_tables() {
+  aq_transform_tables t{};
+  for (int s = 0; s < AQ_TRANSFORM_SEEDS; ++s)
+    for (int e = 0; e < 64; ++e) {
+      t.perm[s][e] = (uint8_t)((e * 5 + s) % 64);
+      t.dl[s][e] = (e + s) % 3 ? 1 : -1;
+      t.dr[s][e] = (e * s) % 2 ? -1 : 1;
+    }
+  return t;
+}
+static const aq_transform_tables g_tables = make_tables();
+
 // launches: whether the failure comes from a launcher (else from the HIP
 // copies that precede it, as in packing)
 static void expect_launch(aq_status (*call)(void *), void *ctx, const char *name, bool launches = true) {
@@ -163,6 +176,36 @@ int main() {
           return aq_linear_decode_grouped(&c->f->p, (const int8_t *)dev(0), (const float *)dev(4096), c->M,
                                           nullptr, (float *)dev(8192), 0, c->wd, c->nd, nullptr); }, &c,
                       "aq_linear_decode_grouped");
+      }
+      {
+        // the transformed decode: its own workspace size (hand-over of tile rows)
+        const size_t wx = aq_workspace_bytes(&f.p, M, AQ_PHASE_DECODE_TRANSFORMED, 0);
+        CHECK(wx >= wd);
+        std::vector<unsigned char> wsx(wx + 256);
+        unsigned char *wsx_a = wsx.data() + (256 - (uintptr_t)wsx.data() % 256) % 256;
+        struct X { Fake *f; int M; void *w; size_t n; } xc{&f, M, wx ? wsx_a : nullptr, wx};
+        expect_launch([](void *v) { X *c = (X *)v;
+          return aq_linear_decode_transformed(&c->f->p, (const int8_t *)dev(0), (const float *)dev(4096), c->M,
+                                              (const float *)dev(12288), (const int8_t *)dev(16384), &g_tables,
+                                              (float *)dev(8192), 0, c->w, c->n, nullptr); }, &xc,
+                      "aq_linear_decode_transformed");
+        const int before = g_launches;
+        if (wx)
+          CHECK(aq_linear_decode_transformed(&f.p, (const int8_t *)dev(0), (const float *)dev(4096), M, nullptr,
+                                             (const int8_t *)dev(16384), &g_tables, (float *)dev(8192), 0, wsx_a,
+                                             wx - 1, nullptr) == AQ_ERR_WORKSPACE);
+        CHECK(aq_linear_decode_transformed(&f.p, (const int8_t *)dev(0), (const float *)dev(4096), M, nullptr,
+                                           nullptr, &g_tables, (float *)dev(8192), 0, xc.w, xc.n,
+                                           nullptr) == AQ_ERR_NULL);
+        aq_transform_tables bad = g_tables;
+        bad.dl[1][3] = 2;
+        CHECK(aq_linear_decode_transformed(&f.p, (const int8_t *)dev(0), (const float *)dev(4096), M, nullptr,
+                                           (const int8_t *)dev(16384), &bad, (float *)dev(8192), 0, xc.w, xc.n,
+                                           nullptr) == AQ_ERR_ARG);
+        CHECK(aq_linear_decode_transformed(&f.p, (const int8_t *)dev(0), (const float *)dev(4096), M, nullptr,
+                                           (const int8_t *)dev(16384), &g_tables, (float *)dev(8192), 5, xc.w,
+                                           xc.n, nullptr) == AQ_ERR_ARG);
+        CHECK(g_launches == before);
       }
       {
         const size_t wg = aq_workspace_bytes(&f.p, M, AQ_PHASE_PREFILL_GROUPED, 0);

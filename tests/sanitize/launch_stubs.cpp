@@ -60,6 +60,11 @@ hipError_t launch_quant_act_transformed(const float *, int, int, const int8_t *,
                                         int8_t *, float *, hipStream_t) {
   return launched();
 }
+hipError_t launch_decode_transformed(const PackedView &, const int8_t *, const float *, int, const float *,
+                                     float *, int, void *, const int8_t *, const TransformTables &,
+                                     hipStream_t) {
+  return launched();
+}
 hipError_t decode_scratch(hipStream_t, void **out) {
   static unsigned char fake[64];
   *out = fake;

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(aqlib):
 
 
 def test_abi_version_and_status_strings(aqlib):
-    assert B.aq_abi_version() == 9
+    assert B.aq_abi_version() == 10
     for code in list(B.STATUS) + [-99]:
         assert aqlib.aq_status_string(code)
 
@@ -288,3 +288,36 @@ def test_prefill_transformed_rejected(aqlib):
                                                     k.get("ws", None), k.get("n", 0), None)
     assert f(M=0) == 0 and f(us=None) == -1 and f(t=None) == -1
     assert f(M=1024) == -6                     # long prompt with INT4 tiles: the operand workspace
+
+
+def test_decode_transformed_workspace(aqlib):
+    """The transformed decode needs the whole 64-row tile row in one
+    workgroup.  Where the plan gives a tile row's row groups to several
+    workgroups (few tile rows of many columns) or cuts its columns into
+    chunks, the sums meet in a workspace (counters in the fixed 256 KiB
+    head, then the sums); where one workgroup holds the tile row (many tile
+    rows, or rows short enough for one batch of loads per wave), none is
+    needed.  A call without it is rejected on the host."""
+    from workloads import gen
+    L = B.lib()
+    ws = L.aq_workspace_bytes
+    t = B.transform_tables(*gen.transform_tables())
+    f = lambda d, M, w=None, n=0, split=0, us=FAKE: L.aq_linear_decode_transformed(
+        ctypes.byref(d), FAKE, FAKE, M, None, us, ctypes.byref(t), FAKE, split, w, n, None)
+    few = fake_packed(N=3072, K=8192, T4=48 * 64 - 5, T8=5)        # 48 tile rows of 64 columns
+    short = fake_packed(N=3072, K=3072, T4=48 * 24 - 5, T8=5)      # 48 tile rows of 24 columns
+    many = fake_packed(N=16384, K=3072, T4=256 * 24 - 9, T8=9)     # 256 tile rows
+    for M in (1, 4, 16):
+        need = ws(ctypes.byref(few), M, B.AQ_PHASE_DECODE_TRANSFORMED, 0)
+        assert need > 256 * 1024 and need % 16 == 0, (M, need)
+        assert ws(ctypes.byref(few), M, B.AQ_PHASE_DECODE, 0) == 0
+        assert f(few, M) == -6 and f(few, M, FAKE, need - 1) == -6 and f(few, M, FAKE + 4, need) == -5
+        assert ws(ctypes.byref(many), M, B.AQ_PHASE_DECODE_TRANSFORMED, 0) == 0
+        assert ws(ctypes.byref(short), M, B.AQ_PHASE_DECODE_TRANSFORMED, 0) == 0
+        # a fixed split of 16 waves per row group spreads the tile row over 4 workgroups
+        assert ws(ctypes.byref(short), M, B.AQ_PHASE_DECODE_TRANSFORMED, 16) > 256 * 1024
+        # a fixed split of 4 waves per row group keeps the tile row in one workgroup
+        assert ws(ctypes.byref(few), M, B.AQ_PHASE_DECODE_TRANSFORMED, 4) == 0
+    big = fake_packed(N=256, K=65536, T4=4 * 512 - 3, T8=3)        # column chunks
+    assert ws(ctypes.byref(big), 16, B.AQ_PHASE_DECODE_TRANSFORMED, 0) >= ws(ctypes.byref(big), 16, 0, 0) > 0
+    assert f(many, 0) == 0 and f(many, 4, us=None) == -1 and f(many, 4, split=5) == -8

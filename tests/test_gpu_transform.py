@@ -298,3 +298,108 @@ def test_prefill_transformed_bad_seed():
     qx, sx = aq.aq_quant_act(to_dev(gen.acts_heavy_tail(rng, 1024, 256)))
     Y = aq.aq_linear_prefill_transformed(pw, qx, sx, np.array([0, 9], np.int8), TABLES).cpu().numpy()
     assert np.isfinite(Y[:, :64]).all() and np.isnan(Y[:, 64:]).all()
+
+
+# Decode with U in its epilogue.  The Llama-3.2-3B-shaped projections cover
+# every way the planner lays out a tile row: one workgroup per tile row
+# (gate_up, 4 row groups per workgroup), row groups spread over 2 or 4
+# workgroups (qkv, o, down at M <= 32), and column chunks (down at M = 64,
+# whose activations do not fit on chip), at M in the per-wave-slice (<= 4),
+# shared-staging and multi-chunk (> 64 tokens) routes.
+DECODE_XF_CASES = [("qkv", 5120, 3072, 1), ("o", 3072, 3072, 4), ("gate_up", 16384, 3072, 16),
+                   ("down", 3072, 8192, 16), ("down", 3072, 8192, 64), ("o", 3072, 3072, 33),
+                   ("qkv", 5120, 3072, 100), ("small64", 256, 640, 5)]
+
+
+def _decode_xf_setup(name, N, K, M, seed):
+    bK = 64 if name == "small64" else 128
+    rng = np.random.default_rng(seed)
+    W = gen.weights(rng, N, K)
+    z = gen.map_uniform(rng, N // 64, K // bK, 0.25)
+    X = gen.acts_outliers(rng, M, K, max(1, K // 100), 25.0)
+    us = every_seed(rng, N // 64)
+    b = rng.standard_normal(N).astype(np.float32)
+    pw = aq.aq_pack_weights(to_dev(W), aq.aq_labels_from_map(z.astype(np.uint8)), 64, bK)
+    qx, sx = aq.aq_quant_act(to_dev(X))
+    return pw, qx, sx, us, to_dev(b)
+
+
+@pytest.mark.parametrize("name,N,K,M", DECODE_XF_CASES)
+def test_decode_transformed_bit_exact(name, N, K, M):
+    """aq_linear_decode_transformed is bit for bit aq_linear_decode (no bias)
+    with the same split followed by aq_transform_out (bias), at every fixed
+    split (which moves the tile row between one workgroup and several), with
+    and without a bias.  The adaptive call takes either the plain decode's
+    adaptive split or 4 waves per row group (the tile row in one workgroup),
+    and matches that call bit for bit."""
+    pw, qx, sx, us, b = _decode_xf_setup(name, N, K, M, N + K + M)
+    Wv = 16 if M <= 32 else 8
+    for bias in (b, None):
+        refs = {}
+        for split in (Wv, Wv // 2, Wv // 4):
+            say(f"  decode_transformed {name} {N}x{K} M={M} split={split} bias={bias is not None}")
+            Yt = aq.aq_linear_decode(pw, qx, sx, split=split)
+            ref = aq.aq_transform_out(Yt, us, TABLES, bias=bias).cpu().numpy()
+            Y = aq.aq_linear_decode_transformed(pw, qx, sx, us, TABLES, bias=bias, split=split)
+            torch.cuda.synchronize()
+            assert_bits_equal(Y.cpu().numpy(), ref, f"{name}/M{M}/split{split}")
+            refs[split] = ref
+        Y0 = aq.aq_linear_decode_transformed(pw, qx, sx, us, TABLES, bias=bias).cpu().numpy()
+        cands = (aq.aq_decode_split(pw, M), Wv // 4)
+        assert any(np.array_equal(bits(Y0), bits(refs[c])) for c in cands), \
+            f"{name}/M{M}: the adaptive call matches neither split {cands}"
+
+
+def test_decode_transformed_against_oracle():
+    """The fused decode end to end against the oracle's transformed layer:
+    W~ = U W V packed, X~ = X V quantized in one pass, Y = Y~ U + bias from the
+    decode epilogue, on the Llama-3.2-3B-shaped o projection at M = 4 (row
+    groups of a tile row in four workgroups) and a 64 x 64-tile case."""
+    for N, K, bK, M in ((3072, 3072, 128, 4), (256, 640, 64, 7)):
+        rng = np.random.default_rng(5 + N + M)
+        W = gen.weights(rng, N, K)
+        X = gen.acts_outliers(rng, M, K, max(1, K // 100), 25.0)
+        z = gen.map_uniform(rng, N // 64, K // bK, 0.3)
+        us, vs = every_seed(rng, N // 64), every_seed(rng, K // 64)
+        b = rng.standard_normal(N).astype(np.float32)
+        say(f"  fused transformed decode {N}x{K}/bK{bK}/M{M} against the oracle")
+        Wt_r = O.transform_weights(W, us, vs, TABLES)
+        codes, sW = O.quant_weights(Wt_r, z, 64, bK)
+        qx_r, sx_r = O.quant_act(O.transform_rows(X, vs, TABLES))
+        P = O.tile_partials(qx_r, codes, bK)
+        yt = O.linear_from_partials(P, sx_r, sW)
+        y_ref = O.transform_out(yt, us, TABLES) + b.astype(np.float64)[None, :]
+        pw = aq.aq_pack_weights(aq.aq_transform_weights(to_dev(W), us, vs, TABLES),
+                                aq.aq_labels_from_map(z.astype(np.uint8)), 64, bK)
+        qx, sx = aq.aq_quant_act_transformed(to_dev(X), vs, TABLES)
+        Y = aq.aq_linear_decode_transformed(pw, qx, sx, us, TABLES, bias=to_dev(b))
+        torch.cuda.synchronize()
+        assert np.array_equal(qx.cpu().numpy().astype(np.int64), qx_r), "codes differ"
+        assert_blocks_close(Y.cpu().numpy(), y_ref, f"fused transformed decode {N}x{K}", rel=1e-4, src=yt)
+
+
+def test_decode_transformed_calls_in_a_row():
+    """Calls that hand tile rows over leave their arrival counters at zero:
+    transformed and plain decode calls of different sizes on one workspace,
+    one after another, each equal to its reference."""
+    pw, qx, sx, us, b = _decode_xf_setup("o", 3072, 3072, 64, 11)
+    need = max(aq.aq_workspace_bytes(pw, M, ph, 16 if M <= 32 else 8) for M in (1, 16, 64)
+               for ph in (aq.AQ_PHASE_DECODE, aq.AQ_PHASE_DECODE_TRANSFORMED))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for M in (16, 1, 64, 16):
+        sp = 16 if M <= 32 else 8  # one row group per workgroup: every tile row handed over
+        say(f"  decode_transformed in a row: M={M} split={sp}")
+        Yt = aq.aq_linear_decode(pw, qx[:M], sx[:M], split=sp, ws=ws)
+        ref = aq.aq_transform_out(Yt, us, TABLES, bias=b)
+        Y = aq.aq_linear_decode_transformed(pw, qx[:M], sx[:M], us, TABLES, bias=b, split=sp, ws=ws)
+        torch.cuda.synchronize()
+        assert_bits_equal(Y.cpu().numpy(), ref.cpu().numpy(), f"in a row M={M}")
+    assert int(ws[:4 * 65536].view(torch.int32).abs().sum()) == 0, "arrival counters left set"
+
+
+def test_decode_transformed_bad_seed():
+    """A seed outside -1 .. 6 turns its tile row's outputs NaN; the others
+    are finite."""
+    pw, qx, sx, _, _ = _decode_xf_setup("small64", 256, 640, 3, 2)
+    Y = aq.aq_linear_decode_transformed(pw, qx, sx, np.array([0, 9, -1, 6], np.int8), TABLES).cpu().numpy()
+    assert np.isfinite(Y[:, :64]).all() and np.isnan(Y[:, 64:128]).all() and np.isfinite(Y[:, 128:]).all()
