@@ -261,6 +261,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
   const int zc = blockIdx.z;  // input-column chunk of this workgroup
   const int yc = blockIdx.y;  // token chunk
   const int bx = blockIdx.x;  // row block
+  const int Y = gridDim.y;    // token chunks of this launch
   const int r = bx / blocks_per_row;
   const int rgl = wave % RG;  // row group inside the block
   const int rg = (bx % blocks_per_row) * RG + rgl;
@@ -691,7 +692,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
       float *ys = reinterpret_cast<float *>(smem + 768);         // [16*MG tokens][64 outputs]
       constexpr int kParts = 4 / RG;                      // workgroups per tile row and chunk
       if (kParts * Z > 1) {
-        float4 *pp = a.part + ((size_t)(r * 4 + rg) * gridDim.y + yc) * Z * MG * 64 + lane;
+        float4 *pp = a.part + ((size_t)(r * 4 + rg) * Y + yc) * Z * MG * 64 + lane;
         if (sp == 0) {
 #pragma unroll
           for (int mg = 0; mg < MG; ++mg) store_coherent(pp + ((size_t)zc * MG + mg) * 64, F[mg]);
@@ -699,7 +700,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
         }
         __syncthreads();
         if (tid == 0) {
-          uint32_t *cp = a.cnt + (size_t)r * gridDim.y + yc;
+          uint32_t *cp = a.cnt + (size_t)r * Y + yc;
           const uint32_t prev = __hip_atomic_fetch_add(cp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const uint32_t last = prev == (uint32_t)(kParts * Z - 1) ? 1u : 0u;
           if (last) __hip_atomic_store(cp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -708,7 +709,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
         __syncthreads();
         if (*flag == 0u) return;
         if (wave < 4) {  // wave w takes row group w
-          const float4 *qp = a.part + ((size_t)(r * 4 + wave) * gridDim.y + yc) * Z * MG * 64 + lane;
+          const float4 *qp = a.part + ((size_t)(r * 4 + wave) * Y + yc) * Z * MG * 64 + lane;
 #pragma unroll
           for (int mg = 0; mg < MG; ++mg) {
             float4 v = load_coherent(qp + mg * 64);
@@ -775,7 +776,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
       // its stores have completed before the barrier that precedes the
       // counter increment, and the last workgroup reads the slots only after
       // its increment has returned.
-      float4 *pp = a.part + ((size_t)(r * 4 + rg) * gridDim.y + yc) * Z * MG * 64 + lane;
+      float4 *pp = a.part + ((size_t)(r * 4 + rg) * Y + yc) * Z * MG * 64 + lane;
       if (sp == 0) {
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg) store_coherent(pp + ((size_t)zc * MG + mg) * 64, F[mg]);
@@ -784,7 +785,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
       __syncthreads();
       uint32_t *flag = reinterpret_cast<uint32_t *>(smem);  // LDS is free again
       if (tid == 0) {
-        uint32_t *cp = a.cnt + (size_t)bx * gridDim.y + yc;
+        uint32_t *cp = a.cnt + (size_t)bx * Y + yc;
         const uint32_t prev = __hip_atomic_fetch_add(cp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t last = prev == (uint32_t)(Z - 1) ? 1u : 0u;
         if (last) __hip_atomic_store(cp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -841,11 +842,11 @@ template <int BK, int MODE, int MG, int WAVES, int DEPTH, int XMODE, bool PARTIA
           bool WNT, bool XF>
 void launch_rg(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL, XF> &args) {
   const dim3 block(WAVES * 64);
-  const int y = args.ychunks, z = p.Z;
+  const dim3 grid(R * (4 / p.RG), args.ychunks, p.Z);
   switch (p.RG) {
-    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS, INL, GRP, WNT, XF>, dim3(R, y, z), block, p.lds, stream, args); break;
-    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS, INL, GRP, WNT, XF>, dim3(R * 2, y, z), block, p.lds, stream, args); break;
-    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS, INL, GRP, WNT, XF>, dim3(R * 4, y, z), block, p.lds, stream, args); break;
+    case 4: launch_one(decode_kernel<BK, MODE, MG, WAVES, 4, DEPTH, XMODE, PARTIALS, INL, GRP, WNT, XF>, grid, block, p.lds, stream, args); break;
+    case 2: launch_one(decode_kernel<BK, MODE, MG, WAVES, 2, DEPTH, XMODE, PARTIALS, INL, GRP, WNT, XF>, grid, block, p.lds, stream, args); break;
+    default: launch_one(decode_kernel<BK, MODE, MG, WAVES, 1, DEPTH, XMODE, PARTIALS, INL, GRP, WNT, XF>, grid, block, p.lds, stream, args); break;
   }
 }
 

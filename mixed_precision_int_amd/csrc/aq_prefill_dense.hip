@@ -354,10 +354,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_dense_kernel(const De
     __builtin_amdgcn_s_barrier();
     if constexpr (GRP && !PARTIALS) {
       // the previous column's second-group scales, from its stage slot
-      // before the issue below refills that stage
+      // before the issue below refills that stage.  Column 0 has none: its
+      // slot has not been loaded (it holds what an earlier kernel left in
+      // LDS, possibly a NaN, which times the zero products would still be
+      // NaN), so its scales are zero.
       const float *xs_ = stageX((q + S - 1) % S);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xp[i] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(xs_[2 * i + 1])));
+      for (int i = 0; i < 4; ++i)
+        xp[i] = j > 0 ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(xs_[2 * i + 1]))) : 0.f;
     }
     issue(min(j + S - 1, a.C - 1), (q + S - 1) % S);
     scp0 = scn0;

@@ -165,3 +165,38 @@ def test_grouped_long_route_full_size_sampled():
 
 def K_GROUPS(X):
     return X.shape[1] // 64
+
+
+def test_grouped_long_route_after_nan_in_lds():
+    """The grouped long-prompt GEMM reads no LDS it has not written: run
+    right after a kernel that leaves NaN across every compute unit's LDS (the
+    one-pass transformed quantizer staging 512 rows of 40768 features with an
+    invalid seed, 160 KiB of NaN per row), its outputs stay finite and within
+    the bar.  Column 0 has no previous column whose second-group scales it
+    would rescale; reading that unloaded stage slot once turned rows NaN."""
+    N, K, M = 512, 1024, 1040
+    rng = np.random.default_rng(1234)
+    W = gen.weights(rng, N, K)
+    z = gen.map_uniform(rng, N // 64, K // 128, 0.35)
+    X = gen.acts_outliers(rng, M, K, 4, 25.0)
+    b = rng.standard_normal(N).astype(np.float32)
+    codes, sW = O.quant_weights(W, z, 64, 128)
+    qx_r, sxg_r = O.quant_act_grouped(X)
+    P_r = O.group_partials(qx_r, codes)
+    y_r = O.linear_from_group_partials(P_r, sxg_r, sW, 128, b)
+    c_r = O.abs_contrib_grouped(P_r, sxg_r, sW, 128) + np.abs(b.astype(np.float64))[None, :]
+    pw = aq.aq_pack_weights(to_dev(W), aq.aq_labels_from_map(z.astype(np.uint8)), 64, 128)
+    qx, sxg = aq.aq_quant_act_grouped(to_dev(X))
+    bd = to_dev(b)
+    ws = torch.empty(max(16, aq.aq_workspace_bytes(pw, M, aq.AQ_PHASE_PREFILL_GROUPED)), dtype=torch.uint8,
+                     device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    Kn = 40768
+    Xn = torch.ones((512, Kn), dtype=torch.float32, device="cuda")
+    qn, sn = aq.aq_quant_act_transformed(Xn, np.full(Kn // 64, 9, np.int8), gen.transform_tables())
+    torch.cuda.synchronize()
+    assert torch.isnan(sn).all(), "the planting kernel did not stage NaN"
+    say(f"  grouped long route {N}x{K}/M{M} right after NaN in LDS")
+    aq.aq_linear_prefill_grouped(pw, qx, sxg, bd, out=Y, ws=ws)
+    torch.cuda.synchronize()
+    assert_output_close(Y.cpu().numpy(), y_r, c_r, "grouped long route after NaN in LDS")

@@ -98,12 +98,14 @@ def test_transform_out_close(M, N, bias):
     assert_bits_equal(Yd.cpu().numpy(), Y.cpu().numpy(), f"out in place M{M} N{N}")
 
 
-@pytest.mark.parametrize("M,K", [(1, 64), (5, 3072), (33, 1088), (300, 9728), (2, 40768), (256, 2560)])
+@pytest.mark.parametrize("M,K", [(1, 64), (5, 3072), (33, 1088), (255, 4096), (7, 4160), (300, 9728), (2, 40768),
+                                 (256, 2560)])
 def test_quant_act_transformed_bit_exact(M, K):
     """X V and the per-token quantizer in one pass: codes and scales equal the
-    oracle's quantizer applied to the oracle's X V, on both workgroup widths
-    (fewer than 256 rows: 1024 threads; else 256) and the longest row the
-    on-chip staging takes; a zero row keeps the 1e-12 floor."""
+    oracle's quantizer applied to the oracle's X V, on every layout (fewer
+    than 256 rows of at most 64 blocks: lane by element; other rows: the quad
+    layout on 1024 or 256 threads) and the longest row the on-chip staging
+    takes; a zero row keeps the 1e-12 floor."""
     rng = np.random.default_rng(13 * M + K)
     X = gen.acts_outliers(rng, M, K, max(1, K // 100), 30.0)
     X[0, :] = 0.0
