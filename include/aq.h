@@ -222,9 +222,8 @@ int aq_decode_split(const aq_packed *W, int M);
  *   qx    device INT8 [M][K] (from aq_quant_act);  sx device FP32 [M]
  *   bias  device FP32 [N] or NULL
  *   Y     device FP32 [M][N] row-major (written, not accumulated)
- *   split 0 = adaptive (aq_decode_split); otherwise S, which must be one of
- *         Wv, Wv/2, Wv/4 with Wv = 16 when M <= 32 or when the
- *         projection's packed tiles exceed 16 MB, else 8 (other values
+ *   split 0 = adaptive (aq_decode_split); otherwise S, which must be 16, 8
+ *         or 4 (16 waves per workgroup, 1, 2 or 4 row groups; other values
  *         return AQ_ERR_ARG); Z is then the fewest chunks whose
  *         activations fit on chip
  *   ws    device workspace of at least aq_workspace_bytes(W, M, 0, split)
@@ -436,7 +435,7 @@ aq_status aq_linear_prefill_transformed(const aq_packed *W, const int8_t *qx, co
  * column chunks), their sums meet in the workspace as for chunked K, with
  * one arrival counter per tile row and token chunk.  split = 0 takes the
  * adaptive split of aq_linear_decode, except that it keeps a tile row's four
- * row groups in one workgroup (split Wv/4) where each wave's share of the
+ * row groups in one workgroup (split 4) where each wave's share of the
  * row then still fits one batch of weight loads.
  *   useeds   device INT8 [N/64];  tables_host as for the transforms
  *   ws       device workspace of at least

@@ -872,8 +872,8 @@ void launch_mode(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL
     switch (p.MG) {
       case 1: launch_rg<BK, kMfma, 1, 16, kSharedDepth1, kXShared, PARTIALS, INL, GRP, true, XF>(p, R, stream, args); break;
       case 2: launch_rg<BK, kMfma, 2, 16, kSharedDepthN, kXShared, PARTIALS, INL, GRP, true, XF>(p, R, stream, args); break;
-      case 3: launch_rg<BK, kMfma, 3, 8, kSharedDepthN, kXShared, PARTIALS, INL, GRP, true, XF>(p, R, stream, args); break;
-      default: launch_rg<BK, kMfma, 4, 8, kSharedDepthN, kXShared, PARTIALS, INL, GRP, true, XF>(p, R, stream, args); break;
+      case 3: launch_rg<BK, kMfma, 3, 16, kSharedDepthW, kXShared, PARTIALS, INL, GRP, true, XF>(p, R, stream, args); break;
+      default: launch_rg<BK, kMfma, 4, 16, kSharedDepthW, kXShared, PARTIALS, INL, GRP, true, XF>(p, R, stream, args); break;
     }
     return;
   }
@@ -881,8 +881,8 @@ void launch_mode(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL
     switch (p.MG) {
       case 1: launch_rg<BK, kMfma, 1, 16, kSharedDepth1, kXShared, false, INL, GRP, false, XF>(p, R, stream, args); break;
       case 2: launch_rg<BK, kMfma, 2, 16, kSharedDepthN, kXShared, false, INL, GRP, false, XF>(p, R, stream, args); break;
-      case 3: launch_rg<BK, kMfma, 3, 8, kSharedDepthN, kXShared, false, INL, GRP, false, XF>(p, R, stream, args); break;
-      default: launch_rg<BK, kMfma, 4, 8, kSharedDepthN, kXShared, false, INL, GRP, false, XF>(p, R, stream, args); break;
+      case 3: launch_rg<BK, kMfma, 3, 16, kSharedDepthW, kXShared, false, INL, GRP, false, XF>(p, R, stream, args); break;
+      default: launch_rg<BK, kMfma, 4, 16, kSharedDepthW, kXShared, false, INL, GRP, false, XF>(p, R, stream, args); break;
     }
   }
 }

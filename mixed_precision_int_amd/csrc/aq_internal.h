@@ -123,7 +123,8 @@ constexpr int kValuMaxM = 1;            // largest M on the vector-ALU path
 constexpr int kPrivMaxM = 4;            // largest M with per-wave activation slices
 constexpr int kPrivDepth = 8;           // tiles per batch with per-wave activation slices
 constexpr int kSharedDepth1 = 8;        // tiles per batch, shared staging, one token group
-constexpr int kSharedDepthN = 6;        // tiles per batch, shared staging, 2-4 token groups
+constexpr int kSharedDepthN = 6;        // tiles per batch, shared staging, 2 token groups
+constexpr int kSharedDepthW = 4;        // tiles per batch, shared staging, 3-4 token groups
 constexpr int kDecodeCounters = 65536;  // arrival counters at the head of a decode workspace
 constexpr int kInlineWords = 896;       // metadata words that may travel in the kernel arguments
 constexpr int kInlineWordsXf = 768;     // the same with the output-transform tables beside them

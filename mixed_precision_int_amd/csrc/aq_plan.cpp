@@ -19,13 +19,23 @@ bool streams_from_hbm(const PackedView &w) {
 
 // Token groups of 16 per workgroup, waves per workgroup, token chunks.  Up
 // to 64 tokens share one pass over the weights; on projections that stream
-// from HBM, groups of at most 32 tokens (16 waves, one token chunk after
-// another) measure faster at M = 33..128 than 48 or 64 tokens on 8 waves.
+// from HBM, groups of at most 32 tokens (one token chunk after another)
+// measure faster at M = 33..128 than 48 or 64 tokens in one pass (8B-class
+// gate_up at M = 64: 49.5 us in two chunks of 32, 59.9 us in one pass of 64
+// on 16 waves with the columns in two chunks).
 int mgroups(const PackedView &w, int M) {
   const int g = M >= 49 ? 4 : (M + 15) / 16;
   return streams_from_hbm(w) && g > 2 ? 2 : g;
 }
-int waves_of(const PackedView &w, int M) { return mgroups(w, M) <= 2 ? 16 : 8; }
+// 16 waves for every token-group count; 3-4 groups take 4 tiles per batch to
+// stay within 128 registers.  Measured on 8B-class qkv and o (M = 48, 64):
+// 14.7 / 17.6 us and 13.8 / 16.7 us, against 17.8 / 19.7 and 16.9 / 18.8 us
+// with 8 waves and 6 tiles per batch.
+int waves_of(const PackedView &w, int M) {
+  (void)w;
+  (void)M;
+  return 16;
+}
 int mchunks_of(const PackedView &w, int M) {
   const int MG = mgroups(w, M);
   return (M + 16 * MG - 1) / (16 * MG);
@@ -137,7 +147,10 @@ DecodePlan plan_decode(const PackedView &w, int M, int split, bool xform) {
     // rows of 64 (down: 8.6 against 13.7 us).
     if (split == 0 && p.Z == 1 && p.RG < 4) {
       const int s4 = p.waves / 4;
-      const int depth = p.xmode == kXPriv ? kPrivDepth : p.MG == 1 ? kSharedDepth1 : kSharedDepthN;
+      const int depth = p.xmode == kXPriv ? kPrivDepth
+                        : p.MG == 1       ? kSharedDepth1
+                        : p.MG == 2       ? kSharedDepthN
+                                          : kSharedDepthW;
       if ((w.C + s4 - 1) / s4 <= depth) {
         p.RG = 4;
         p.S = s4;

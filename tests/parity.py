@@ -142,7 +142,7 @@ class Case:
             bad = np.argwhere(Pg != ref["P_rows"])
             assert bad.size == 0, f"{self.name}/{ph}: {len(bad)} partials differ, first {bad[:4].tolist()}"
             if ph == "decode":
-                Wv = 16 if len(rows) <= 32 else 8
+                Wv = 16  # waves per decode workgroup
                 ok = {0, Wv, Wv // 2, Wv // 4}
                 for s in sorted({s for s in splits if s in ok} | {0}):
                     Y = aq.aq_linear_decode(pw, qx_rows, sx_rows, bias_d, split=s)

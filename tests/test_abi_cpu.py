@@ -162,7 +162,7 @@ def test_decode_chunk_workspace(aqlib):
         assert decode(big, M=M, split=0) == -6
         assert decode(big, M=M, split=0, ws=FAKE, ws_bytes=need - 1) == -6
         assert decode(big, M=M, split=0, ws=FAKE + 4, ws_bytes=need) == -5
-        for sp in ((16, 8, 4) if M <= 32 else (8, 4, 2)):
+        for sp in (16, 8, 4):
             assert ws(ctypes.byref(big), M, 0, sp) > 0
     # one token, or few tokens: per-wave activation slices, no chunks
     for M in (1, 4):

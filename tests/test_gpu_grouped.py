@@ -63,7 +63,7 @@ def run_case(N, K, bK, M, kind="mixed", bias=False, seed=0, splits=(0,), phases=
 def test_grouped_token_counts(M):
     """b_M = 1 for one token (the vector-ALU path), 16 otherwise, with
     ragged last groups; every decode split the kernel offers."""
-    Wv = 16 if M <= 32 else 8
+    Wv = 16  # waves per decode workgroup
     run_case(256, 1024, 128, M, splits=(0, Wv, Wv // 2, Wv // 4), bias=(M % 2 == 1))
 
 

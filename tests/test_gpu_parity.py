@@ -228,7 +228,7 @@ def test_decode_chunked_columns(N, K, bK, M, kind):
     X = gen.acts_outliers(rng, M, K, 5, 25.0)
     bias = rng.standard_normal(N).astype(np.float32)
     c = Case(W, z, X, 64, bK, bias=bias, name=f"chunked{N}x{K}/bK{bK}/M{M}/{kind}")
-    Wv = 16 if M <= 32 else 8
+    Wv = 16  # waves per decode workgroup
     out = c.check_all(phases=("decode",), splits=(0, Wv, Wv // 2, Wv // 4))
     assert aq.aq_workspace_bytes(c.pw, M, aq.AQ_PHASE_DECODE) > 0
     bias_d = to_dev(bias)

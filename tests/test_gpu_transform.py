@@ -335,7 +335,7 @@ def test_decode_transformed_bit_exact(name, N, K, M):
     adaptive split or 4 waves per row group (the tile row in one workgroup),
     and matches that call bit for bit."""
     pw, qx, sx, us, b = _decode_xf_setup(name, N, K, M, N + K + M)
-    Wv = 16 if M <= 32 else 8
+    Wv = 16  # waves per decode workgroup
     for bias in (b, None):
         refs = {}
         for split in (Wv, Wv // 2, Wv // 4):
@@ -385,11 +385,11 @@ def test_decode_transformed_calls_in_a_row():
     transformed and plain decode calls of different sizes on one workspace,
     one after another, each equal to its reference."""
     pw, qx, sx, us, b = _decode_xf_setup("o", 3072, 3072, 64, 11)
-    need = max(aq.aq_workspace_bytes(pw, M, ph, 16 if M <= 32 else 8) for M in (1, 16, 64)
+    need = max(aq.aq_workspace_bytes(pw, M, ph, 16) for M in (1, 16, 64)
                for ph in (aq.AQ_PHASE_DECODE, aq.AQ_PHASE_DECODE_TRANSFORMED))
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for M in (16, 1, 64, 16):
-        sp = 16 if M <= 32 else 8  # one row group per workgroup: every tile row handed over
+        sp = 16  # one row group per workgroup: every tile row handed over
         say(f"  decode_transformed in a row: M={M} split={sp}")
         Yt = aq.aq_linear_decode(pw, qx[:M], sx[:M], split=sp, ws=ws)
         ref = aq.aq_transform_out(Yt, us, TABLES, bias=b)
