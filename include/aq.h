@@ -413,7 +413,8 @@ aq_status aq_transform_out(const float *Yt, int M, int N, const int8_t *useeds,
  * eq. 19): Y = Y~ U + bias, Y~ the
  * aq_linear_prefill product of the transformed operands (W~ packed, qx / sx
  * from aq_quant_act_transformed).  Long prompts (the long-prompt route of
- * aq_linear_prefill) apply U in the GEMM's epilogue, where each wave holds
+ * aq_linear_prefill, on the GEMM kernel its plain call takes) apply U in the
+ * GEMM's epilogue, where each wave holds
  * the 64 outputs of a tile row per token, before the token scale and the
  * bias; shorter prompts run the linear and then aq_transform_out.  Within
  * FP32 rounding of aq_linear_prefill followed by aq_transform_out.

@@ -571,14 +571,16 @@ aq_status aq_linear_prefill_transformed(const aq_packed *W, const int8_t *qx, co
   if (st != AQ_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (aq::prefill_long(v, M)) {
-    // the long-prompt GEMM applies U in its epilogue
+    // the long-prompt GEMMs apply U in their epilogue
     const int8_t *E = v.w8;
     const float *Es = v.s8;
     if (v.T4 > 0 && aq::launch_expand(v, ws, s, &E, &Es) != hipSuccess) return AQ_ERR_HIP;
-    return aq::launch_prefill_dense(E, Es, v.N, v.K, v.bK, qx, sx, M, bias, Y, nullptr, s, useeds,
-                                    tables_host) == hipSuccess
-               ? AQ_OK
-               : AQ_ERR_HIP;
+    const hipError_t e = aq::prefill_big_fits(v.N, v.K, v.bK, M)
+                             ? aq::launch_prefill_big(E, Es, v.N, v.K, qx, sx, M, bias, Y, nullptr, s, useeds,
+                                                      tables_host)
+                             : aq::launch_prefill_dense(E, Es, v.N, v.K, v.bK, qx, sx, M, bias, Y, nullptr, s,
+                                                        useeds, tables_host);
+    return e == hipSuccess ? AQ_OK : AQ_ERR_HIP;
   }
   // short prompts: the linear, then the output transform, which adds the bias
   if (aq::launch_prefill(v, qx, sx, M, nullptr, Y, nullptr, s) != hipSuccess) return AQ_ERR_HIP;

@@ -30,6 +30,7 @@
 
 #include "aq_device.h"
 #include "aq_internal.h"
+#include "aq_tile_xform.h"
 
 namespace aq {
 namespace {
@@ -42,6 +43,8 @@ struct BigArgs {
   float *Y;
   int32_t *P;
   int N, K, R, C, M, MB, NB, T;
+  const int8_t *useeds;  // output transform (XFORM): per tile row seed (-1 .. 6)
+  OutTables ot;
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -81,8 +84,9 @@ __device__ __forceinline__ void tile_coords(const BigArgs &a, int t, int G, int 
   bn = (L % in_group) / gsize;
 }
 
-template <bool PARTIALS>
+template <bool PARTIALS, bool XFORM>
 __global__ __launch_bounds__(512, 1) void prefill_big_kernel(const BigArgs a) {
+  static_assert(!(PARTIALS && XFORM), "the debug products take no output transform");
   constexpr int A_BYTES = kBM * kBK, B_BYTES = kBN * kBK;
   __shared__ __attribute__((aligned(1024))) int8_t As0[A_BYTES];
   __shared__ __attribute__((aligned(1024))) int8_t As1[A_BYTES];
@@ -232,11 +236,18 @@ __global__ __launch_bounds__(512, 1) void prefill_big_kernel(const BigArgs a) {
   acc[0] = acc[1] = v16i{0};
   float scp0 = 0.f, scp1 = 0.f, scn0 = 0.f, scn1 = 0.f;
 
-  // the finished tile ti's outputs: Y = F * sx + bias, then F = 0
+  // the finished tile ti's outputs: Y = F * sx + bias (XFORM: Y~ U on the
+  // wave's tile row first, one 32-token slice at a time to bound the
+  // registers of the exchange), then F = 0
   auto epilogue = [&](int ti) __attribute__((always_inline)) {
     int bm, bn;
     tile_coords(a, (int)blockIdx.x + ti * G, G, bm, bn);
     const int m0 = bm * kBM, r0 = bn * 4;
+    if constexpr (XFORM) {
+      const int s = a.useeds[min(r0 + wn, a.R - 1)];
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm) out_transform<1>(*reinterpret_cast<float(*)[1][2][16]>(&F[fm]), s, lane, a.ot);
+    }
     const float *xs = xs_buf(ti) + wm * 128 + 4 * h;
     const float *bb = bb_buf(ti) + wn * 64 + l32;
     const float b0 = a.bias ? bb[0] : 0.f, b1 = a.bias ? bb[32] : 0.f;
@@ -394,18 +405,22 @@ __global__ __launch_bounds__(512, 1) void prefill_big_kernel(const BigArgs a) {
 
 hipError_t launch_prefill_big(const int8_t *E, const float *Es, int N, int K, const int8_t *qx,
                               const float *sx, int M, const float *bias, float *Y, int32_t *P,
-                              hipStream_t stream) {
+                              hipStream_t stream, const int8_t *useeds, const aq_transform_tables *tables) {
   BigArgs a;
   a.qx = qx; a.E = E; a.Es = Es; a.sx = sx; a.bias = bias; a.Y = Y; a.P = P;
+  a.useeds = useeds;
+  a.ot = useeds && tables ? out_tables(*tables) : OutTables{};
   a.N = N; a.K = K; a.R = N / 64; a.C = K / kBK; a.M = M;
   a.MB = (M + kBM - 1) / kBM;
   a.NB = (a.R + 3) / 4;
   a.T = a.MB * a.NB;
   const int G = min(a.T, compute_units());
   if (P)
-    hipLaunchKernelGGL(prefill_big_kernel<true>, dim3(G), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((prefill_big_kernel<true, false>), dim3(G), dim3(512), 0, stream, a);
+  else if (useeds && tables)
+    hipLaunchKernelGGL((prefill_big_kernel<false, true>), dim3(G), dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL(prefill_big_kernel<false>, dim3(G), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((prefill_big_kernel<false, false>), dim3(G), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

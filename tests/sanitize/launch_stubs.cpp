@@ -40,7 +40,8 @@ hipError_t launch_prefill_dense_grouped(const int8_t *, const float *, int, int,
   return launched();
 }
 hipError_t launch_prefill_big(const int8_t *, const float *, int, int, const int8_t *, const float *, int,
-                              const float *, float *, int32_t *, hipStream_t) {
+                              const float *, float *, int32_t *, hipStream_t, const int8_t *,
+                              const aq_transform_tables *) {
   return launched();
 }
 hipError_t launch_expand(const PackedView &w, void *ws, hipStream_t, const int8_t **E, const float **Es) {
