@@ -412,12 +412,11 @@ aq_status aq_transform_out(const float *Yt, int M, int N, const int8_t *useeds,
 /* The transformed layer's prefill linear (App. B.1 eq. 4 around App. E.3
  * eq. 19): Y = Y~ U + bias, Y~ the
  * aq_linear_prefill product of the transformed operands (W~ packed, qx / sx
- * from aq_quant_act_transformed).  Long prompts (the long-prompt route of
- * aq_linear_prefill, on the GEMM kernel its plain call takes) apply U in the
- * GEMM's epilogue, where each wave holds
- * the 64 outputs of a tile row per token, before the token scale and the
- * bias; shorter prompts run the linear and then aq_transform_out.  Within
- * FP32 rounding of aq_linear_prefill followed by aq_transform_out.
+ * from aq_quant_act_transformed).  Every route of aq_linear_prefill (the
+ * short-prompt GEMM, and for long prompts the GEMM kernel the plain call
+ * takes) applies U in its epilogue, where each wave holds the 64 outputs of
+ * a tile row per token, before the token scale and the bias.  Within FP32
+ * rounding of aq_linear_prefill followed by aq_transform_out.
  *   useeds   device INT8 [N/64];  tables_host as for the transforms
  * Other arguments, workspace and errors as aq_linear_prefill. */
 aq_status aq_linear_prefill_transformed(const aq_packed *W, const int8_t *qx, const float *sx, int M,

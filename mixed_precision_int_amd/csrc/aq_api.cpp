@@ -582,12 +582,9 @@ aq_status aq_linear_prefill_transformed(const aq_packed *W, const int8_t *qx, co
                                                         useeds, tables_host);
     return e == hipSuccess ? AQ_OK : AQ_ERR_HIP;
   }
-  // short prompts: the linear, then the output transform, which adds the bias
-  if (aq::launch_prefill(v, qx, sx, M, nullptr, Y, nullptr, s) != hipSuccess) return AQ_ERR_HIP;
-  return aq::launch_transform(aq::kTransformOut, Y, Y, M, v.N, useeds, nullptr, bias, *tables_host, s) ==
-                 hipSuccess
-             ? AQ_OK
-             : AQ_ERR_HIP;
+  // short prompts: the 32 x 32 MFMA GEMM, U in its epilogue too
+  return aq::launch_prefill(v, qx, sx, M, bias, Y, nullptr, s, useeds, tables_host) == hipSuccess ? AQ_OK
+                                                                                                 : AQ_ERR_HIP;
 }
 
 }  // extern "C"

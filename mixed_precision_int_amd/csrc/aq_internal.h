@@ -60,8 +60,12 @@ constexpr int kActGroupK = 64;
 inline int act_group_rows(int M) { return M == 1 ? 1 : 16; }
 hipError_t launch_quant_act_grouped(const float *X, int M, int K, int8_t *qx, float *sxg,
                                     hipStream_t stream);
+// Short prompts: the 32 x 32 MFMA GEMM over the packed tiles; useeds and
+// tables (both or neither) apply the output transform in its epilogue, as
+// for launch_prefill_dense.
 hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx, int M,
-                          const float *bias, float *Y, int32_t *P, hipStream_t stream);
+                          const float *bias, float *Y, int32_t *P, hipStream_t stream,
+                          const int8_t *useeds = nullptr, const aq_transform_tables *tables = nullptr);
 
 // Long-prefill GEMM over INT8 tiles in logical tile order: E holds tile
 // (r, j) at (r*C + j) * 64*bK bytes (b_K/16 panels of [64][16]) and Es its

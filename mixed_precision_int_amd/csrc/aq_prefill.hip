@@ -26,6 +26,7 @@
 
 #include "aq_device.h"
 #include "aq_internal.h"
+#include "aq_tile_xform.h"
 
 namespace aq {
 namespace {
@@ -41,12 +42,15 @@ struct PrefillArgs {
   float *Y;
   int32_t *P;
   int N, K, R, C, T4, T8, M, MB, NB, label_words;
+  const int8_t *useeds;  // output transform (XFORM): per tile row seed (-1 .. 6)
+  OutTables ot;
 };
 
 __device__ __forceinline__ v4i ld16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
 
-template <int BK, int WM, int WN, bool PARTIALS>
+template <int BK, int WM, int WN, bool PARTIALS, bool XFORM>
 __global__ __launch_bounds__(64 * WM * WN, 8 / (WM * WN)) void prefill_kernel(const PrefillArgs a) {
+  static_assert(!(PARTIALS && XFORM), "the debug products take no output transform");
   constexpr int NT = 64 * WM * WN;            // threads
   constexpr int BM = 64 * WM, BN = 64 * WN;   // block tile
   constexpr int NP = BK / 16;                 // 16-byte chunks per row of a tile column
@@ -291,6 +295,9 @@ _Pragma("unroll") \
 
   if constexpr (!PARTIALS) {
     if (!wave_live) return;
+    // XFORM: Y = Y~ U on this wave's tile row (a token's 64 outputs sit in
+    // one half-wave), before the token scale and the bias
+    if constexpr (XFORM) out_transform<2>(F, a.useeds[rw], lane, a.ot);
 #pragma unroll
     for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
@@ -314,17 +321,22 @@ void launch_cfg(bool partials, hipStream_t stream, const PrefillArgs &args) {
   const dim3 grid(args.MB * args.NB);
   const dim3 block(64 * WM * WN);
   if (partials)
-    hipLaunchKernelGGL((prefill_kernel<BK, WM, WN, true>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<BK, WM, WN, true, false>), grid, block, 0, stream, args);
+  else if (args.useeds)
+    hipLaunchKernelGGL((prefill_kernel<BK, WM, WN, false, true>), grid, block, 0, stream, args);
   else
-    hipLaunchKernelGGL((prefill_kernel<BK, WM, WN, false>), grid, block, 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<BK, WM, WN, false, false>), grid, block, 0, stream, args);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PackedView &w, const int8_t *qx, const float *sx, int M,
-                          const float *bias, float *Y, int32_t *P, hipStream_t stream) {
+                          const float *bias, float *Y, int32_t *P, hipStream_t stream,
+                          const int8_t *useeds, const aq_transform_tables *tables) {
   constexpr int WM = 2, WN = 2;
   PrefillArgs args;
+  args.useeds = useeds && tables && !P ? useeds : nullptr;
+  args.ot = args.useeds ? out_tables(*tables) : OutTables{};
   args.labels = w.labels; args.off4 = w.off4; args.off8 = w.off8;
   args.w4 = w.w4; args.w8 = w.w8; args.s4 = w.s4; args.s8 = w.s8;
   args.qx = qx; args.sx = sx; args.bias = bias; args.Y = Y; args.P = P;

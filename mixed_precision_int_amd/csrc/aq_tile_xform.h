@@ -3,7 +3,8 @@
 // on their 32 x 32 MFMA accumulator layout: one token's 64 outputs of a
 // tile row sit in one half-wave, output 32 fn + l32 in register fn of lane
 // l32, so a wave that owns one tile row transforms every token it holds at
-// once.  Shared by the 256 x 128 and the persistent 256 x 256 kernels.
+// once.  Shared by the short-prompt, the 256 x 128 and the persistent
+// 256 x 256 kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>

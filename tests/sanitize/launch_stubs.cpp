@@ -27,7 +27,7 @@ hipError_t launch_decode(const PackedView &, const int8_t *, const float *, int,
 }
 hipError_t launch_quant_act_grouped(const float *, int, int, int8_t *, float *, hipStream_t) { return launched(); }
 hipError_t launch_prefill(const PackedView &, const int8_t *, const float *, int, const float *, float *,
-                          int32_t *, hipStream_t) {
+                          int32_t *, hipStream_t, const int8_t *, const aq_transform_tables *) {
   return launched();
 }
 hipError_t launch_prefill_dense(const int8_t *, const float *, int, int, int, const int8_t *, const float *, int,
