@@ -258,7 +258,9 @@ aq_status aq_linear_decode_noalloc(const aq_packed *W, const int8_t *qx, const f
 /* Compute-bound phase (Sec. 3.3 "Prefill weight reuse"; App. E.3): the same
  * Y as aq_linear_decode, computed with INT8 matrix-core (MFMA) tiles that
  * reuse each weight tile across many activation rows.  Short prompts
- * (M < 1024) widen the mixed tiles on chip.  Long prompts (M >= 1024, with
+ * (M < 1024) widen the mixed tiles on chip; up to 64 rows they run on the
+ * decode kernels where those need no workspace (their GEMM would have one
+ * block row).  Long prompts (M >= 1024, with
  * M*K and N*K below 2^31) first prepare the selected weights as INT8 tiles
  * in logical tile order, once per call, in the workspace (App. E.3
  * Prefill), then run the GEMM over them; a projection without INT4 tiles

@@ -68,7 +68,10 @@ aq_status check_workspace(void *ws, size_t ws_bytes, size_t need) {
 hipError_t run_prefill(const aq::PackedView &v, const int8_t *qx, const float *sx, int M,
                        const float *bias, float *Y, int32_t *P, void *ws, hipStream_t s,
                        bool prepared = false) {
-  if (!aq::prefill_long(v, M)) return aq::launch_prefill(v, qx, sx, M, bias, Y, P, s);
+  if (!aq::prefill_long(v, M)) {
+    if (aq::prefill_on_decode(v, M)) return aq::launch_decode(v, qx, sx, M, bias, Y, 0, nullptr, P, s);
+    return aq::launch_prefill(v, qx, sx, M, bias, Y, P, s);
+  }
   const int8_t *E = v.w8;
   const float *Es = v.s8;
   if (v.T4 > 0 && prepared) {
@@ -582,9 +585,13 @@ aq_status aq_linear_prefill_transformed(const aq_packed *W, const int8_t *qx, co
                                                         useeds, tables_host);
     return e == hipSuccess ? AQ_OK : AQ_ERR_HIP;
   }
-  // short prompts: the 32 x 32 MFMA GEMM, U in its epilogue too
-  return aq::launch_prefill(v, qx, sx, M, bias, Y, nullptr, s, useeds, tables_host) == hipSuccess ? AQ_OK
-                                                                                                 : AQ_ERR_HIP;
+  // short prompts: the decode kernels or the 32 x 32 MFMA GEMM, U in the
+  // epilogue of either
+  const hipError_t e =
+      aq::prefill_on_decode(v, M, true)
+          ? aq::launch_decode_transformed(v, qx, sx, M, bias, Y, 0, nullptr, useeds, *tables_host, s)
+          : aq::launch_prefill(v, qx, sx, M, bias, Y, nullptr, s, useeds, tables_host);
+  return e == hipSuccess ? AQ_OK : AQ_ERR_HIP;
 }
 
 }  // extern "C"

@@ -115,6 +115,12 @@ inline bool prefill_long(const PackedView &w, int M) {
   return M >= kLongPrefillM && (long long)M * w.K < (1LL << 31) &&
          (long long)w.N * w.K < (1LL << 31);
 }
+// Prompts of at most kPrefillDecodeMaxM rows run on the decode kernels when
+// their decode plan needs no workspace (prefill workspaces carry no
+// counters): the short-prompt GEMM has one 128-token block row there, too
+// few blocks to fill the chip.  xform: the plan of the transformed decode.
+constexpr int kPrefillDecodeMaxM = 64;
+bool prefill_on_decode(const PackedView &w, int M, bool xform = false);
 // Grouped activations (App. B.3) take the long-prompt GEMM for long prompts
 // at b_K = 128; otherwise the decode kernels.
 inline bool prefill_grouped_long(const PackedView &w, int M) { return w.bK == 128 && prefill_long(w, M); }

@@ -188,6 +188,12 @@ size_t decode_workspace_bytes(const PackedView &w, int M, int split, bool xform)
   return plan_decode(w, M, split, xform).ws_bytes;
 }
 
+bool prefill_on_decode(const PackedView &w, int M, bool xform) {
+  if (M > kPrefillDecodeMaxM) return false;
+  const DecodePlan p = plan_decode(w, M, 0, xform);
+  return p.ws_bytes == 0 && decode_plan_ok(p, w, xform);
+}
+
 size_t expand_bytes(const PackedView &w) {
   const size_t e = (size_t)w.N * w.K;               // INT8 tiles
   const size_t s = (size_t)w.R * w.C * 64 * 4;      // FP32 scales
