@@ -100,8 +100,8 @@ struct XfTables {
   uint64_t dlm[kTransformSeeds], drm[kTransformSeeds];
 };
 constexpr int kXfWords = sizeof(XfTables) / 4;
-// one word per thread of the smallest workgroup (8 waves), 512 bytes of LDS
-static_assert(sizeof(XfTables) % 4 == 0 && kXfWords <= 512 && sizeof(XfTables) <= 512, "transform tables");
+// staged in 512 bytes of LDS, one word per thread
+static_assert(sizeof(XfTables) % 4 == 0 && sizeof(XfTables) <= 512, "transform tables");
 struct XfArgs {
   const int8_t *useeds;
   XfTables xt;
@@ -246,6 +246,7 @@ template <int BK, int MODE, int MG, int WAVES, int RG, int DEPTH, int XMODE, boo
           bool GRP, bool WNT, bool XF>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF> a) {
   static_assert(!XF || (MODE == kMfma && !PARTIALS && !GRP), "output transform: per-token MFMA route");
+  static_assert(!XF || WAVES * 64 >= kXfWords, "one transform-table word per thread");
   constexpr int KS = BK / 64;    // MFMA steps (16-byte operands per lane) per tile
   constexpr int S = WAVES / RG;  // splits per row group
   constexpr int NT = WAVES * 64;
