@@ -200,7 +200,12 @@ aq_status aq_quant_act(const float *X, int M, int K, int8_t *qx, float *sx, void
  *   holds INT4 tiles: the temporary INT8 operand of App. E.3 (Prefill), N*K
  *   bytes of INT8 tiles in logical tile order, rounded up to 256, plus
  *   4*N*(K/bK) bytes of scales; its contents need no initialization and are
- *   overwritten by every call that uses it. */
+ *   overwritten by every call that uses it.  A prompt on the decode
+ *   kernels (at most 64 rows, or 128 on narrow projections) needs the
+ *   decode workspace of the
+ *   adaptive split when that plan hands sums over (the larger of the plain
+ *   and the transformed plan); the call zeroes its counters itself, so here
+ *   too the contents need no initialization. */
 size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split);
 
 /* Split count that aq_linear_decode uses for `split` = 0: the number of
@@ -258,9 +263,10 @@ aq_status aq_linear_decode_noalloc(const aq_packed *W, const int8_t *qx, const f
 /* Compute-bound phase (Sec. 3.3 "Prefill weight reuse"; App. E.3): the same
  * Y as aq_linear_decode, computed with INT8 matrix-core (MFMA) tiles that
  * reuse each weight tile across many activation rows.  Short prompts
- * (M < 1024) widen the mixed tiles on chip; up to 64 rows they run on the
- * decode kernels where those need no workspace (their GEMM would have one
- * block row).  Long prompts (M >= 1024, with
+ * (M < 1024) widen the mixed tiles on chip; up to 64 rows (128 on
+ * projections whose GEMM grid would not fill half of the compute units)
+ * they run on the decode kernels.  Long prompts
+ * (M >= 1024, with
  * M*K and N*K below 2^31) first prepare the selected weights as INT8 tiles
  * in logical tile order, once per call, in the workspace (App. E.3
  * Prefill), then run the GEMM over them; a projection without INT4 tiles

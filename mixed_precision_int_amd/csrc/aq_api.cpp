@@ -69,7 +69,17 @@ hipError_t run_prefill(const aq::PackedView &v, const int8_t *qx, const float *s
                        const float *bias, float *Y, int32_t *P, void *ws, hipStream_t s,
                        bool prepared = false) {
   if (!aq::prefill_long(v, M)) {
-    if (aq::prefill_on_decode(v, M)) return aq::launch_decode(v, qx, sx, M, bias, Y, 0, nullptr, P, s);
+    if (aq::prefill_on_decode(v, M)) {
+      // the products need no hand-over; a prepared workspace holds the
+      // operand and is not the decode kernels' to use
+      const size_t need = P ? 0 : aq::decode_workspace_bytes(v, M, 0);
+      if (need == 0) return aq::launch_decode(v, qx, sx, M, bias, Y, 0, nullptr, P, s);
+      if (!prepared) {
+        const hipError_t e = aq::launch_zero_counters(ws, s);
+        if (e != hipSuccess) return e;
+        return aq::launch_decode(v, qx, sx, M, bias, Y, 0, ws, nullptr, s);
+      }
+    }
     return aq::launch_prefill(v, qx, sx, M, bias, Y, P, s);
   }
   const int8_t *E = v.w8;
@@ -274,7 +284,7 @@ int aq_decode_split(const aq_packed *W, int M) {
 size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split) {
   if (check_packed(W) != AQ_OK || M <= 0) return 0;
   const aq::PackedView v = aq::view_of(*W);
-  if (phase == AQ_PHASE_PREFILL) return aq::prefill_workspace_bytes(v, M);
+  if (phase == AQ_PHASE_PREFILL) return aq::prefill_call_workspace_bytes(v, M);
   if (phase == AQ_PHASE_PREFILL_GROUPED)
     return aq::prefill_grouped_long(v, M) ? aq::prefill_workspace_bytes(v, M) : aq::decode_workspace_bytes(v, M, 0);
   if (phase != AQ_PHASE_DECODE && phase != AQ_PHASE_DECODE_TRANSFORMED) return 0;
@@ -386,7 +396,7 @@ aq_status aq_linear_prefill(const aq_packed *W, const int8_t *qx, const float *s
   st = check_linear_io(W, qx, sx, M, bias, Y);
   if (st != AQ_OK || M == 0) return st;
   const aq::PackedView v = aq::view_of(*W);
-  st = check_workspace(ws, ws_bytes, aq::prefill_workspace_bytes(v, M));
+  st = check_workspace(ws, ws_bytes, aq::prefill_call_workspace_bytes(v, M));
   if (st != AQ_OK) return st;
   return run_prefill(v, qx, sx, M, bias, Y, nullptr, ws, static_cast<hipStream_t>(stream)) ==
                  hipSuccess
@@ -570,7 +580,7 @@ aq_status aq_linear_prefill_transformed(const aq_packed *W, const int8_t *qx, co
   st = check_tables(tables_host);
   if (st != AQ_OK) return st;
   const aq::PackedView v = aq::view_of(*W);
-  st = check_workspace(ws, ws_bytes, aq::prefill_workspace_bytes(v, M));
+  st = check_workspace(ws, ws_bytes, aq::prefill_call_workspace_bytes(v, M));
   if (st != AQ_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (aq::prefill_long(v, M)) {
@@ -587,11 +597,16 @@ aq_status aq_linear_prefill_transformed(const aq_packed *W, const int8_t *qx, co
   }
   // short prompts: the decode kernels or the 32 x 32 MFMA GEMM, U in the
   // epilogue of either
-  const hipError_t e =
-      aq::prefill_on_decode(v, M, true)
-          ? aq::launch_decode_transformed(v, qx, sx, M, bias, Y, 0, nullptr, useeds, *tables_host, s)
-          : aq::launch_prefill(v, qx, sx, M, bias, Y, nullptr, s, useeds, tables_host);
-  return e == hipSuccess ? AQ_OK : AQ_ERR_HIP;
+  if (aq::prefill_on_decode(v, M, true)) {
+    const bool handover = aq::decode_workspace_bytes(v, M, 0, true) > 0;
+    if (handover && aq::launch_zero_counters(ws, s) != hipSuccess) return AQ_ERR_HIP;
+    return aq::launch_decode_transformed(v, qx, sx, M, bias, Y, 0, handover ? ws : nullptr, useeds,
+                                         *tables_host, s) == hipSuccess
+               ? AQ_OK
+               : AQ_ERR_HIP;
+  }
+  return aq::launch_prefill(v, qx, sx, M, bias, Y, nullptr, s, useeds, tables_host) == hipSuccess ? AQ_OK
+                                                                                                 : AQ_ERR_HIP;
 }
 
 }  // extern "C"

@@ -918,6 +918,12 @@ __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *__restrict__ 
 
 }  // namespace
 
+hipError_t launch_zero_counters(void *ws, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream, static_cast<uint32_t *>(ws),
+                     kDecodeCounters);
+  return hipGetLastError();
+}
+
 hipError_t decode_scratch(hipStream_t stream, void **out) {
   constexpr int kMaxDevices = 64;
   static std::mutex mu;

@@ -115,12 +115,24 @@ inline bool prefill_long(const PackedView &w, int M) {
   return M >= kLongPrefillM && (long long)M * w.K < (1LL << 31) &&
          (long long)w.N * w.K < (1LL << 31);
 }
-// Prompts of at most kPrefillDecodeMaxM rows run on the decode kernels when
-// their decode plan needs no workspace (prefill workspaces carry no
-// counters): the short-prompt GEMM has one 128-token block row there, too
-// few blocks to fill the chip.  xform: the plan of the transformed decode.
+// Prompts of at most kPrefillDecodeMaxM rows run on the decode kernels: the
+// short-prompt GEMM has one 128-token block row there, too few blocks to
+// fill the chip.  A decode plan that hands sums over gets its workspace from
+// the prefill call, whose arrival counters the call zeroes first (prefill
+// workspaces need no initialization).  xform: the plan of the transformed
+// decode.
 constexpr int kPrefillDecodeMaxM = 64;
+// ... and up to kPrefillDecodeNarrowM rows on projections whose GEMM grid
+// (one block per 128 tokens x 2 tile rows) would not reach half of the CUs
+constexpr int kPrefillDecodeNarrowM = 128;
 bool prefill_on_decode(const PackedView &w, int M, bool xform = false);
+// Workspace of a prefill call (aq_linear_prefill, its transformed variant):
+// the temporary operand of long prompts, or the decode kernels' workspace of
+// short prompts on them (the larger of the plain and transformed plans).
+size_t prefill_call_workspace_bytes(const PackedView &w, int M);
+// Zeroes the arrival counters at the head of a decode workspace (a fill
+// kernel, so that it can be captured into a graph).
+hipError_t launch_zero_counters(void *ws, hipStream_t stream);
 // Grouped activations (App. B.3) take the long-prompt GEMM for long prompts
 // at b_K = 128; otherwise the decode kernels.
 inline bool prefill_grouped_long(const PackedView &w, int M) { return w.bK == 128 && prefill_long(w, M); }

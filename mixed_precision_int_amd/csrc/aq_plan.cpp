@@ -188,10 +188,24 @@ size_t decode_workspace_bytes(const PackedView &w, int M, int split, bool xform)
   return plan_decode(w, M, split, xform).ws_bytes;
 }
 
+// Measured on the 8B-class shapes at M = 96 / 128: qkv 26.4 / 29.5 us on the
+// decode kernels against 41.9 / 42.0 us on the GEMM (48 blocks), o 16.8 /
+// 18.7 against 41.5 / 41.7, down 47.6 / 50.9 against 125.9 / 126.2; gate_up
+// (224 blocks) 72.3 / 88.4 against 46.7 / 47.0 stays on the GEMM.
 bool prefill_on_decode(const PackedView &w, int M, bool xform) {
-  if (M > kPrefillDecodeMaxM) return false;
-  const DecodePlan p = plan_decode(w, M, 0, xform);
-  return p.ws_bytes == 0 && decode_plan_ok(p, w, xform);
+  const bool narrow = M <= kPrefillDecodeNarrowM && 2 * ((w.R + 1) / 2) < compute_units();
+  return (M <= kPrefillDecodeMaxM || narrow) && decode_plan_ok(plan_decode(w, M, 0, xform), w, xform);
+}
+
+size_t prefill_call_workspace_bytes(const PackedView &w, int M) {
+  if (prefill_long(w, M)) return prefill_workspace_bytes(w, M);
+  size_t need = 0;
+  if (prefill_on_decode(w, M, false)) need = plan_decode(w, M, 0, false).ws_bytes;
+  if (prefill_on_decode(w, M, true)) {
+    const size_t x = plan_decode(w, M, 0, true).ws_bytes;
+    if (x > need) need = x;
+  }
+  return need;
 }
 
 size_t expand_bytes(const PackedView &w) {

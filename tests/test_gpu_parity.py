@@ -344,3 +344,30 @@ def test_long_prefill_persistent_tiles_ragged():
     X = gen.acts_heavy_tail(rng, M, K)
     bias = rng.standard_normal(N).astype(np.float32)
     Case(W, z, X, 64, 128, bias=bias, name="persistent16448x256/M1040").check_all(phases=("prefill",))
+
+
+@pytest.mark.parametrize("N,K,M", [(256, 8192, 64), (192, 5120, 37), (1024, 14336, 24), (256, 8192, 100)])
+def test_short_prefill_on_decode_with_handover(N, K, M):
+    """A prompt of at most 64 rows (128 on a projection too narrow for the
+    GEMM grid, 256 x 8192 at M = 100) runs on the decode kernels; where their
+    plan cuts the columns into chunks, the prefill call's workspace (handed
+    in uninitialized: filled with 0xFF here) serves as the decode workspace
+    after the call zeroes its counters.  Outputs against the oracle, the same
+    bits as the decode call, twice in a row on the same dirty workspace."""
+    rng = np.random.default_rng(7 * N + K + M)
+    W = gen.weights(rng, N, K)
+    z = gen.map_uniform(rng, N // 64, K // 128, 0.3)
+    X = gen.acts_outliers(rng, M, K, 5, 25.0)
+    bias = rng.standard_normal(N).astype(np.float32)
+    c = Case(W, z, X, 64, 128, bias=bias, name=f"shortprefill{N}x{K}/M{M}")
+    c.check_all(phases=("prefill",))
+    need = aq.aq_workspace_bytes(c.pw, M, aq.AQ_PHASE_PREFILL)
+    assert need >= aq.aq_workspace_bytes(c.pw, M, aq.AQ_PHASE_DECODE) > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    bias_d = to_dev(bias)
+    ref = aq.aq_linear_decode(c.pw, c.qx_d, c.sx_d, bias_d)
+    for _ in range(2):
+        Y = aq.aq_linear_prefill(c.pw, c.qx_d, c.sx_d, bias_d, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int32), ref.view(torch.int32))
+        ws.fill_(0xFF)

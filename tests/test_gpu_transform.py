@@ -229,12 +229,15 @@ def test_transforms_full_prefill_size_sampled(proj):
 @pytest.mark.parametrize("N,K,bK,M,bias", [(256, 1024, 128, 1030, True), (320, 2560, 128, 2048, False),
                                            (256, 640, 64, 1040, True), (192, 768, 128, 100, True),
                                            (256, 640, 64, 300, False), (6144, 2560, 128, 2048, True),
-                                           (8192, 1024, 128, 1040, True)])
+                                           (8192, 1024, 128, 1040, True), (3072, 8192, 128, 40, True),
+                                           (512, 3072, 128, 9, False)])
 def test_prefill_transformed(N, K, bK, M, bias):
     """Y = Y~ U + bias with U applied inside the GEMMs' epilogue (M >= 1024:
     the 256 x 128 kernel, or the persistent 256 x 256 one for the wide
     shapes, 6144 x 2560 and 8192 x 1024 with a ragged last M-block; shorter
-    prompts: the 32 x 32 MFMA kernel at b_K = 128 and 64): within FP32 rounding of
+    prompts: the 32 x 32 MFMA kernel at b_K = 128 and 64; up to 64 rows the
+    decode kernels, with tile rows handed over through the workspace at
+    3072 x 8192, M = 40): within FP32 rounding of
     aq_linear_prefill followed by aq_transform_out (per 64-block,
     |difference|_2 <= 1e-5 |y~|_2: the token scale is applied after U instead
     of before), and every seed value on some tile row."""
