@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-models", action="store_true",
                     help="skip the whole-model fields (8B-class decode steps, Qwen3-14B-shaped chunk and step)")
+    ap.add_argument("--no-fp32-decode", action="store_true",
+                    help="skip the decode segment from FP32 activations (profiles of the timed region)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -147,7 +149,8 @@ def setup(aq, gen, torch):
                        torch.empty((M,), dtype=torch.float32, device=dev),
                        torch.empty((M, N), dtype=torch.float32, device=dev))
         dec.append((proj, copies, xs, bufs))
-    ws_need = max(aq.aq_workspace_bytes(c[1][0], M, aq.AQ_PHASE_DECODE) for c in dec for M in DECODE_M)
+    ws_need = max(aq.aq_workspace_bytes(c[1][0], M, ph) for c in dec for M in DECODE_M
+                  for ph in (aq.AQ_PHASE_DECODE, aq.AQ_PHASE_DECODE_FP32))
     ws = torch.zeros(max(ws_need, 16), dtype=torch.uint8, device=dev)  # counters start at zero
     pre = []
     for proj, N, K in gen.QWEN4B:
@@ -178,6 +181,54 @@ def decode_linears(aq, i, dec, ws):
         for proj, copies, xs, bufs in dec:
             qx, sx, Y = bufs[M]
             aq.aq_linear_decode(copies[c], qx, sx, None, 0, Y, ws)
+
+
+def decode_fp32_calls(aq, i, dec, ws, two_launch=False):
+    """The 12 decode calls from the FP32 activations: aq_linear_decode_fp32
+    (one kernel where the tokens fit, else the quantizer into the workspace,
+    then the linear), or with two_launch the quantizer and the linear per
+    call; same weight copies as decode_linears."""
+    for mi, M in enumerate(DECODE_M):
+        c = (i * len(DECODE_M) + mi) % N_COPIES
+        for proj, copies, xs, bufs in dec:
+            qx, sx, Y = bufs[M]
+            if two_launch:
+                aq.aq_quant_act(xs[M], qx, sx)
+                aq.aq_linear_decode(copies[c], qx, sx, None, 0, Y, ws)
+            else:
+                aq.aq_linear_decode_fp32(copies[c], xs[M], None, 0, Y, ws)
+
+
+def fp32_decode_segment(aq, torch, dec, ws, steps: int, first: int) -> dict:
+    """The decode segment as a caller holding FP32 activations runs it, call
+    by call, both ways, each behind its own GPU hold: the quantizer and the
+    linear per call, then aq_linear_decode_fp32.  GB/s over the same
+    algorithmic bytes as the main line."""
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    cyc = sleep_cycles_per_us(torch)
+    dbytes1, _ = step_bytes_ops(dec, [])
+    out = {}
+    for name, two in (("quant_then_linear", True), ("fp32_entry", False)):
+        decode_fp32_calls(aq, first, dec, ws, two)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        decode_fp32_calls(aq, first, dec, ws, two)
+        host_us = (time.perf_counter() - t0) * 1e6
+        torch.cuda.synchronize()
+        a, b = E(), E()
+        torch.cuda._sleep(int(cyc * (2.0 * host_us * (steps + 1) + 2000.0)))
+        a.record()
+        for i in range(steps):
+            decode_fp32_calls(aq, first + i, dec, ws, two)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        out[name] = {"segment_ms_per_step": round(ms, 4), "GB/s": round(dbytes1 / (ms * 1e-3) / 1e9, 1),
+                     "us_per_call": round(ms * 1e3 / (len(DECODE_M) * len(dec)), 3)}
+    out["note"] = ("12 calls per step (M = 1, 4, 16); aq_linear_decode_fp32 runs one kernel for "
+                   "M*K <= 8192 (here the M = 1 calls of qkv, o, gate_up and down), else the same "
+                   "two launches")
+    return out
 
 
 def prefill_quant(aq, pre):
@@ -715,8 +766,10 @@ def model_fields(aq, gen, torch, reps: int = 5) -> dict:
     hold, mean of `reps` steps), then the Qwen3-14B-shaped model's one
     8192-token prefill chunk through all 160 projections (operand built by
     every call) and one batch-32 decode step (best of 3).  Each step
-    quantizes every projection's activations and runs its linear; rates are
-    algorithmic bytes or 2MNK operations over the step."""
+    quantizes every projection's activations and runs its linear (the 8B
+    M = 1 step also through aq_linear_decode_fp32, which quantizes inside the
+    linear's kernel where the tokens fit); rates are algorithmic bytes or
+    2MNK operations over the step."""
     from mixed_precision_int_amd.model import pack_model
     dev = torch.device("cuda", 0)
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -739,19 +792,23 @@ def model_fields(aq, gen, torch, reps: int = 5) -> dict:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
-    def decode_step_fn(model, geometry, M, seed_cfg, salt):
+    def decode_step_fn(model, geometry, M, seed_cfg, salt, fp32=False):
         xs = {name: gen.device_acts_outliers(M, K, gen.act_seed(seed_cfg, 0, name, salt)) for name, N, K in geometry}
         bufs = {name: (torch.empty((M, K), dtype=torch.int8, device=dev),
                        torch.empty((M,), dtype=torch.float32, device=dev),
                        torch.empty((M, N), dtype=torch.float32, device=dev)) for name, N, K in geometry}
-        need = max(aq.aq_workspace_bytes(pw, M, aq.AQ_PHASE_DECODE) for _, _, pw in model)
+        need = max(aq.aq_workspace_bytes(pw, M, ph) for _, _, pw in model
+                   for ph in (aq.AQ_PHASE_DECODE, aq.AQ_PHASE_DECODE_FP32))
         ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
 
         def step():
             for _, name, pw in model:
                 qx, sx, Y = bufs[name]
-                aq.aq_quant_act(xs[name], qx, sx)
-                aq.aq_linear_decode(pw, qx, sx, None, 0, Y, ws)
+                if fp32:  # the quantization inside the linear's kernel where the tokens fit
+                    aq.aq_linear_decode_fp32(pw, xs[name], None, 0, Y, ws)
+                else:
+                    aq.aq_quant_act(xs[name], qx, sx)
+                    aq.aq_linear_decode(pw, qx, sx, None, 0, Y, ws)
         return step, sum(linear_bytes(pw.plan, M) for _, _, pw in model)
 
     model = pack_model(gen.DENSE8B, gen.dense8b_maps(),
@@ -759,11 +816,12 @@ def model_fields(aq, gen, torch, reps: int = 5) -> dict:
     torch.cuda.synchronize()
     d8 = {"workload": "8B-class dense model (hidden 4096, FFN 14336, 36 layers), all 144 projections resident, "
                       "one decode step", "packed_gb": round(model.nbytes() / 1e9, 3)}
-    for M in (1, 64):
-        step, nbytes = decode_step_fn(model, gen.DENSE8B, M, 4, M)
+    for M, fp32 in ((1, False), (1, True), (64, False)):
+        step, nbytes = decode_step_fn(model, gen.DENSE8B, M, 4, M, fp32)
         ms = timed_ahead(step, reps)
-        d8[f"M{M}"] = {"ms_per_step": round(ms, 3), "GB/s": round(nbytes / ms / 1e6, 1),
-                       "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        d8[f"M{M}" + ("_fp32_entry" if fp32 else "")] = {
+            "ms_per_step": round(ms, 3), "GB/s": round(nbytes / ms / 1e6, 1),
+            "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
         del step
     out["dense8b_decode"] = d8
     del model
@@ -1148,6 +1206,11 @@ def main():
             "prefill_segment_ms": _med_min([p_seg[i].elapsed_time(p_seg[i + 1]) for i in range(K)]),
         },
     }
+    if not args.no_fp32_decode:
+        try:  # after the timed region, outside ms_per_step
+            out["decode_fp32"] = fp32_decode_segment(aq, torch, dec, ws, args.steps, args.warmup + args.steps)
+        except Exception as e:  # the headline line is printed regardless
+            out["decode_fp32"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_models:
         try:
             out["models"] = model_fields(aq, gen, torch)

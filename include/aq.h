@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AQ_ABI_VERSION 10
+#define AQ_ABI_VERSION 11
 
 typedef enum aq_status {
   AQ_OK = 0,
@@ -112,11 +112,13 @@ typedef struct aq_packed {
 /* Phase selector for aq_workspace_bytes / aq_linear_tile_partials;
  * AQ_PHASE_PREFILL_GROUPED sizes the workspace of aq_linear_prefill_grouped
  * and aq_linear_tile_partials_grouped, AQ_PHASE_DECODE_TRANSFORMED that of
- * aq_linear_decode_transformed (workspace sizes only). */
+ * aq_linear_decode_transformed, AQ_PHASE_DECODE_FP32 that of
+ * aq_linear_decode_fp32 (workspace sizes only). */
 #define AQ_PHASE_DECODE 0
 #define AQ_PHASE_PREFILL 1
 #define AQ_PHASE_PREFILL_GROUPED 2
 #define AQ_PHASE_DECODE_TRANSFORMED 3
+#define AQ_PHASE_DECODE_FP32 4
 
 /* ABI version of the loaded library (AQ_ABI_VERSION). */
 int aq_abi_version(void);
@@ -239,6 +241,28 @@ int aq_decode_split(const aq_packed *W, int M);
 aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx, int M,
                            const float *bias, float *Y, int split, void *ws, size_t ws_bytes,
                            void *stream);
+
+/* Decode from FP32 activations: the per-token quantization of
+ * aq_quant_act (App. B.3, eq. 5 rounding) followed by aq_linear_decode, in
+ * one call.  Y is bit for bit that of aq_quant_act then aq_linear_decode
+ * with the same split and bias.  Up to 4 tokens with M*K <= 8192 (so
+ * K <= 4096 at M = 2, K <= 8192 at M = 1) run as one kernel: every
+ * workgroup quantizes the tokens' rows into on-chip memory as its first
+ * weight loads land, which saves the quantizer's launch.  Other calls run
+ * aq_quant_act into the workspace, then aq_linear_decode.
+ *   X     device FP32 [M][K] row-major, 16-byte aligned
+ *   bias, Y, split as aq_linear_decode
+ *   ws    device workspace of at least
+ *         aq_workspace_bytes(W, M, AQ_PHASE_DECODE_FP32, split) bytes,
+ *         16-byte aligned (NULL when that is 0, as for the one-kernel
+ *         route), else AQ_ERR_WORKSPACE.  Layout: aq_linear_decode's
+ *         workspace first, at least its 256 KiB block of arrival counters
+ *         (zero before the call and left zero by it, so one workspace can
+ *         serve this call and aq_linear_decode alike), then the INT8 rows
+ *         and the FP32 scales, whose contents need no initialization.
+ * M == 0 is a no-op. */
+aq_status aq_linear_decode_fp32(const aq_packed *W, const float *X, int M, const float *bias, float *Y,
+                                int split, void *ws, size_t ws_bytes, void *stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation):

@@ -21,6 +21,7 @@ AQ_PHASE_DECODE = 0
 AQ_PHASE_PREFILL = 1
 AQ_PHASE_PREFILL_GROUPED = 2
 AQ_PHASE_DECODE_TRANSFORMED = 3
+AQ_PHASE_DECODE_FP32 = 4
 
 STATUS = {0: "AQ_OK", -1: "AQ_ERR_NULL", -2: "AQ_ERR_SHAPE", -3: "AQ_ERR_TILE", -4: "AQ_ERR_MAP",
           -5: "AQ_ERR_ALIGN", -6: "AQ_ERR_WORKSPACE", -7: "AQ_ERR_HIP", -8: "AQ_ERR_ARG"}
@@ -33,7 +34,8 @@ EXPORTS = ["aq_abi_version", "aq_status_string", "aq_labels_from_map", "aq_plan_
            "aq_linear_tile_partials_grouped", "aq_pack_weights_mse",
            "aq_transform_rows", "aq_transform_out", "aq_transform_weights", "aq_quant_act_transformed",
            "aq_prefill_prepare", "aq_linear_prefill_prepared", "aq_linear_prefill_transformed",
-           "aq_act_group_shape", "aq_linear_decode_noalloc", "aq_linear_decode_transformed"]
+           "aq_act_group_shape", "aq_linear_decode_noalloc", "aq_linear_decode_transformed",
+           "aq_linear_decode_fp32"]
 
 
 class AqError(RuntimeError):
@@ -95,6 +97,7 @@ def lib() -> ctypes.CDLL:
         "aq_linear_decode": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp, sz, vp]),
         "aq_linear_prefill": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, vp, sz, vp]),
         "aq_linear_decode_noalloc": (i32, [ctypes.POINTER(AqPacked), vp, vp, i32, vp, vp, i32, vp]),
+        "aq_linear_decode_fp32": (i32, [ctypes.POINTER(AqPacked), vp, i32, vp, vp, i32, vp, sz, vp]),
         "aq_linear_tile_partials": (i32, [ctypes.POINTER(AqPacked), vp, i32, i32, vp, vp, sz, vp]),
         "aq_quant_act_grouped": (i32, [vp, i32, i32, vp, vp, vp]),
         "aq_act_group_shape": (i32, [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
@@ -288,6 +291,27 @@ def aq_linear_decode(pw: PackedWeights, qx, sx, bias=None, split: int = 0, out=N
     _check(lib().aq_linear_decode(ctypes.byref(pw.desc), _ptr(qx), _ptr(sx), M, _ptr(bias),
                                   _ptr(out), split, _ptr(ws), ws_bytes, _stream(stream)),
            "aq_linear_decode")
+    return out
+
+
+def aq_linear_decode_fp32(pw: PackedWeights, X, bias=None, split: int = 0, out=None, ws=None,
+                          stream=None):
+    """Decode-phase linear from FP32 activations X [M, K]: the per-token
+    quantization and the linear in one call (one kernel for up to 4 tokens
+    with M*K <= 8192); FP32 Y [M, N], bit for bit aq_quant_act followed by
+    aq_linear_decode.  Without `ws` the stream's cached decode workspace is
+    used when the call needs one."""
+    import torch
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=X.device)
+    need = aq_workspace_bytes(pw, M, AQ_PHASE_DECODE_FP32, split)
+    if ws is None and need:
+        ws = decode_workspace(need, X.device, stream)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().aq_linear_decode_fp32(ctypes.byref(pw.desc), _ptr(X), M, _ptr(bias), _ptr(out), split,
+                                       _ptr(ws), ws_bytes, _stream(stream)),
+           "aq_linear_decode_fp32")
     return out
 
 

@@ -287,8 +287,10 @@ size_t aq_workspace_bytes(const aq_packed *W, int M, int phase, int split) {
   if (phase == AQ_PHASE_PREFILL) return aq::prefill_call_workspace_bytes(v, M);
   if (phase == AQ_PHASE_PREFILL_GROUPED)
     return aq::prefill_grouped_long(v, M) ? aq::prefill_workspace_bytes(v, M) : aq::decode_workspace_bytes(v, M, 0);
-  if (phase != AQ_PHASE_DECODE && phase != AQ_PHASE_DECODE_TRANSFORMED) return 0;
+  if (phase != AQ_PHASE_DECODE && phase != AQ_PHASE_DECODE_TRANSFORMED && phase != AQ_PHASE_DECODE_FP32)
+    return 0;
   if (split < 0 || (split > 0 && !aq::decode_split_supported(v, M, split))) return 0;
+  if (phase == AQ_PHASE_DECODE_FP32) return aq::fp32_workspace_bytes(v, M, split);
   return aq::decode_workspace_bytes(v, M, split, phase == AQ_PHASE_DECODE_TRANSFORMED);
 }
 
@@ -306,6 +308,28 @@ aq_status aq_linear_decode(const aq_packed *W, const int8_t *qx, const float *sx
   if (st != AQ_OK) return st;
   return aq::launch_decode(v, qx, sx, M, bias, Y, split, ws, nullptr,
                            static_cast<hipStream_t>(stream)) == hipSuccess
+             ? AQ_OK
+             : AQ_ERR_HIP;
+}
+
+aq_status aq_linear_decode_fp32(const aq_packed *W, const float *X, int M, const float *bias, float *Y,
+                                int split, void *ws, size_t ws_bytes, void *stream) {
+  aq_status st = check_packed(W);
+  if (st != AQ_OK) return st;
+  if (M < 0) return AQ_ERR_SHAPE;
+  if (M == 0) return AQ_OK;
+  if (!X || !Y) return AQ_ERR_NULL;
+  if (!aligned16(X) || !aligned16(Y)) return AQ_ERR_ALIGN;
+  if (bias && !aligned16(bias)) return AQ_ERR_ALIGN;
+  if ((long long)M * W->K > (1LL << 40) || (long long)M * W->N > (1LL << 40) || M > (1 << 30))
+    return AQ_ERR_SHAPE;
+  const aq::PackedView v = aq::view_of(*W);
+  if (split < 0 || (split > 0 && !aq::decode_split_supported(v, M, split))) return AQ_ERR_ARG;
+  if (!aq::decode_plan_ok(aq::plan_decode(v, M, split), v)) return AQ_ERR_SHAPE;
+  st = check_workspace(ws, ws_bytes, aq::fp32_workspace_bytes(v, M, split));
+  if (st != AQ_OK) return st;
+  return aq::launch_decode_fp32(v, X, M, bias, Y, split, ws, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
              ? AQ_OK
              : AQ_ERR_HIP;
 }

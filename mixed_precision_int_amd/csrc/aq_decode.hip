@@ -38,7 +38,15 @@
 //            that the 16 rows one MFMA operand reads fall in distinct banks)
 //            and publishes them with one barrier while the first weight batch
 //            is in flight; when they do not fit, lanes read them from global
-//            memory instead.
+//            memory instead;
+//   fused  : (M <= 4, from FP32 activations) the workgroup loads the tokens'
+//            FP32 rows right behind its first weight batch, finds each row's
+//            max |x| (waves, then LDS, one barrier), quantizes the rows by the
+//            rule of the activation quantizer (App. B.3: per-token scale,
+//            INT8 codes) into the staged layout above and publishes them with
+//            the staging barrier; the rows come from L2 faster than the
+//            weights from HBM, so only the quantization itself is added to
+//            the critical path, not a second kernel launch.
 //
 // Products (the pages split decode by M too, Table 5, with byte dot
 // products for one token):
@@ -60,6 +68,7 @@
 
 #include "aq_device.h"
 #include "aq_internal.h"
+#include "aq_quant.h"
 
 namespace aq {
 namespace {
@@ -74,6 +83,7 @@ struct DecodeArgs {
   const float *sx, *bias;
   float *Y;
   int32_t *P;
+  const float *xf;  // fused route: FP32 activations [M][K] (qx and sx unused)
   int N, K, R, C, T4, T8, M, label_words;
   // input-column chunks per row block (one workgroup each), the LDS row
   // stride of staged activations, and the workspace of chunked calls:
@@ -322,6 +332,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
   v4i xb[XU];
   const int8_t *xsrc = a.qx + (size_t)mbase * K + (size_t)ca * BK;
   const bool xstage = XMODE == kXShared;
+  constexpr bool FUSED = XMODE == kXFused;
   const int xgran = xstage ? xrows * kg : 0;
   if (xstage) {
 #pragma unroll
@@ -478,19 +489,126 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
   float bv = 0.0f;
   uint32_t xtw = 0u;  // XF: word tid of the transform tables
   if constexpr (!PARTIALS && !GRP && MODE == kMfma) {
+    if constexpr (!FUSED) {
 #pragma unroll
-    for (int mg = 0; mg < MG; ++mg)
+      for (int mg = 0; mg < MG; ++mg)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = mbase + mg * 16 + 4 * g + e;
-        sxv[mg][e] = m < M ? a.sx[m] : 0.0f;
-      }
+        for (int e = 0; e < 4; ++e) {
+          const int m = mbase + mg * 16 + 4 * g + e;
+          sxv[mg][e] = m < M ? a.sx[m] : 0.0f;
+        }
+    }
     if (a.bias) bv = a.bias[(size_t)r * 64 + (XF ? lane : rg * 16 + i16)];
   }
   if constexpr (XF) {
     if (tid < kXfWords) xtw = reinterpret_cast<const uint32_t *>(&a.xf.xt)[tid];
   }
-  if (xstage) {
+  // ---- fused route: the tokens' FP32 rows, kFusedUnits float4 per thread
+  // (consecutive threads, consecutive float4), loaded right behind the first
+  // weight batch: waiting for them waits for that batch too, whose HBM
+  // latency exceeds theirs, so the quantization below starts about when the
+  // weights land
+  float4 xq32[FUSED ? kFusedUnits : 1];
+  const int nf4 = FUSED ? M * (K >> 2) : 0;
+  if constexpr (FUSED) {
+    // (threads past the rows in a partly used pass re-read a unit inside
+    // them, spread over the largest power-of-two prefix: one address read
+    // by every workgroup would queue on one L2 channel)
+    const float4 *xsrc32 = reinterpret_cast<const float4 *>(a.xf);
+    const int p2m = (1 << (31 - __builtin_clz(nf4))) - 1;
+#pragma unroll
+    for (int u = 0; u < kFusedUnits; ++u) {
+      const int q = tid + u * NT;
+      if (u * NT < nf4) xq32[u] = xsrc32[q < nf4 ? q : (q & p2m)];
+    }
+  }
+  if constexpr (FUSED) {
+    // Per-token quantization, the rule of the activation quantizer: s =
+    // max(max|x| / 127, 1e-12) in FP64, codes rint(x / s) clipped to INT8.
+    // Row maxima of this thread's units, of the wave (uniform), then of the
+    // workgroup through LDS row M of the staging area (the token rows are
+    // rows 0 .. M-1).
+    const int k4 = K >> 2;
+    // token row of unit q without a division (M <= 4)
+    auto row_of = [&](int q) __attribute__((always_inline)) {
+      return (int)(q >= k4) + (int)(q >= 2 * k4) + (int)(q >= 3 * k4);
+    };
+    uint32_t pm[kFusedMaxM] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < kFusedUnits; ++u) {
+      const int q = tid + u * NT;
+      if (u * NT < nf4 && q < nf4) {
+        const int row = row_of(q);
+        const uint32_t v = abs_bits4(xq32[u]);
+#pragma unroll
+        for (int t = 0; t < kFusedMaxM; ++t)
+          if (row == t) pm[t] = max(pm[t], v);
+      }
+    }
+    uint32_t *amx = reinterpret_cast<uint32_t *>(xs + (size_t)M * xst);  // [token][wave]
+#pragma unroll
+    for (int t = 0; t < kFusedMaxM; ++t) {
+      if (t < M) {  // uniform
+        const uint32_t v = wave_max_u32(pm[t]);
+        if (lane == 0) amx[t * WAVES + wave] = v;
+      }
+    }
+    __syncthreads();
+    // lane t < M finds token t's scale and its FP32 reciprocal (one FP64
+    // division pair per wave), then every lane takes them from there
+    uint32_t mx = 0u;
+    if (lane < M) {
+      const uint4 *am4 = reinterpret_cast<const uint4 *>(amx + lane * WAVES);
+      uint4 v[WAVES / 4];
+#pragma unroll
+      for (int w4 = 0; w4 < WAVES / 4; ++w4) v[w4] = am4[w4];  // all issued, then one wait
+#pragma unroll
+      for (int w4 = 0; w4 < WAVES / 4; ++w4) mx = max(mx, max(max(v[w4].x, v[w4].y), max(v[w4].z, v[w4].w)));
+    }
+    const double sl = row_scale(mx);
+    const float il = (float)(1.0 / sl);
+    const long long slb = __double_as_longlong(sl);
+    double sd[kFusedMaxM];
+    float inv[kFusedMaxM], sq[kFusedMaxM];
+#pragma unroll
+    for (int t = 0; t < kFusedMaxM; ++t) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)slb, t);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(slb >> 32), t);
+      sd[t] = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+      inv[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(il), t));
+      sq[t] = (float)sd[t];
+    }
+    // this thread's codes into the token rows, granules swizzled as staged
+#pragma unroll
+    for (int u = 0; u < kFusedUnits; ++u) {
+      const int q = tid + u * NT;
+      if (u * NT < nf4 && q < nf4) {
+        const int row = row_of(q);
+        const int c = (q - row * k4) * 4;
+        double sr = sd[0];
+        float ir = inv[0];
+#pragma unroll
+        for (int t = 1; t < kFusedMaxM; ++t)
+          if (row == t) {
+            sr = sd[t];
+            ir = inv[t];
+          }
+        *reinterpret_cast<uint32_t *>(xs + row * xst + 16 * ((c >> 4) ^ (row & 15)) + (c & 15)) =
+            codes4_fast(xq32[u], sr, ir);
+      }
+    }
+    // the token scales of the lane's outputs (one token group)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * g + e;
+      float v = 0.0f;
+#pragma unroll
+      for (int t = 0; t < kFusedMaxM; ++t)
+        if (m == t && t < M) v = sq[t];
+      sxv[0][e] = v;
+    }
+  }
+  if (xstage || FUSED) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS writes done; vmcnt left open
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -545,7 +663,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
           const int trow = min(mg * 16 + i16, xrows - 1);
           const int8_t *xr = XMODE == kXPriv ? xw + trow * XW : xs + trow * xst;
           const int xcol = XMODE == kXPriv ? d * BK : (jt - ca) * BK;
-          const int sw = XMODE == kXShared ? (trow & 15) : 0;
+          const int sw = XMODE != kXPriv ? (trow & 15) : 0;
           if constexpr (GRP) {
             // one INT32 product per 64-feature group (step u), each scaled by
             // its own activation-group scale (token group of 16 rows)
@@ -660,7 +778,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
     if (MODE == kValu) F[0].x = sum_kgroups(F[0].x);  // sum the four k-groups of each row
     // ordered split reduction through LDS
     if (S > 1) {
-      if (XMODE == kXShared) __syncthreads();  // every wave is done with the token rows
+      if (XMODE != kXPriv) __syncthreads();  // every wave is done with the token rows
 #pragma unroll
       for (int mg = 0; mg < MG; ++mg) red[(wave * MG + mg) * 64 + lane] = F[mg];
       __syncthreads();
@@ -867,6 +985,12 @@ void launch_mode(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL
     launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP, true, XF>(p, R, stream, args);
     return;
   }
+  if constexpr (!PARTIALS && !GRP && !XF) {
+    if (p.xmode == kXFused) {  // (6 tiles per batch: the FP32 rows' registers fit beside them)
+      launch_rg<BK, kMfma, 1, 16, kSharedDepthN, kXFused, false, INL, false, true, false>(p, R, stream, args);
+      return;
+    }
+  }
   // (the transformed route keeps the non-temporal loads for every call: one
   // set of kernels fewer to build)
   if (PARTIALS || XF || p.mchunks == 1) {
@@ -954,13 +1078,14 @@ hipError_t decode_scratch(hipStream_t stream, void **out) {
 namespace {
 
 // The launches of one decode call (tables != nullptr: with the output
-// transform in the epilogue).
+// transform in the epilogue; X != nullptr: the fused route from FP32
+// activations, which the caller has checked with fused_ok).
 hipError_t decode_launches(const PackedView &w, const int8_t *qx, const float *sx, int M,
                            const float *bias, float *Y, int split, void *ws, int32_t *P,
                            hipStream_t stream, bool grouped, const int8_t *useeds,
-                           const TransformTables *tables) {
+                           const TransformTables *tables, const float *X = nullptr) {
   const bool xf = tables != nullptr;
-  DecodePlan p = plan_decode(w, M, split, xf);
+  DecodePlan p = X ? plan_decode_fused(w, M, split) : plan_decode(w, M, split, xf);
   if (!decode_plan_ok(p, w, xf) || p.ylaunch < 1) return hipErrorInvalidValue;
   if (grouped && M <= kValuMaxM) p.mode = kValu;
   DecodeArgs args;
@@ -968,6 +1093,7 @@ hipError_t decode_launches(const PackedView &w, const int8_t *qx, const float *s
   args.w4 = w.w4; args.w8 = w.w8; args.s4 = w.s4; args.s8 = w.s8;
   args.qx = qx; args.sx = sx; args.bias = bias;
   args.Y = Y; args.P = P;
+  args.xf = X;
   args.N = w.N; args.K = w.K; args.R = w.R; args.C = w.C; args.T4 = w.T4; args.T8 = w.T8;
   args.M = M; args.label_words = (w.R * w.C + 31) / 32;
   args.Z = p.Z;
@@ -991,13 +1117,13 @@ hipError_t decode_launches(const PackedView &w, const int8_t *qx, const float *s
     DArgs<false, false> la;
     static_cast<DecodeArgs &>(la) = args;
     la.M = M - m0 < mstep ? M - m0 : mstep;
-    la.qx = qx + (size_t)m0 * w.K;
+    if (qx) la.qx = qx + (size_t)m0 * w.K;
     // grouped scales: one row of K/64 per 16 tokens (launches start on a
     // multiple of 16 tokens; a single token is its own group)
     if (sx) la.sx = grouped ? sx + (size_t)(m0 / 16) * (w.K / 64) : sx + m0;
     if (Y) la.Y = Y + (size_t)m0 * w.N;
     if (P) la.P = P + (size_t)m0 * w.N * w.C;
-    la.ychunks = p.mode == kValu || p.xmode == kXPriv ? 1 : (la.M + 16 * p.MG - 1) / (16 * p.MG);
+    la.ychunks = p.mode == kValu || p.xmode != kXShared ? 1 : (la.M + 16 * p.MG - 1) / (16 * p.MG);
     if (P && grouped) {
       if (w.bK == 128) launch_mode<128, true, false, true>(p, w.R, stream, la);
       else launch_mode<64, true, false, true>(p, w.R, stream, la);
@@ -1049,6 +1175,19 @@ hipError_t launch_decode_transformed(const PackedView &w, const int8_t *qx, cons
                                      const int8_t *useeds, const TransformTables &t,
                                      hipStream_t stream) {
   return decode_launches(w, qx, sx, M, bias, Y, split, ws, nullptr, stream, false, useeds, &t);
+}
+
+hipError_t launch_decode_fp32(const PackedView &w, const float *X, int M, const float *bias, float *Y,
+                              int split, void *ws, hipStream_t stream) {
+  if (fused_ok(w, M, split))
+    return decode_launches(w, nullptr, nullptr, M, bias, Y, split, nullptr, nullptr, stream, false,
+                           nullptr, nullptr, X);
+  // quantize into the workspace behind the decode workspace, then decode
+  int8_t *qx = static_cast<int8_t *>(ws) + fp32_head_bytes(w, M, split);
+  float *sx = reinterpret_cast<float *>(qx + (((size_t)M * w.K + 255) & ~(size_t)255));
+  const hipError_t e = launch_quant_act(X, M, w.K, qx, sx, stream);
+  if (e != hipSuccess) return e;
+  return decode_launches(w, qx, sx, M, bias, Y, split, ws, nullptr, stream, false, nullptr, nullptr);
 }
 
 }  // namespace aq

@@ -155,8 +155,18 @@ constexpr int kInlineWordsXf = 768;     // the same with the output-transform ta
 constexpr int kMetaStride = 6;          // words per tile row in the host metadata image
 enum { kValu = 0, kMfma = 1 };
 // Where the MFMA/VALU activation operands come from: a per-wave LDS slice
-// of the batch, or the workgroup's LDS copy of its tokens' chunk columns.
-enum { kXPriv = 0, kXShared = 1 };
+// of the batch, the workgroup's LDS copy of its tokens' chunk columns, or
+// that copy quantized by the workgroup itself from the FP32 activations.
+enum { kXPriv = 0, kXShared = 1, kXFused = 2 };
+// The fused route quantizes at most kFusedMaxM tokens, whose FP32 rows are
+// loaded once, kFusedUnits float4 per thread of the 16-wave workgroup
+// (M * K <= 4 * 1024 * kFusedUnits).  Every workgroup quantizes all of them:
+// measured on the Llama-3.2-3B-shaped projections, the route beats the
+// separate quantizer launch by 0.7-1.0 us per call at M = 1 and 0.3-0.5 us
+// at M = 2, K = 3072, and loses 0.8 us beyond 8192 elements (K = 8192,
+// M = 2).
+constexpr int kFusedMaxM = kPrivMaxM;
+constexpr int kFusedUnits = 2;
 
 // Launch plan of one decode call: products on the vector ALU or MFMA, where
 // the activation operands live, token groups of 16 per workgroup, waves,
@@ -184,6 +194,21 @@ bool decode_plan_ok(const DecodePlan &p, const PackedView &w, bool xform = false
 int decode_split(const PackedView &w, int M);
 bool decode_split_supported(const PackedView &w, int M, int S);
 size_t decode_workspace_bytes(const PackedView &w, int M, int split, bool xform = false);
+// Decode from FP32 activations.  fused_ok: the call fits the one-kernel
+// route (at most kFusedMaxM tokens, rows within the per-thread loads and
+// LDS, no column chunks), whose plan is plan_decode_fused: the per-token
+// plan's row groups and splits, the tokens' quantized rows shared in LDS.
+// Otherwise launch_decode_fp32 quantizes into the workspace and runs the
+// decode linear: the decode workspace first, at least the whole block of
+// arrival counters (fp32_head_bytes, so that a workspace shared with other
+// decode calls keeps zero counters), then the INT8 rows and the scales;
+// fp32_workspace_bytes covers both routes.
+bool fused_ok(const PackedView &w, int M, int split);
+DecodePlan plan_decode_fused(const PackedView &w, int M, int split);
+size_t fp32_head_bytes(const PackedView &w, int M, int split);
+size_t fp32_workspace_bytes(const PackedView &w, int M, int split);
+hipError_t launch_decode_fp32(const PackedView &w, const float *X, int M, const float *bias, float *Y,
+                              int split, void *ws, hipStream_t stream);
 // The allocation-free decode's device scratch (AQ_DECODE_SCRATCH_BYTES):
 // its address on the current device, found once per device with
 // hipGetSymbolAddress; the first call on a device also enqueues, on

@@ -188,6 +188,44 @@ size_t decode_workspace_bytes(const PackedView &w, int M, int split, bool xform)
   return plan_decode(w, M, split, xform).ws_bytes;
 }
 
+// The fused route keeps the per-token plan's row groups and splits (so its
+// sums are those of the plan it replaces, bit for bit) and stages the M
+// quantized token rows, then a row of per-wave maxima, in LDS.
+DecodePlan plan_decode_fused(const PackedView &w, int M, int split) {
+  DecodePlan p = plan_decode(w, M, split);
+  p.xmode = kXFused;
+  p.MG = 1;
+  p.Z = 1;
+  p.mchunks = 1;
+  p.ylaunch = 1;
+  p.xstride = chunk_stride(w.C, w.bK);
+  const size_t xb = (size_t)(M + 1) * p.xstride;
+  const size_t red = (size_t)p.waves * 64 * sizeof(float4);
+  p.lds = xb > red ? xb : red;
+  p.cnt_bytes = 0;
+  p.ws_bytes = 0;
+  return p;
+}
+
+bool fused_ok(const PackedView &w, int M, int split) {
+  if (M < 1 || M > kFusedMaxM || M > kPrivMaxM || w.C > 128) return false;  // labels from one window
+  const DecodePlan p = plan_decode_fused(w, M, split);
+  if ((long long)M * w.K > 4LL * 64 * p.waves * kFusedUnits) return false;
+  return p.mode == kMfma && p.waves == 16 && p.lds <= (size_t)kLdsBudget && decode_plan_ok(p, w);
+}
+
+size_t fp32_head_bytes(const PackedView &w, int M, int split) {
+  const size_t dws = decode_workspace_bytes(w, M, split);
+  const size_t cnt = (size_t)kDecodeCounters * 4;
+  return ((dws > cnt ? dws : cnt) + 255) & ~(size_t)255;
+}
+
+size_t fp32_workspace_bytes(const PackedView &w, int M, int split) {
+  if (M <= 0 || fused_ok(w, M, split)) return 0;
+  return fp32_head_bytes(w, M, split) + (((size_t)M * w.K + 255) & ~(size_t)255) +
+         (((size_t)M * sizeof(float) + 255) & ~(size_t)255);
+}
+
 // Measured on the 8B-class shapes at M = 96 / 128: qkv 26.4 / 29.5 us on the
 // decode kernels against 41.9 / 42.0 us on the GEMM (48 blocks), o 16.8 /
 // 18.7 against 41.5 / 41.7, down 47.6 / 50.9 against 125.9 / 126.2; gate_up

@@ -20,6 +20,26 @@ __device__ __forceinline__ uint32_t codes4(const float4 &v, double s) {
          (code_of(v.w, s) << 24);
 }
 
+// code_of(x, s) with the FP64 division taken only where an FP32 estimate
+// cannot decide it.  inv = 1/s rounded to FP32 (from the FP64 reciprocal),
+// p = x * inv rounded to FP32, so p = (x / s)(1 + d) with |d| < 2^-23 +
+// 2^-47.  The estimate is used when r = rint(p) has |r| <= 127 and
+// |p - r| < 1/2 - 2^-15: then |x / s| < 128, |p - x / s| < 2^-16 + 2^-40,
+// and x / s lies inside (r - 1/2 + 2^-17, r + 1/2 - 2^-17); its FP64
+// quotient (within 2^-46 of it) rounds to r too, and r needs no clipping.
+// Every other case (near ties, out of range, NaN) takes code_of.
+__device__ __forceinline__ uint32_t code_fast(float x, double s, float inv) {
+  const float p = x * inv;
+  const float r = rintf(p);
+  if (fabsf(p - r) < 0.5f - 0x1p-15f && fabsf(r) <= 127.0f) return (uint32_t)((int)r & 0xFF);
+  return code_of(x, s);
+}
+
+__device__ __forceinline__ uint32_t codes4_fast(const float4 &v, double s, float inv) {
+  return code_fast(v.x, s, inv) | (code_fast(v.y, s, inv) << 8) | (code_fast(v.z, s, inv) << 16) |
+         (code_fast(v.w, s, inv) << 24);
+}
+
 // Bits of |x|: for non-negative IEEE floats the unsigned order of the bit
 // patterns is the numeric order, so the maximum is an integer max.
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }

@@ -208,6 +208,34 @@ int main() {
         CHECK(g_launches == before);
       }
       {
+        // decode from FP32 activations: one kernel (no workspace) or the
+        // quantizer into the workspace behind a whole counter block
+        const size_t wf = aq_workspace_bytes(&f.p, M, AQ_PHASE_DECODE_FP32, 0);
+        CHECK(wf == 0 || wf >= wd + (size_t)M * sh[1]);
+        CHECK(wf == 0 || wf >= ((size_t)256 << 10));
+        std::vector<unsigned char> wsf(wf + 256);
+        unsigned char *wsf_a = wsf.data() + (256 - (uintptr_t)wsf.data() % 256) % 256;
+        struct F32 { Fake *f; int M; void *w; size_t n; } fc{&f, M, wf ? wsf_a : nullptr, wf};
+        expect_launch([](void *v) { F32 *c = (F32 *)v;
+          return aq_linear_decode_fp32(&c->f->p, (const float *)dev(0), c->M, (const float *)dev(12288),
+                                       (float *)dev(8192), 0, c->w, c->n, nullptr); }, &fc, "aq_linear_decode_fp32");
+        const int before = g_launches;
+        if (wf)
+          CHECK(aq_linear_decode_fp32(&f.p, (const float *)dev(0), M, nullptr, (float *)dev(8192), 0, wsf_a, wf - 1,
+                                      nullptr) == AQ_ERR_WORKSPACE);
+        CHECK(aq_linear_decode_fp32(&f.p, nullptr, M, nullptr, (float *)dev(8192), 0, fc.w, fc.n, nullptr) ==
+              AQ_ERR_NULL);
+        CHECK(aq_linear_decode_fp32(&f.p, (const float *)dev(4), M, nullptr, (float *)dev(8192), 0, fc.w, fc.n,
+                                    nullptr) == AQ_ERR_ALIGN);
+        CHECK(aq_linear_decode_fp32(&f.p, (const float *)dev(0), M, nullptr, (float *)dev(8192), 5, fc.w, fc.n,
+                                    nullptr) == AQ_ERR_ARG);
+        CHECK(aq_linear_decode_fp32(&f.p, (const float *)dev(0), -1, nullptr, (float *)dev(8192), 0, fc.w, fc.n,
+                                    nullptr) == AQ_ERR_SHAPE);
+        CHECK(aq_linear_decode_fp32(&f.p, (const float *)dev(0), 0, nullptr, nullptr, 0, nullptr, 0, nullptr) ==
+              AQ_OK);
+        CHECK(g_launches == before);
+      }
+      {
         const size_t wg = aq_workspace_bytes(&f.p, M, AQ_PHASE_PREFILL_GROUPED, 0);
         std::vector<unsigned char> wsg(wg + 256);
         unsigned char *wsg_a = wsg.data() + (256 - (uintptr_t)wsg.data() % 256) % 256;

@@ -66,6 +66,10 @@ hipError_t launch_decode_transformed(const PackedView &, const int8_t *, const f
                                      hipStream_t) {
   return launched();
 }
+hipError_t launch_decode_fp32(const PackedView &, const float *, int, const float *, float *, int, void *,
+                              hipStream_t) {
+  return launched();
+}
 hipError_t launch_zero_counters(void *, hipStream_t) { return launched(); }
 hipError_t decode_scratch(hipStream_t, void **out) {
   static unsigned char fake[64];

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(aqlib):
 
 
 def test_abi_version_and_status_strings(aqlib):
-    assert B.aq_abi_version() == 10
+    assert B.aq_abi_version() == 11
     for code in list(B.STATUS) + [-99]:
         assert aqlib.aq_status_string(code)
 
@@ -321,3 +321,29 @@ def test_decode_transformed_workspace(aqlib):
     big = fake_packed(N=256, K=65536, T4=4 * 512 - 3, T8=3)        # column chunks
     assert ws(ctypes.byref(big), 16, B.AQ_PHASE_DECODE_TRANSFORMED, 0) >= ws(ctypes.byref(big), 16, 0, 0) > 0
     assert f(many, 0) == 0 and f(many, 4, us=None) == -1 and f(many, 4, split=5) == -8
+
+
+def test_decode_fp32_workspace(aqlib):
+    """Decode from FP32 activations: up to 4 tokens with M*K <= 8192 run as
+    one kernel that needs no workspace; other calls quantize into the
+    workspace behind a whole block of arrival counters (256 KiB or the
+    decode workspace, whichever is larger), then run the decode linear.
+    Invalid calls are rejected on the host."""
+    L = B.lib()
+    ws = L.aq_workspace_bytes
+    f = lambda d, M, X=FAKE, w=None, n=0, split=0: L.aq_linear_decode_fp32(
+        ctypes.byref(d), X, M, None, FAKE, split, w, n, None)
+    q = fake_packed(N=3072, K=3072, T4=48 * 24 - 5, T8=5)         # K = 3072
+    d = fake_packed(N=3072, K=8192, T4=48 * 64 - 5, T8=5)         # K = 8192
+    for M in (1, 2):
+        assert ws(ctypes.byref(q), M, B.AQ_PHASE_DECODE_FP32, 0) == 0, M
+    assert ws(ctypes.byref(q), 3, B.AQ_PHASE_DECODE_FP32, 0) > 0
+    assert ws(ctypes.byref(d), 1, B.AQ_PHASE_DECODE_FP32, 0) == 0
+    for M in (2, 3, 4, 5, 16, 64):
+        need = ws(ctypes.byref(d), M, B.AQ_PHASE_DECODE_FP32, 0)
+        head = max(ws(ctypes.byref(d), M, B.AQ_PHASE_DECODE, 0), 256 * 1024)
+        rows = (M * 8192 + 255) // 256 * 256
+        assert need == (head + 255) // 256 * 256 + rows + (4 * M + 255) // 256 * 256, (M, need)
+        assert f(d, M) == -6 and f(d, M, w=FAKE, n=need - 1) == -6 and f(d, M, w=FAKE + 4, n=need) == -5
+    assert f(q, 4, X=None) == -1 and f(q, 4, X=FAKE + 4) == -5 and f(q, 4, split=5) == -8
+    assert f(q, -1) == -2 and f(q, 0, X=None) == 0
