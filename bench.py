@@ -110,6 +110,9 @@ def parse():
                          "read and copy bandwidth by size, back-to-back launch floor, and hipBLASLt INT8 "
                          "GEMM rate (torch._int_mm) on the prefill shapes and a large square; print a "
                          "markdown table")
+    ap.add_argument("--trace-summary", metavar="DB",
+                    help="print the per-call kernel times of the timed region from a rocprofv3 "
+                         "--kernel-trace database of a default bench run (run with --no-fp32-decode)")
     ap.add_argument("--traffic-summary", nargs=4, metavar="CSV",
                     help="print the per-launch HBM traffic summary from four rocprofv3 counter "
                          "CSVs: bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE")
@@ -318,6 +321,70 @@ def traffic_summary(paths) -> dict:
                          calls=ncalls, sources_sha=sources_sha(kind))
     return dict(copy_calibration=dict(bytes=cal_bytes, fetch_factor=round(f_fetch, 4),
                                       write_factor=round(f_write, 4)), kernels=res)
+
+
+def trace_summary(db_path: str) -> str:
+    """Per-call kernel times of the timed region from a rocprofv3 kernel-trace
+    database (its `kernels` view) of a bench run made with --no-fp32-decode:
+    the dispatches after the last spin kernel (the hold that opens the timed
+    region), which runs the decode segments of all steps, then the prefill
+    segments.  Decode calls are averaged per position in the step (M, then
+    projection, as decode_linears issues them); GB/s and fractions use the
+    bench's algorithmic bytes (plans from the same seeded maps, on the host)
+    and 2MNK."""
+    import sqlite3
+    from mixed_precision_int_amd import binding as aqb
+    from workloads import gen
+
+    rows = sqlite3.connect(db_path).execute("select name, start, end from kernels order by start").fetchall()
+    last = max(i for i, r in enumerate(rows) if "spin_kernel" in r[0])
+    tr = [(n, (e - b) / 1000.0) for n, b, e in rows[last + 1:]]
+    dec = [d for n, d in tr if "decode_kernel" in n]
+    ncall = len(DECODE_M) * len(gen.LLAMA3B)
+    steps = len(dec) // ncall
+    plans = {}
+    for proj, N, K in gen.LLAMA3B:
+        z = gen.llama3b_decode(proj, 1)["zmap"]
+        plans[proj] = aqb.aq_plan_pack(N, K, 64, 128, aqb.aq_labels_from_map(z.astype(np.uint8)))
+    out = [f"Timed region: {steps} steps.", "",
+           "| decode call | µs | GB/s |", "|---|---|---|"]
+    per_m = {}
+    for mi, M in enumerate(DECODE_M):
+        for pi, (proj, N, K) in enumerate(gen.LLAMA3B):
+            k = mi * len(gen.LLAMA3B) + pi
+            us = float(np.mean([dec[s * ncall + k] for s in range(steps)]))
+            b = linear_bytes(plans[proj], M)
+            per_m.setdefault(M, [0, 0.0])
+            per_m[M][0] += b
+            per_m[M][1] += us
+            out.append(f"| {proj} {N}x{K} M={M} | {us:.2f} | {b / us / 1e3:.0f} |")
+    out += ["", "| M | algorithmic MB | kernel µs | GB/s | fraction of 8 TB/s |", "|---|---|---|---|---|"]
+    tb, tu = 0, 0.0
+    for M, (b, us) in per_m.items():
+        tb, tu = tb + b, tu + us
+        out.append(f"| {M} | {b / 1e6:.2f} | {us:.2f} | {b / us / 1e3:.0f} | {b / us / 1e3 / 8000:.3f} |")
+    out.append(f"| all | {tb / 1e6:.2f} | {tu:.2f} | {tb / tu / 1e3:.0f} | {tb / tu / 1e3 / 8000:.3f} |")
+    out.append(f"\nDecode mean per call: {tu / ncall:.2f} µs.")
+    pre = [(n, d) for n, d in tr if "expand_kernel" in n or "prefill_big" in n or "prefill_dense" in n]
+    gemm = [(n, d) for n, d in pre if "expand_kernel" not in n]
+    exp_ = [d for n, d in pre if "expand_kernel" in n]
+    nproj = len(gen.QWEN4B)
+    psteps = len(gemm) // nproj
+    out += ["", "| prefill call | expansion µs | GEMM kernel | GEMM µs | GEMM only | expansion + GEMM |",
+            "|---|---|---|---|---|---|"]
+    tops, tg, te = 0, 0.0, 0.0
+    for pi, (proj, N, K) in enumerate(gen.QWEN4B):
+        g = float(np.mean([gemm[s * nproj + pi][1] for s in range(psteps)]))
+        e = float(np.mean([exp_[s * nproj + pi] for s in range(psteps)])) if len(exp_) == len(gemm) else 0.0
+        kname = gemm[pi][0].replace("void aq::(anonymous namespace)::", "").split("(")[0]
+        ops = 2 * PREFILL_M * N * K
+        tops, tg, te = tops + ops, tg + g, te + e
+        out.append(f"| {proj} {N}x{K} | {e:.2f} | `{kname}` | {g:.2f} | {ops / g / 1e6 / 5000:.3f} | "
+                   f"{ops / (g + e) / 1e6 / 5000:.3f} |")
+    out.append(f"| all four ({tops / 1e9:.1f} G-ops) | {te:.2f} | | {tg:.2f} | {tops / tg / 1e6 / 5000:.3f} | "
+               f"{tops / (tg + te) / 1e6 / 5000:.3f} |")
+    out.append(f"\nPrefill mean per call (expansion + GEMM): {(tg + te) / nproj:.2f} µs.")
+    return "\n".join(out)
 
 
 def sleep_cycles_per_us(torch):
@@ -1043,6 +1110,9 @@ def _med_min(v):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
     if args.traffic_summary:
         print(json.dumps(traffic_summary(args.traffic_summary), indent=1))
         return
