@@ -262,6 +262,14 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
   constexpr int NT = WAVES * 64;
   constexpr int XU = 8;          // activation granules per thread per staging pass
   constexpr int XW = DEPTH * BK; // bytes of one token's activations per batch (per-wave slices)
+  // Per-wave slices of 4 tiles hold up to 16 tokens: each slot of a lane
+  // carries one 16-byte granule of XTPS tokens (XLPT lanes per token); the
+  // 8-tile slices keep one token per slot, lane l at granule l.
+  constexpr bool P16 = XMODE == kXPriv && DEPTH == kPriv16Depth;
+  constexpr int XLPT = P16 ? XW / 16 : 64;
+  constexpr int XTPS = P16 ? 64 / XLPT : 1;
+  constexpr int XSLOTS = P16 ? kPriv16MaxM / XTPS : kPrivMaxM;
+  static_assert(!P16 || (BK == 128 && XLPT * XTPS == 64), "16-token slices: b_K = 128");
   extern __shared__ __align__(16) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -386,7 +394,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
   v4i W[DEPTH][2];
   float SC[DEPTH];
   int live[DEPTH], is4v[DEPTH], jv[DEPTH];
-  v4i xv[kPrivMaxM];  // per-wave slices: this lane's granule of the batch, per token
+  v4i xv[XSLOTS];  // per-wave slices: this lane's granules of the batch
 
   // Issue the loads of the live tiles among t0 .. t0+DEPTH-1 of the split:
   // the rows' 16-byte panel chunks (two for an INT8 tile at b_K = 128, one
@@ -443,7 +451,13 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
         }                                                                                       \
       }                                                                                         \
     }                                                                                           \
-    if (XMODE == kXPriv) {                                                                      \
+    if (XMODE == kXPriv && P16) {                                                               \
+      const int col = min(t0i * BK + 16 * (lane % XLPT), K - 16);                               \
+      _Pragma("unroll") for (int q = 0; q < XSLOTS; ++q) {                                      \
+        const int m = q * XTPS + lane / XLPT;                                                   \
+        if (m < M) xv[q] = load16(a.qx + (size_t)m * K + col);                                  \
+      }                                                                                         \
+    } else if (XMODE == kXPriv) {                                                               \
       const int col = min(t0i * BK + 16 * lane, K - 16);                                        \
       _Pragma("unroll") for (int m = 0; m < kPrivMaxM; ++m)                                     \
         if (m < M) xv[m] = load16(a.qx + (size_t)m * K + col);                                  \
@@ -617,7 +631,13 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const DArgs<INL, XF>
 
   for (int t0 = c0; t0 < c1; t0 += DEPTH) {
     if (t0 != c0) AQ_DECODE_ISSUE(t0);
-    if (XMODE == kXPriv) {  // the wave's own activation slice; read back by this wave only
+    if (XMODE == kXPriv && P16) {  // the wave's own activation slice; read back by this wave only
+#pragma unroll
+      for (int q = 0; q < XSLOTS; ++q) {
+        const int m = q * XTPS + lane / XLPT;
+        if (m < M) *reinterpret_cast<v4i *>(xw + m * XW + 16 * (lane % XLPT)) = xv[q];
+      }
+    } else if (XMODE == kXPriv) {
 #pragma unroll
       for (int m = 0; m < kPrivMaxM; ++m)
         if (m < M && 16 * lane < XW) *reinterpret_cast<v4i *>(xw + m * XW + 16 * lane) = xv[m];
@@ -982,6 +1002,12 @@ void launch_mode(const DecodePlan &p, int R, hipStream_t stream, const DArgs<INL
     }
   }
   if (p.xmode == kXPriv) {
+    if constexpr (BK == 128 && !XF) {
+      if (p.depth == kPriv16Depth) {
+        launch_rg<BK, kMfma, 1, 16, kPriv16Depth, kXPriv, PARTIALS, INL, GRP, true, XF>(p, R, stream, args);
+        return;
+      }
+    }
     launch_rg<BK, kMfma, 1, 16, kPrivDepth, kXPriv, PARTIALS, INL, GRP, true, XF>(p, R, stream, args);
     return;
   }

@@ -144,8 +144,12 @@ inline size_t prefill_workspace_bytes(const PackedView &w, int M) {
 // planner (aq_plan.cpp).
 constexpr int kLdsBudget = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kValuMaxM = 1;            // largest M on the vector-ALU path
-constexpr int kPrivMaxM = 4;            // largest M with per-wave activation slices
+constexpr int kPrivMaxM = 4;            // largest M with per-wave activation slices of 8 tiles
 constexpr int kPrivDepth = 8;           // tiles per batch with per-wave activation slices
+// Per-wave slices of 4 tiles for up to 16 tokens, where every wave's share
+// of the columns is one batch (b_K = 128)
+constexpr int kPriv16MaxM = 16;
+constexpr int kPriv16Depth = 4;
 constexpr int kSharedDepth1 = 8;        // tiles per batch, shared staging, one token group
 constexpr int kSharedDepthN = 6;        // tiles per batch, shared staging, 2 token groups
 constexpr int kSharedDepthW = 4;        // tiles per batch, shared staging, 3-4 token groups
@@ -165,7 +169,7 @@ enum { kXPriv = 0, kXShared = 1, kXFused = 2 };
 // separate quantizer launch by 0.7-1.0 us per call at M = 1 and 0.3-0.5 us
 // at M = 2, K = 3072, and loses 0.8 us beyond 8192 elements (K = 8192,
 // M = 2).
-constexpr int kFusedMaxM = kPrivMaxM;
+constexpr int kFusedMaxM = 4;
 constexpr int kFusedUnits = 2;
 
 // Launch plan of one decode call: products on the vector ALU or MFMA, where
@@ -179,6 +183,7 @@ constexpr int kFusedUnits = 2;
 // beyond that take further launches of ylaunch chunks each.
 struct DecodePlan {
   int mode, xmode, MG, waves, RG, S, Z, mchunks, ylaunch, xstride;
+  int depth;  // tiles per batch of the per-wave slices (kPrivDepth or kPriv16Depth)
   size_t lds, cnt_bytes, ws_bytes;
 };
 // split = 0: adaptive; otherwise S, one of the supported values.  xform:

@@ -107,10 +107,24 @@ DecodePlan plan_decode(const PackedView &w, int M, int split, bool xform) {
   // Products: vector ALU for one token, MFMA otherwise.  Activations: a
   // per-wave LDS slice of each batch for M <= 4 (no workgroup barrier),
   // else the block's 16*MG token rows over its chunk of columns.
-  if (M <= kPrivMaxM) {
+  p.depth = kPrivDepth;
+  // 5..16 tokens: per-wave slices of 4 tiles where each wave's columns are
+  // one batch, the workgroup holds one row group (its waves then read
+  // disjoint columns) and the staged token rows would be large (M*K of at
+  // least 64 KB), instead of the block's staged rows (no workgroup-wide
+  // staging before the first products).  Llama-3.2-3B-shaped shapes at
+  // M = 16: down (3072 x 8192) 8.74 -> 7.80-7.82 us; o (3072 x 3072, 48 KB of
+  // rows) 5.84 -> 5.89-6.03 us and qkv (two row groups per workgroup, whose
+  // waves would load the same columns twice) 6.20 -> 6.66 us, so those keep
+  // the staged rows.
+  const int rg16 = split > 0 ? p.waves / split : rowgroups_unchunked(w);
+  const bool priv16 = !xform && w.bK == 128 && M > kPrivMaxM && M <= kPriv16MaxM && rg16 == 1 &&
+                      (long long)M * w.K >= 65536 && (w.C + p.waves - 1) / p.waves <= kPriv16Depth;
+  if (M <= kPrivMaxM || priv16) {
     p.xmode = kXPriv;
-    p.RG = split > 0 ? p.waves / split : rowgroups_unchunked(w);
-    p.lds = (size_t)p.waves * M * kPrivDepth * w.bK + red;
+    p.RG = rg16;
+    p.depth = priv16 ? kPriv16Depth : kPrivDepth;
+    p.lds = (size_t)p.waves * M * p.depth * w.bK + red;
     p.mchunks = 1;
   } else {
     p.xmode = kXShared;
@@ -147,7 +161,7 @@ DecodePlan plan_decode(const PackedView &w, int M, int split, bool xform) {
     // rows of 64 (down: 8.6 against 13.7 us).
     if (split == 0 && p.Z == 1 && p.RG < 4) {
       const int s4 = p.waves / 4;
-      const int depth = p.xmode == kXPriv ? kPrivDepth
+      const int depth = p.xmode == kXPriv ? p.depth
                         : p.MG == 1       ? kSharedDepth1
                         : p.MG == 2       ? kSharedDepthN
                                           : kSharedDepthW;
@@ -194,6 +208,7 @@ size_t decode_workspace_bytes(const PackedView &w, int M, int split, bool xform)
 DecodePlan plan_decode_fused(const PackedView &w, int M, int split) {
   DecodePlan p = plan_decode(w, M, split);
   p.xmode = kXFused;
+  p.depth = kPrivDepth;
   p.MG = 1;
   p.Z = 1;
   p.mchunks = 1;

@@ -50,6 +50,26 @@ def test_ragged_shapes(N, K, bK, M):
     Case(W, z, X, 64, bK, name=f"ragged{N}x{K}/bK{bK}/M{M}").check_all(splits=(0, 2, 4, 8, 16))
 
 
+@pytest.mark.parametrize("N,K,M", [
+    (3072, 8192, 16),   # 64 tile columns over 16 waves: 4 per wave, one batch of per-wave slices
+    (5120, 3072, 13),   # 2 row groups per workgroup: staged rows (split 16: one row group, slices)
+    (768, 2048, 5),     # 10 KB of token rows: staged rows (split 16 too)
+    (1024, 8192, 9),    # 64 columns, 4 per wave; 9 tokens, 72 KB of rows: slices
+    (1024, 8448, 9),    # 66 columns: 5 per wave, more than one batch: the block's staged token rows
+])
+def test_decode_private_slices_up_to_16_tokens(N, K, M):
+    """5..16 tokens on per-wave activation slices of 4 tiles (two tokens'
+    granules per lane slot) where the workgroup holds one row group, each
+    wave's columns are one batch and the rows are at least 64 KB, the block's
+    staged token rows otherwise;
+    the explicit splits move a shape between the two (split 16: one row group
+    per workgroup, split 4: four, each wave C/4 columns)."""
+    W, z, X = _ragged(N, K, 128, M, seed=N + 3 * K + M)
+    bias = np.random.default_rng(M).standard_normal(N).astype(np.float32)
+    Case(W, z, X, 64, 128, bias=bias, name=f"priv{N}x{K}/M{M}").check_all(phases=("decode",),
+                                                                          splits=(0, 4, 8, 16))
+
+
 @pytest.mark.parametrize("kind", ["all_int4", "all_int8", "checker", "zero_rows"])
 def test_uniform_and_degenerate_maps(kind):
     rng = np.random.default_rng(11)
