@@ -6,9 +6,10 @@
 // float4 per thread, coalesced 16-byte loads), its |x| maximum is reduced
 // across the wavefront with DPP row permutes and one ds_swizzle, then across
 // the waves through LDS; each thread then writes the INT8 codes of its own
-// float4 groups as 4-byte stores.  Decode-sized batches (few rows) take
-// 1024 threads per row so that each lane divides few elements; prefill-sized
-// batches take 256 threads per row and fill the chip with rows.  Rows longer
+// float4 groups as 4-byte stores (an FP32 estimate of x / s decides most codes,
+// the FP64 division the rest).  Decode-sized batches (few rows) take 1024
+// threads per row; prefill-sized batches take 256 threads per row and fill
+// the chip with rows.  Rows longer
 // than the register-resident variants cover fall back to a two-pass loop.
 
 #include "aq_device.h"
@@ -35,11 +36,14 @@ __global__ __launch_bounds__(T) void quant_act_kernel(const float *__restrict__ 
   }
   const double s = row_scale(block_max_u32<T>(amax));
   if (threadIdx.x == 0) sx[m] = (float)s;
+  // codes by the FP32 estimate where it decides them, else the FP64 rule
+  // (code_fast: the same codes as the FP64 division, bit for bit)
+  const float inv = (float)(1.0 / s);
   uint32_t *out = reinterpret_cast<uint32_t *>(qx + m * K);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = threadIdx.x + i * T;
-    if (c < n4) out[c] = codes4(v[i], s);
+    if (c < n4) out[c] = codes4_fast(v[i], s, inv);
   }
 }
 
@@ -54,8 +58,9 @@ __global__ __launch_bounds__(256) void quant_act_loop_kernel(const float *__rest
   for (int c = threadIdx.x; c < n4; c += 256) amax = max(amax, abs_bits4(row[c]));
   const double s = row_scale(block_max_u32<256>(amax));
   if (threadIdx.x == 0) sx[m] = (float)s;
+  const float inv = (float)(1.0 / s);
   uint32_t *out = reinterpret_cast<uint32_t *>(qx + m * K);
-  for (int c = threadIdx.x; c < n4; c += 256) out[c] = codes4(row[c], s);
+  for (int c = threadIdx.x; c < n4; c += 256) out[c] = codes4_fast(row[c], s, inv);
 }
 
 // The pages' grouping (App. B.3): one wave per group of 64 features x BM
@@ -133,7 +138,10 @@ int round_nv(int need) {
 hipError_t launch_quant_act(const float *X, int M, int K, int8_t *qx, float *sx,
                             hipStream_t stream) {
   const int n4 = K / 4;
-  // Few rows: a wide workgroup per row keeps the per-lane FP64 work short.
+  // Few rows: a wide workgroup per row (16 waves).  With 4 waves the
+  // decode-sized rows measured the same (K = 3072: 4.59 against 4.64 us;
+  // K = 8192: 4.55 against 4.53 us): the call is one load round trip and the
+  // launch, not the lanes' arithmetic.
   if (M < 256) {
     const int nv = round_nv((n4 + 1023) / 1024);
     if (nv && nv <= 8) return launch_t<1024>(nv, X, M, K, qx, sx, stream);
