@@ -107,6 +107,55 @@ def test_extreme_codes_and_ties():
     Case(W, z, X, name="ties").check_all(splits=(0, 4, 8, 16))
 
 
+def _tie_rows(M, K, seed):
+    """Rows whose codes sit on or next to a rounding tie: even rows have
+    max |x| = 127 (scale exactly 1) and values k + 1/2 and 1 or 2 ulps from
+    it; odd rows have max |x| = 100 (an inexact scale s) and values
+    (k + 1/2) s rounded to FP32, so x / s lands within an ulp or so of a
+    tie on either side."""
+    rng = np.random.default_rng(seed)
+    X = np.zeros((M, K), np.float32)
+    k = rng.integers(-126, 126, size=(M, K)).astype(np.float64)
+    nudge = rng.integers(-2, 3, size=(M, K))
+    s_odd = 100.0 / 127.0
+    for r in range(M):
+        if r % 2 == 0:
+            base = (k[r] + 0.5).astype(np.float32)
+            X[r, 0] = 127.0
+        else:
+            base = ((k[r] + 0.5) * s_odd).astype(np.float32)
+            X[r, 0] = 100.0
+        v = base.copy()
+        for step in (1, 2):
+            up, dn = nudge[r] == step, nudge[r] == -step
+            for _ in range(step):
+                v[up] = np.nextafter(v[up], np.float32(np.inf))
+                v[dn] = np.nextafter(v[dn], np.float32(-np.inf))
+        v[0] = X[r, 0]
+        X[r] = v
+    return X
+
+
+@pytest.mark.parametrize("M,K", [
+    (3, 3072),      # 1024-thread rows
+    (300, 2560),    # 256-thread rows
+    (2, 40960),     # few rows past the 1024-thread variants: two-pass loop
+    (256, 81984),   # rows past the 256-thread variants: two-pass loop
+])
+def test_quant_act_near_ties(M, K):
+    """Every quantizer route takes its codes from an FP32 estimate of x / s
+    where that decides them and from the FP64 division otherwise; exact
+    ties and values one or two ulps from a tie, at an exact and an inexact
+    scale, must give the oracle's FP64 codes and scales bit for bit."""
+    X = _tie_rows(M, K, seed=M + K)
+    qx, sx = aq.aq_quant_act(torch.from_numpy(X).cuda())
+    torch.cuda.synchronize()
+    qr, sr = O.quant_act(X)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sr.astype(np.float32).view(np.uint32))
+    bad = np.argwhere(qx.cpu().numpy().astype(np.int64) != qr)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:4].tolist()}"
+
+
 @pytest.mark.parametrize("proj", [p[0] for p in gen.LLAMA3B])
 def test_llama3b_decode_linears(proj):
     for M in (1, 4, 16):
