@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256) void quant_act_loop_kernel(const float *__rest
 // feature 64c + l of every row of the group; the group's maximum and minimum
 // are reduced across the wave; the scale is eq. 6 at 8 bits,
 // s = max(max(0, max A) / 127, max(0, -min A) / 128, 1e-12) in FP64, and the
-// codes are eq. 5's clip(rint(x / s), -128, 127) in FP64.
+// codes are eq. 5's clip(rint(x / s), -128, 127) in FP64 (by code_fast: an
+// FP32 estimate where it decides the code, the FP64 division otherwise).
 template <int BM>
 __global__ __launch_bounds__(256) void quant_act_grouped_kernel(const float *__restrict__ X, int M,
                                                                 int K, int8_t *__restrict__ qx,
@@ -96,9 +97,10 @@ __global__ __launch_bounds__(256) void quant_act_grouped_kernel(const float *__r
   }
   const double s = fmax(fmax((double)mx / 127.0, -(double)mn / 128.0), 1e-12);
   if (lane == 0) sxg[(size_t)blockIdx.y * kg + c] = (float)s;
+  const float inv = (float)(1.0 / s);  // code_fast: the FP64 rule's codes (-128 always takes it)
 #pragma unroll
   for (int r = 0; r < BM; ++r)
-    if (r < nr) qx[(size_t)(r0 + r) * K + col] = (int8_t)(code_of(v[r], s) & 0xFF);
+    if (r < nr) qx[(size_t)(r0 + r) * K + col] = (int8_t)(code_fast(v[r], s, inv) & 0xFF);
 }
 
 template <int T, int NV>

@@ -369,8 +369,9 @@ __global__ __launch_bounds__(T) void quant_act_transformed_kernel(const QuantTAr
   const uint32_t am = block_max_u32<T>(amax);
   const double sc = am > 0x7F800000u ? (double)__builtin_nanf("") : row_scale(am);
   if (threadIdx.x == 0) a.sx[m] = (float)sc;
+  const float inv = (float)(1.0 / sc);
   uint32_t *out = reinterpret_cast<uint32_t *>(a.qx + m * a.K);
-  for (int c4 = threadIdx.x; c4 < (a.K >> 2); c4 += T) out[c4] = codes4(xt4[c4], sc);
+  for (int c4 = threadIdx.x; c4 < (a.K >> 2); c4 += T) out[c4] = codes4_fast(xt4[c4], sc, inv);
 }
 
 // The one-pass quantizer for few, short rows, lane by element:
@@ -466,11 +467,12 @@ __global__ __launch_bounds__(1024) void quant_act_transformed_lanes_kernel(const
   const uint32_t am = block_max_u32<1024>(amax);
   const double sc = am > 0x7F800000u ? (double)__builtin_nanf("") : row_scale(am);
   if (threadIdx.x == 0) a.sx[m] = (float)sc;
+  const float inv = (float)(1.0 / sc);
   int8_t *out = a.qx + m * a.K;
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const int c = wave + 16 * j;
-    if (c < nb) out[(size_t)c * 64 + lane] = (int8_t)(code_of(v[j], sc) & 0xFF);
+    if (c < nb) out[(size_t)c * 64 + lane] = (int8_t)(code_fast(v[j], sc, inv) & 0xFF);
   }
 }
 
